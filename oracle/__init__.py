@@ -1,0 +1,51 @@
+"""Plain, slow, fp64 CPU oracle for the speculative-verification hot path.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import or call anything in this
+package.  The product path (the HIP library and its Python binding) never
+imports it, and this package imports nothing from the product path: the two
+share no code, no tables and no pre- or post-processing.
+
+What each function follows (pages cited by title and section):
+
+* ``spec_verify_attn`` -- causal multi-query attention of the k draft queries of
+  each sequence over its paged KV cache.  "Decoding Speculative Decoding from
+  First Principles", sections "Speculating to get sequence parallelism during
+  decode" (the target scores every draft in one prefill-style pass) and the
+  prerequisites section (causal masked attention); "CXL-SpecKV", key
+  observation (1) (token t reads positions 0..t-1) and the memory-hierarchy
+  section (4 KB pages).  Written as the plain softmax-attention definition,
+  because split-KV with an online softmax reaches exactly that result.
+* ``kv_quant_int8`` / ``dequant_int8`` -- "CXL-SpecKV", Algorithm 2 (KV-Cache
+  Compression), steps 3 and 5: scale = max|X|/127, code = round(X/scale); key
+  observation (4) (values cluster near zero, INT8 gives a 2x ratio).
+* ``kv_append`` -- "HeteroReason", workflow Phase 3 and the KVMU description
+  (Fig. 7): the cache holds context plus speculated rows; rows past the
+  validated length are invalid after a rejection.
+* ``argmax_rows`` / ``accept_prefix`` -- "Decoding Speculative Decoding from
+  First Principles", section "Speculating to get sequence parallelism during
+  decode": reject at the first disagreement, keep the target's token, and the
+  last row gives the +1 bonus token (1 to n+1 tokens per pass).
+
+Pins (tests marked ``not gpu``): a torch float64 SDPA with an explicit mask and
+a pure-Python triple loop for attention; closed forms (constant V rows,
+identical keys, k=1 decode) and invariants (prefix invariance, page
+permutation, GQA = MHA on repeated KV); a brute-force exact-rational INT8
+quantiser, hand-derived tie cases and the round-trip bound; numpy.argmax and
+constructed tie / NaN / signed-zero rows for acceptance.  No function here is
+"parity unpinned".
+"""
+from .attention import spec_verify_attn
+from .kv_quant import kv_quant_int8, dequant_int8, round_to_bf16
+from .kv_append import kv_append
+from .accept import argmax_rows, accept_prefix
+
+__all__ = [
+    "spec_verify_attn",
+    "kv_quant_int8",
+    "dequant_int8",
+    "round_to_bf16",
+    "kv_append",
+    "argmax_rows",
+    "accept_prefix",
+]
