@@ -1,0 +1,265 @@
+"""Benchmark of the speculative-verification hot path on one MI355X.
+
+One step = one pass of the whole hot path over one synthetic batch:
+  kv_append (the k new K/V rows of every sequence; INT8 caches quantise on
+  write) -> spec_verify_attn -> accept_prefix (argmax over the vocabulary and
+  the longest accepted prefix).
+Default workload: 7B-MHA shape, B=8, Hq=Hkv=32, d=128, S=2048, k=4, bf16 paged
+KV (16-token pages, random page permutation).  That shape names no vocabulary;
+acceptance runs over fp32 logits [B*(k+1), 128256] with drafts agreeing with
+the target argmax with probability 0.8 (the ragged serving batch's vocabulary
+and agreement rate).
+
+Prints ONE JSON line.  `value` is verified draft tokens per second for whole
+steps (inputs resident in HBM); `roofline` is the attention kernel's KV bytes
+over its own average launch time (HIP events on its stream, inside the timed
+region) against 8 TB/s; `cpu_baseline` is the fp64 oracle on the host.
+"""
+import argparse
+import dataclasses
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+METRIC = "verify-attn KV HBM GB/s (% of peak) and verified draft tokens/sec, 1 GPU"
+HBM_PEAK_GBPS = 8000.0
+MALL_BYTES = 256 << 20
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kv_bytes(w, ctx, ks):
+    """Algorithmic KV bytes of one verify-attn launch: K and V rows 0..S_b+k_b-1
+    of every kv head, plus the fp16 scale of every INT8 row."""
+    elem = {"f32": 4, "bf16": 2, "int8": 1}[w.kv_dtype]
+    per_row = w.d * elem + (2 if w.kv_dtype == "int8" else 0)
+    rows = sum(c + k for c, k in zip(ctx, ks))
+    return 2 * w.Hkv * rows * per_row
+
+
+def other_bytes(w, ctx, ks, max_pages):
+    qe = {"f32": 4, "bf16": 2}[w.q_dtype]
+    T = sum(ks)
+    return 2 * T * w.Hq * w.d * qe + 4 * len(ctx) * max_pages + 8 * len(ctx)
+
+
+class Inputs:
+    """One resident input set and the prepared calls of one step."""
+
+    def __init__(self, tva, wl, w, seed_offset, dev):
+        self.case = case = wl.make_case(w, device=dev, seed_offset=seed_offset)
+        self.batch = tva.Batch(case["ctx_lens"], case["cu_q"], total_q=case["T"],
+                               max_q=case["max_q"], max_len=case["max_len"])
+        if w.kv_dtype == "int8":
+            kc, ks = tva.kv_quant_int8(case["k_pool"])
+            vc, vs = tva.kv_quant_int8(case["v_pool"])
+            self.kv = tva.PagedKV(kc, vc, case["block_table"], ks, vs)
+        else:
+            self.kv = tva.PagedKV(case["k_pool"], case["v_pool"], case["block_table"])
+        self.out = torch.empty_like(case["q"])
+        B = case["B"]
+        self.ids = torch.empty(case["T"] + B, dtype=torch.int32, device=dev)
+        self.alen = torch.empty(B, dtype=torch.int32, device=dev)
+        self.nxt = torch.empty(B, dtype=torch.int32, device=dev)
+        self.append = tva.prepare_kv_append(self.batch, case["k_new"], case["v_new"], self.kv)
+        self.attn = tva.prepare_spec_verify_attn(self.batch, case["q"], self.kv, self.out)
+        self.accept = tva.prepare_accept_prefix(self.batch, case["logits"], case["draft_ids"],
+                                                self.ids, self.alen, self.nxt)
+
+
+def copy_probe_gbps(dev, nbytes=1 << 30, reps=10):
+    """A plain device-to-device copy, the achievable-bandwidth reference."""
+    a = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    return 2 * nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+
+
+def cpu_baseline(inp, w, budget_s):
+    """The fp64 oracle (as it stands) on a bounded sample of the same step:
+    append + attention over (sequence, kv-head) pairs taken in order until the
+    time budget is spent, + acceptance over the sampled sequences' logit rows.
+    Scaled to draft tokens per second of the whole batch."""
+    import oracle
+    from threadpoolctl import threadpool_limits
+
+    case = inp.case
+    np_ = lambda t: (t.float() if t.dtype == torch.bfloat16 else t).cpu().numpy()
+    kp, vp = np_(case["k_pool"]), np_(case["v_pool"])
+    bt, ctx, cu = np_(case["block_table"]), np_(case["ctx_lens"]), np_(case["cu_q"])
+    qn = np_(case["q"])
+    kn, vn = np_(case["k_new"]), np_(case["v_new"])
+    logits, drafts = np_(case["logits"]), np_(case["draft_ids"])
+    scale = 1.0 / math.sqrt(w.d)
+    B, H = case["B"], w.Hkv
+    pairs = [(b, g) for b in range(B) for g in range(H)]
+    done_pairs, t_attn = 0, 0.0
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        if w.kv_dtype == "int8":
+            # the INT8 cache holds oracle codes of the fp32 pool (cache fill, untimed)
+            P = kp.shape[0]
+            kc, ksc = oracle.kv_quant_int8(kp.reshape(-1, w.d))
+            vc, vsc = oracle.kv_quant_int8(vp.reshape(-1, w.d))
+            kp, vp = kc.reshape(kp.shape), vc.reshape(vp.shape)
+            sc = dict(k_scale=ksc.reshape(P, H, 16), v_scale=vsc.reshape(P, H, 16))
+            t0 = time.perf_counter()
+            kp, vp, k_s, v_s = oracle.kv_append(kn, vn, kp, vp, bt, ctx, cu, "int8",
+                                                sc["k_scale"], sc["v_scale"])
+            sc = dict(k_scale=k_s, v_scale=v_s)
+        else:
+            sc = {}
+            kp, vp, _, _ = oracle.kv_append(kn, vn, kp, vp, bt, ctx, cu, w.kv_dtype)
+        t_append = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        for pair in pairs:
+            oracle.spec_verify_attn(qn, kp, vp, bt, ctx, cu, scale, select=[pair], **sc)
+            done_pairs += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+        t_attn = time.perf_counter() - t0
+        seqs = sorted({b for b, _ in pairs[:done_pairs]})
+        t0 = time.perf_counter()
+        for b in seqs:
+            r0, r1 = int(cu[b]) + b, int(cu[b + 1]) + b + 1
+            oracle.accept_prefix(logits[r0:r1], drafts[int(cu[b]):int(cu[b + 1])],
+                                 np.array([0, int(cu[b + 1] - cu[b])]))
+        t_acc = time.perf_counter() - t0
+    frac_pairs = done_pairs / len(pairs)
+    frac_seqs = len(seqs) / B
+    step_s = t_append + t_attn / frac_pairs + t_acc / frac_seqs
+    tokens = case["T"]
+    return {
+        "value": tokens / step_s, "unit": "verified draft tokens/s", "cores": 1, "kind": "oracle",
+        "sample": (f"{done_pairs} of {len(pairs)} (sequence, kv-head) attention pairs "
+                   f"({t_attn:.1f} s), acceptance for {len(seqs)} of {B} sequences, the whole "
+                   f"append; scaled to the full batch; numpy BLAS limited to 1 thread"),
+        "seconds_per_step_estimate": step_s,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="mha7b")
+    ap.add_argument("--sets", type=int, default=0, help="input sets rotated (0: enough to defeat the 256 MB MALL)")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle attention")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              "(this path has no multi-GPU mode).", file=sys.stderr)
+        sys.exit(2)
+
+    import token_verify_attention_amd as tva
+    from token_verify_attention_amd import workloads as wl
+
+    tva.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = wl.WORKLOADS[args.workload]
+    if w.vocab is None:
+        w = dataclasses.replace(w, vocab=128256, match_p=0.8)
+
+    ctx, ks = wl.make_lengths(w, 0, "cpu")
+    ctx, ks = [int(x) for x in ctx], [int(x) for x in ks]
+    kvb = kv_bytes(w, ctx, ks)
+    nsets = args.sets or max(1, min(4, math.ceil(3 * MALL_BYTES / max(kvb, 1))))
+    log(f"workload {w.name}: KV bytes per launch {kvb / 1e6:.1f} MB, {nsets} input set(s)")
+    sets = [Inputs(tva, wl, w, s, dev) for s in range(nsets)]
+    # every set has the same lengths (seeded by the workload), so one byte count
+    assert sets[0].case["ctx_host"] == ctx and sets[0].case["k_host"] == ks
+    max_pages = int(sets[0].case["block_table"].shape[1])
+    T = sum(ks)
+
+    stream = torch.cuda.current_stream(dev)
+    for s in range(args.warmup):
+        inp = sets[s % nsets]
+        inp.append()
+        inp.attn()
+        inp.accept()
+    torch.cuda.synchronize()
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    t_start, t_end = ev(), ev()
+    attn_ev = [(ev(), ev()) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for s in range(args.steps):
+        inp = sets[s % nsets]
+        inp.append()
+        attn_ev[s][0].record(stream)
+        inp.attn()
+        attn_ev[s][1].record(stream)
+        inp.accept()
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms_per_step = total_ms / args.steps
+    attn_ms = [a.elapsed_time(b) for a, b in attn_ev]
+    attn_avg = sum(attn_ms) / len(attn_ms)
+    achieved = kvb / (attn_avg * 1e-3) / 1e9
+    value = T / (ms_per_step * 1e-3)
+
+    probe = copy_probe_gbps(dev)
+    result = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "verified draft tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.kv_dtype if w.kv_dtype != "int8" else "int8 KV, bf16 Q",
+        "data": "synthetic (seeded torch Philox; no dataset)",
+        "config": {
+            "workload": (f"{w.name}: B={w.B}, Hq={w.Hq}, Hkv={w.Hkv}, d={w.d}, "
+                         f"S={w.ctx}, k={w.k}, {w.kv_dtype} paged KV (16-token pages, random "
+                         f"page permutation); acceptance over fp32 logits "
+                         f"[{T + w.B}, {w.vocab}]"),
+            "global_batch": w.B, "seq_len": w.ctx if isinstance(w.ctx, int) else list(w.ctx),
+            "drafts_per_seq": w.k if isinstance(w.k, int) else list(w.k),
+            "parallelism": "single GPU", "input_sets_rotated": nsets,
+        },
+        "kv_bytes_per_launch": kvb,
+        "kv_hbm_gbps": achieved,
+        "kv_frac_of_peak": achieved / HBM_PEAK_GBPS,
+        "attn_ms_avg": attn_avg,
+        "attn_ms_min": min(attn_ms),
+        "attn_draft_tokens_per_s": T / (attn_avg * 1e-3),
+        "other_bytes_per_launch": other_bytes(w, ctx, ks, max_pages),
+        "copy_probe_gbps": probe,
+        "roofline": {
+            "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+            "kernel": "verify_attn_kernel",
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        result["cpu_baseline"] = cpu_baseline(sets[0], w, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

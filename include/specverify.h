@@ -1,0 +1,187 @@
+/*
+ * specverify.h -- C ABI of libspecverify.so, the MI355X (gfx950) hot path of
+ * speculative-decoding verification.
+ *
+ * The target model scores the k_b draft tokens of every sequence in one pass
+ * ("Decoding Speculative Decoding from First Principles", section
+ * "Speculating to get sequence parallelism during decode").  Four operations:
+ *
+ *   sva_kv_quant_int8     INT8 KV rows with one fp16 absmax scale per row
+ *   sva_kv_append         write the k_b new K/V rows into the paged cache
+ *   sva_spec_verify_attn  causal multi-query attention of the k_b drafts
+ *   sva_accept_prefix     greedy longest-prefix acceptance over the logits
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Pointers named as device memory are HIP device pointers owned by the
+ *   caller.  Structs are read on the host during the call and not kept.
+ * - `stream` is a hipStream_t passed as void*; NULL means the null stream.
+ *   Every call only enqueues work on that stream and returns; nothing is
+ *   synchronised.  The library allocates no memory.
+ * - Host-checkable argument errors return SVA_ERR_INVALID_ARG or
+ *   SVA_ERR_UNSUPPORTED before anything is enqueued, and nothing is written.
+ *   A failed launch returns SVA_ERR_HIP.  sva_last_error() gives the detail
+ *   (thread-local, valid until the next call on the same thread).
+ * - Values that live in device memory (ctx_lens, cu_q, block-table entries)
+ *   are preconditions.  Kernels clamp out-of-contract values so that they
+ *   never access memory outside the buffers described here, but the results
+ *   for such inputs are unspecified.
+ * - Only gfx950 devices are supported (SVA_ERR_UNSUPPORTED otherwise).
+ */
+#ifndef SPECVERIFY_H
+#define SPECVERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SVA_OK = 0,
+  SVA_ERR_INVALID_ARG = 1,
+  SVA_ERR_UNSUPPORTED = 2,
+  SVA_ERR_HIP = 3
+} sva_status;
+
+typedef enum { SVA_F32 = 0, SVA_BF16 = 1, SVA_F16 = 2, SVA_INT8 = 3 } sva_dtype;
+
+/* Paged KV cache of ONE attention layer.  Pages hold `page_size` (= 16)
+ * consecutive token positions of one sequence; a page of one kv head is
+ * contiguous ("CXL-SpecKV", memory hierarchy section: the pool is organised in
+ * 4 KB pages -- 16 tokens x 128 values x 2 bytes).
+ *   k, v                 [num_pages, Hkv, page_size, d] of kv_dtype
+ *                        (SVA_F32, SVA_BF16 or SVA_INT8 codes)
+ *   k_scale, v_scale     [num_pages, Hkv, page_size] fp16 bit patterns; only for
+ *                        SVA_INT8 (value = code * scale), NULL otherwise
+ *   block_table          [B, max_pages_per_seq] int32: physical page of each
+ *                        logical page of each sequence; -1 marks unused entries
+ * Logical position p of sequence b lives at page block_table[b][p / 16],
+ * slot p % 16. */
+typedef struct {
+  void *k;
+  void *v;
+  void *k_scale;
+  void *v_scale;
+  const int32_t *block_table;
+  int32_t num_pages;
+  int32_t page_size;
+  int32_t Hkv;
+  int32_t d;
+  int32_t max_pages_per_seq;
+  int32_t kv_dtype;
+} sva_paged_kv;
+
+/* One verification batch of B sequences ("HeteroReason", KVMU description,
+ * Fig. 7: ctx_lens[b] is the validated pointer; ctx_lens[b] + k_b the
+ * speculation frontier while the drafts are verified).
+ *   ctx_lens   [B] device int32: committed rows S_b, EXCLUDING this step's drafts
+ *   cu_q       [B+1] device int32: prefix sums of k_b (cu_q[0] = 0); k_b may be 0
+ *   total_q    host copy of cu_q[B] (T, the number of draft rows)
+ *   max_q      host upper bound on every k_b (1..16)
+ *   max_len    host upper bound on every S_b + k_b */
+typedef struct {
+  int32_t B;
+  const int32_t *ctx_lens;
+  const int32_t *cu_q;
+  int32_t total_q;
+  int32_t max_q;
+  int32_t max_len;
+} sva_batch;
+
+/* Optional tuning for sva_spec_verify_attn; pass NULL for the defaults.
+ *   path            0: per sequence, VALU when k_b*G < 16 else MFMA (default)
+ *                   1: VALU for every sequence     2: MFMA for every sequence
+ *   num_workgroups  0: chosen from the device and batch; otherwise the grid size
+ *                   (must equal the value used for the workspace size query) */
+typedef struct {
+  int32_t path;
+  int32_t num_workgroups;
+} sva_verify_opts;
+
+/* INT8 quantisation of `rows` rows of d values, one fp16 scale per row.
+ * "CXL-SpecKV", Algorithm 2 (KV-Cache Compression), steps 3 and 5, and key
+ * observation (4):  a = max|x|,  scale = fp16_rne(a / 127),
+ * code = clamp(rne(fp32(x / scale)), -127, 127), codes 0 when scale == 0.
+ *   x        device [rows, d] of src_dtype (SVA_F32 or SVA_BF16)
+ *   codes    device [rows, d] int8 (written)
+ *   scales   device [rows] fp16 bit patterns (written)
+ *   d        64, 128 or 256
+ * Inputs must be finite with max|x| <= 65504 * 127 (the scale must fit fp16). */
+sva_status sva_kv_quant_int8(const void *x, int32_t src_dtype, int64_t rows, int32_t d,
+                             int8_t *codes, uint16_t *scales, void *stream);
+
+/* Append the k_b new K and V rows of every sequence at logical positions
+ * S_b .. S_b + k_b - 1 ("HeteroReason", workflow Phase 3: the cache holds the
+ * context plus the speculated rows; rows past the validated length are
+ * invalid after a rejection).
+ *   k_new, v_new   device [T, Hkv, d] of src_dtype (SVA_F32 or SVA_BF16),
+ *                  rows ordered by cu_q
+ *   kv             the cache; rows are stored as kv_dtype: F32 and BF16 caches
+ *                  round to nearest-even, INT8 caches quantise each (token,
+ *                  head) row exactly as sva_kv_quant_int8
+ * Block-table entries for the written positions must be valid pages. */
+sva_status sva_kv_append(const sva_batch *batch, const void *k_new, const void *v_new,
+                         int32_t src_dtype, const sva_paged_kv *kv, void *stream);
+
+/* Workspace bytes that sva_spec_verify_attn needs for this batch shape on the
+ * current device (depends on B, Hkv, d, max_q, max_len, Hq and opts). */
+size_t sva_verify_workspace_bytes(const sva_batch *batch, const sva_paged_kv *kv, int32_t Hq,
+                                  const sva_verify_opts *opts);
+
+/* Causal verification attention.  For sequence b, draft query i (position
+ * S_b + i) and query head h (kv head g = h / G, G = Hq / Hkv):
+ *   out[cu_q[b]+i][h] = sum_p softmax_p(scale * q . K_p) V_p,  p = 0 .. S_b + i
+ * ("Decoding Speculative Decoding from First Principles": the target verifies
+ * every draft in one prefill-style pass with causal masking; "CXL-SpecKV", key
+ * observation (1): a token reads all earlier positions).  K/V rows of INT8
+ * caches are code * scale.
+ *   q           device [T, Hq, d] of q_dtype (SVA_F32 or SVA_BF16)
+ *   out         device [T, Hq, d] of out_dtype (SVA_F32 or SVA_BF16), written
+ *   workspace   device, >= sva_verify_workspace_bytes(...) bytes.  Its first
+ *               part holds completion counters: it must be all-zero before its
+ *               first use, and every call leaves it all-zero again.  Calls that
+ *               may run concurrently need distinct workspaces.
+ * Supported: page_size 16, d in {64, 128}, Hq % Hkv == 0, max_q <= 16,
+ * max_q * (Hq / Hkv) <= 128, B <= 4096; SVA_F32 caches use the VALU path and
+ * need max_q * (Hq / Hkv) < 16. */
+sva_status sva_spec_verify_attn(const sva_batch *batch, const void *q, int32_t q_dtype,
+                                int32_t Hq, const sva_paged_kv *kv, float softmax_scale,
+                                void *out, int32_t out_dtype, const sva_verify_opts *opts,
+                                void *workspace, size_t workspace_bytes, void *stream);
+
+/* Workspace bytes that sva_accept_prefix needs for this batch and vocab. */
+size_t sva_accept_workspace_bytes(const sva_batch *batch, int32_t V);
+
+/* Greedy longest-prefix acceptance ("Decoding Speculative Decoding from First
+ * Principles", section "Speculating to get sequence parallelism during
+ * decode": reject at the first disagreement, keep the target's token; the last
+ * row yields the +1 bonus token).
+ *   logits      device [T + B, V] fp32; sequence b owns the k_b + 1 rows that
+ *               start at cu_q[b] + b (row j scores the token after draft j-1)
+ *   draft_ids   device [T] int32
+ *   argmax_ids  device [T + B] int32 (written): first index of each row's
+ *               maximum; a NaN counts as the maximum (first NaN wins);
+ *               -0.0 equals +0.0
+ *   accept_len  device [B] int32 (written): n_b = leading drafts equal to the
+ *               target's tokens (0 .. k_b)
+ *   next_token  device [B] int32 (written): the target's token at row n_b
+ *   workspace   device, >= sva_accept_workspace_bytes(...) bytes, no
+ *               initialisation needed
+ * The step emits draft[0 .. n_b-1] followed by next_token[b]: n_b + 1 tokens.
+ * Committing is the caller's: S_b += n_b + 1 once the bonus token's K/V row is
+ * appended by the next step (or S_b += n_b before it). */
+sva_status sva_accept_prefix(const sva_batch *batch, const float *logits, int32_t V,
+                             const int32_t *draft_ids, int32_t *argmax_ids, int32_t *accept_len,
+                             int32_t *next_token, void *workspace, size_t workspace_bytes,
+                             void *stream);
+
+const char *sva_status_string(sva_status status);
+const char *sva_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPECVERIFY_H */

@@ -1,0 +1,211 @@
+"""GPU parity of sva_spec_verify_attn against the fp64 oracle (through the C ABI).
+
+Small cases span several pages, ragged tails (S = 0, 1, 15, 16, 17, ...), k = 1..16,
+GQA groups 1..8, d = 64 / 128, fp32 / bf16 / INT8 caches and both inner paths,
+and grid sizes that force pairs to be split over workgroups (the cross-workgroup
+merge).  Full-size workloads are checked on sampled (sequence, kv-head) pairs
+in the launch configuration the benchmark uses.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import token_verify_attention_amd as tva
+from token_verify_attention_amd import workloads as wl
+from gpu_helpers import (assert_close, batch_of, np_, oracle_attn, paged_kv, rows_of_pairs,
+                         say)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+W = wl.Workload
+
+
+def _wk(name, Hq, Hkv, d, kv, q, sigma=1.0, ident=50):
+    return W(name, 1, Hq, Hkv, d, 0, 1, kv, q, sigma, None, None, False, ident)
+
+
+SMALL = [
+    # workload, ctx lengths, draft counts
+    (_wk("mha-bf16-d128", 8, 8, 128, "bf16", "bf16", ident=51), [0, 1, 15, 16, 17, 100, 300], [4, 1, 3, 4, 2, 4, 4]),
+    (_wk("gqa4-bf16-d128", 16, 4, 128, "bf16", "bf16", ident=52), [33, 250, 5, 64, 0], [8, 5, 1, 4, 3]),
+    (_wk("gqa8-int8-d128", 32, 4, 128, "int8", "bf16", 0.5, ident=53), [200, 17, 511, 3], [4, 3, 2, 1]),
+    (_wk("tiny-f32-d64", 4, 4, 64, "f32", "f32", ident=54), [128, 40, 0], [4, 3, 2]),
+    (_wk("gqa2-bf16-d64", 8, 4, 64, "bf16", "bf16", ident=55), [70, 1, 31], [7, 8, 2]),
+    (_wk("gqa4-int8-d64", 16, 4, 64, "int8", "f32", 0.5, ident=56), [90, 16, 47], [5, 4, 8]),
+    (_wk("rows128-bf16", 16, 2, 128, "bf16", "bf16", ident=57), [50, 3], [16, 16]),
+]
+
+
+def _case(w, ctx, ks, **kw):
+    return wl.make_case(w, device=DEV, ctx=ctx, k=ks, with_logits=False, **kw)
+
+
+def _kind(w):
+    return {"bf16": "bf16", "int8": "int8", "f32": "f32"}[w.kv_dtype]
+
+
+def _check(case, out, kind_dtype=None):
+    w = case["workload"]
+    kind = kind_dtype or w.kv_dtype
+    if kind == "int8":
+        ref_q = oracle_attn(case, quantised=True)
+        ref_u = oracle_attn(case, quantised=False)
+        assert_close(out, ref_q, "int8_deq")
+        return assert_close(out, ref_u, "int8")
+    ref = oracle_attn(case)
+    return assert_close(out, ref, "f32" if kind == "f32" else "bf16")
+
+
+@pytest.mark.parametrize("path", [0, 1, 2], ids=["auto", "valu", "mfma"])
+@pytest.mark.parametrize("spec", SMALL, ids=[s[0].name for s in SMALL])
+def test_small_cases(spec, path):
+    w, ctx, ks = spec
+    say(f"attn small {w.name} path={path}")
+    case = _case(w, ctx, ks)
+    kv = paged_kv(case)
+    out = tva.spec_verify_attn(batch_of(case), case["q"], kv, path=path)
+    torch.cuda.synchronize()
+    _check(case, out)
+
+
+@pytest.mark.parametrize("nwg", [1, 2, 3, 7, 64, 300])
+def test_pairs_split_over_workgroups(nwg):
+    w = _wk("split-gqa4", 16, 4, 128, "bf16", "bf16", ident=58)
+    say(f"attn split W={nwg}")
+    case = _case(w, [700, 33, 1, 260], [4, 8, 2, 3])
+    kv = paged_kv(case)
+    out = tva.spec_verify_attn(batch_of(case), case["q"], kv, num_workgroups=nwg)
+    torch.cuda.synchronize()
+    _check(case, out)
+
+
+def test_fp32_output_from_bf16_cache():
+    w = _wk("f32out", 16, 4, 128, "bf16", "bf16", ident=59)
+    case = _case(w, [300, 45], [4, 6])
+    out = tva.spec_verify_attn(batch_of(case), case["q"], paged_kv(case), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert out.dtype == torch.float32
+    _check(case, out)
+
+
+@pytest.mark.parametrize("kvd", ["bf16", "int8", "f32"])
+def test_poisoned_garbage_slots_and_pages_never_leak(kvd):
+    """NaN in every slot past S_b + k_b and in unreferenced pages; -1 in
+    unused block-table entries.  Outputs equal the unpoisoned run bitwise."""
+    w = _wk(f"poison-{kvd}", 16, 4, 128, kvd, "bf16", 0.5 if kvd == "int8" else 1.0, ident=60)
+    ctx, ks = [37, 250, 1, 16], [3, 8, 2, 4]
+    clean = _case(w, ctx, ks, extra_pages=5)
+    dirty = _case(w, ctx, ks, extra_pages=5, poison=True)
+    kv_c = paged_kv(clean)
+    if kvd == "int8":
+        kv_d = paged_kv(clean)              # same codes; poison the scales instead
+        for t in (kv_d.k_scale, kv_d.v_scale):
+            pb = dirty["block_table"].cpu()
+            for b, (c, k) in enumerate(zip(ctx, ks)):
+                used = c + k
+                if used % 16:
+                    t[int(pb[b, (used - 1) // 16]), :, used % 16:] = float("nan")
+    else:
+        kv_d = paged_kv(dirty)
+    a = tva.spec_verify_attn(batch_of(clean), clean["q"], kv_c)
+    b = tva.spec_verify_attn(batch_of(dirty), dirty["q"], kv_d)
+    torch.cuda.synchronize()
+    assert torch.isfinite(a.float()).all()
+    assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("kvd", ["bf16", "int8"])
+def test_later_drafts_do_not_change_earlier_queries(kvd):
+    w = _wk(f"prefix-{kvd}", 32, 4, 128, kvd, "bf16", ident=61)
+    ctx, ks = [77, 300], [6, 5]
+    case = _case(w, ctx, ks)
+    base = tva.spec_verify_attn(batch_of(case), case["q"], paged_kv(case)).clone()
+    bt = case["block_table"].cpu()
+    cu = case["cu_q"].cpu()
+    for b in range(2):
+        for j in range(ks[b] - 1):
+            pert = dict(case)
+            kp, vp = case["k_pool"].clone(), case["v_pool"].clone()
+            for jj in range(j + 1, ks[b]):
+                pos = ctx[b] + jj
+                pg = int(bt[b, pos // 16])
+                kp[pg, :, pos % 16] += 3.0
+                vp[pg, :, pos % 16] = 50.0
+            pert["k_pool"], pert["v_pool"] = kp, vp
+            got = tva.spec_verify_attn(batch_of(pert), case["q"], paged_kv(pert))
+            rows = slice(int(cu[b]), int(cu[b]) + j + 1)
+            assert torch.equal(got[rows], base[rows]), (b, j)
+
+
+def test_deterministic_across_runs():
+    w = _wk("det", 32, 8, 128, "bf16", "bf16", ident=62)
+    case = _case(w, [1000, 17, 400], [4, 8, 2])
+    kv = paged_kv(case)
+    outs = [tva.spec_verify_attn(batch_of(case), case["q"], kv, num_workgroups=5).clone()
+            for _ in range(3)]
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[1], outs[2])
+
+
+def test_zero_drafts():
+    w = _wk("zero", 8, 4, 128, "bf16", "bf16", ident=63)
+    case = _case(w, [30, 50, 70], [0, 3, 0])
+    out = tva.spec_verify_attn(batch_of(case), case["q"], paged_kv(case))
+    torch.cuda.synchronize()
+    _check(case, out)
+    empty = _case(w, [30, 50], [0, 0])
+    q = torch.empty((0, 8, 128), dtype=torch.bfloat16, device=DEV)
+    out = tva.spec_verify_attn(batch_of(empty), q, paged_kv(empty))
+    assert out.shape == (0, 8, 128)
+
+
+def _sample_pairs(case, n, seed):
+    w = case["workload"]
+    B, H = case["B"], w.Hkv
+    rng = np.random.default_rng(seed)
+    pairs = {(0, 0), (B - 1, H - 1)}
+    while len(pairs) < n:
+        pairs.add((int(rng.integers(B)), int(rng.integers(H))))
+    return sorted(pairs)
+
+
+@pytest.mark.parametrize("name", ["tiny", "mha7b", "gqa8b", "gqa70b_int8", "ragged"])
+def test_full_size_workloads_sampled(name):
+    w = wl.WORKLOADS[name]
+    say(f"attn full-size {name}: generating")
+    case = wl.make_case(w, device=DEV, with_logits=False)
+    batch = batch_of(case)
+    kv = paged_kv(case)
+    if w.append:
+        tva.kv_append(batch, case["k_new"], case["v_new"], kv)
+    out = tva.spec_verify_attn(batch, case["q"], kv)
+    torch.cuda.synchronize()
+    say(f"attn full-size {name}: kernel done, oracle on sampled pairs")
+    pairs = _sample_pairs(case, 6 if name != "tiny" else 8, 7)
+    if name == "tiny":
+        pairs = [(b, g) for b in range(w.B) for g in range(w.Hkv)]
+    kp, vp = np_(case["k_pool"]), np_(case["v_pool"])
+    ctx, cu, bt = np_(case["ctx_lens"]), np_(case["cu_q"]), np_(case["block_table"])
+    if w.append:
+        kp, vp, _, _ = oracle.kv_append(np_(case["k_new"]), np_(case["v_new"]), kp, vp, bt, ctx,
+                                        cu, w.kv_dtype)
+    scale = 1.0 / math.sqrt(w.d)
+    qn = np_(case["q"])
+    rows = rows_of_pairs(case, pairs)
+    if w.kv_dtype == "int8":
+        P, H = kp.shape[:2]
+        kc, ksc = oracle.kv_quant_int8(kp.reshape(-1, w.d))
+        vc, vsc = oracle.kv_quant_int8(vp.reshape(-1, w.d))
+        ref_q = oracle.spec_verify_attn(qn, kc.reshape(kp.shape), vc.reshape(vp.shape), bt, ctx,
+                                        cu, scale, k_scale=ksc.reshape(P, H, 16),
+                                        v_scale=vsc.reshape(P, H, 16), select=pairs)
+        ref_u = oracle.spec_verify_attn(qn, kp, vp, bt, ctx, cu, scale, select=pairs)
+        assert_close(out, ref_q, "int8_deq", rows)
+        assert_close(out, ref_u, "int8", rows)
+    else:
+        ref = oracle.spec_verify_attn(qn, kp, vp, bt, ctx, cu, scale, select=pairs)
+        assert_close(out, ref, "f32" if w.kv_dtype == "f32" else "bf16", rows)
+    assert torch.isfinite(out.float()).all()

@@ -1,0 +1,75 @@
+"""Build libspecverify.so (gfx950) in-tree with hipcc.
+
+    python -m token_verify_attention_amd.build
+
+Every HIP source under csrc/ is compiled for gfx950 only and linked into
+token_verify_attention_amd/_lib/libspecverify.so.  No fast-math: fp32
+division stays IEEE correctly rounded, which the INT8 codes depend on.
+"""
+import os
+import shutil
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+OUT_DIR = os.path.join(HERE, "_lib")
+LIB_NAME = "libspecverify.so"
+OBJ_DIR = os.path.join(ROOT, "_build")
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = "gfx950"
+
+# Packed fp32 VALU ops are kept out of every kernel on purpose.
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+COMMON_FLAGS = [
+    "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-mcode-object-version=5",
+    "-Wall", "-Wno-unused-function", "-I", INCLUDE, "-I", CSRC,
+]
+
+
+def sources():
+    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
+
+
+def compile_flags():
+    return COMMON_FLAGS + DEVICE_FLAGS
+
+
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    # hipcc's host pass does not know the device-only feature flag; drop that note.
+    lines = [ln for ln in res.stdout.splitlines() if "packed-fp32-ops" not in ln]
+    if res.returncode != 0 or (verbose and lines):
+        print("\n".join(lines), file=sys.stderr)
+    if res.returncode != 0:
+        raise RuntimeError(f"command failed ({res.returncode}): {' '.join(cmd)}")
+
+
+def build(verbose=False, jobs=4):
+    """Compile every HIP source and link the shared library.  Returns its path."""
+    if not os.path.exists(HIPCC):
+        raise RuntimeError(f"hipcc not found at {HIPCC}")
+    os.makedirs(OUT_DIR, exist_ok=True)
+    os.makedirs(OBJ_DIR, exist_ok=True)
+    srcs = sources()
+    objs = [os.path.join(OBJ_DIR, os.path.basename(s) + ".o") for s in srcs]
+    with ThreadPoolExecutor(max_workers=jobs) as ex:
+        futs = [ex.submit(_run, [HIPCC] + compile_flags() + ["-c", s, "-o", o], verbose)
+                for s, o in zip(srcs, objs)]
+        for f in futs:
+            f.result()
+    tmp = os.path.join(OUT_DIR, LIB_NAME + ".tmp")
+    _run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs, verbose)
+    final = os.path.join(OUT_DIR, LIB_NAME)
+    shutil.move(tmp, final)
+    return final
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,244 @@
+// C ABI of libspecverify: argument validation, device checks and dispatch.
+// Every entry point checks what the host can see before enqueuing anything;
+// see include/specverify.h for the contract of each call.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "launch.h"
+#include "specverify.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+sva_status fail(sva_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+sva_status fail(sva_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+sva_status hip_fail(hipError_t e, const char* where) {
+  return fail(SVA_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+constexpr int kMaxDevices = 64;
+struct DeviceInfo {
+  bool checked = false;
+  bool gfx950 = false;
+  int num_cus = 0;
+  std::string arch;
+};
+DeviceInfo g_dev[kMaxDevices];
+std::mutex g_dev_mu;
+
+// Info of the current device; false (with the error set) if unusable.
+sva_status current_device(const DeviceInfo** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(SVA_ERR_UNSUPPORTED, "device index %d", dev);
+  std::lock_guard<std::mutex> lock(g_dev_mu);
+  DeviceInfo& d = g_dev[dev];
+  if (!d.checked) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
+    d.arch = prop.gcnArchName;
+    d.gfx950 = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    d.num_cus = prop.multiProcessorCount;
+    d.checked = true;
+  }
+  if (!d.gfx950) return fail(SVA_ERR_UNSUPPORTED, "device arch %s is not gfx950", d.arch.c_str());
+  *out = &d;
+  return SVA_OK;
+}
+
+sva_status check_batch(const sva_batch* b) {
+  if (!b) return fail(SVA_ERR_INVALID_ARG, "batch is NULL");
+  if (b->B < 0) return fail(SVA_ERR_INVALID_ARG, "B = %d < 0", b->B);
+  if (b->B > 4096) return fail(SVA_ERR_UNSUPPORTED, "B = %d > 4096", b->B);
+  if (b->total_q < 0) return fail(SVA_ERR_INVALID_ARG, "total_q = %d < 0", b->total_q);
+  if (b->B > 0 && (!b->ctx_lens || !b->cu_q))
+    return fail(SVA_ERR_INVALID_ARG, "ctx_lens / cu_q is NULL");
+  if (b->total_q > 0 && b->max_q < 1)
+    return fail(SVA_ERR_INVALID_ARG, "max_q = %d but total_q = %d", b->max_q, b->total_q);
+  if (b->max_q > 16) return fail(SVA_ERR_UNSUPPORTED, "max_q = %d > 16", b->max_q);
+  if (b->max_q < 0) return fail(SVA_ERR_INVALID_ARG, "max_q = %d < 0", b->max_q);
+  if (int64_t(b->B) * b->max_q < b->total_q)
+    return fail(SVA_ERR_INVALID_ARG, "total_q = %d exceeds B * max_q", b->total_q);
+  if (b->max_len < 0) return fail(SVA_ERR_INVALID_ARG, "max_len = %d < 0", b->max_len);
+  return SVA_OK;
+}
+
+sva_status check_kv(const sva_paged_kv* kv, bool need_scales) {
+  if (!kv) return fail(SVA_ERR_INVALID_ARG, "kv is NULL");
+  if (!kv->k || !kv->v || !kv->block_table)
+    return fail(SVA_ERR_INVALID_ARG, "kv k / v / block_table is NULL");
+  if (kv->page_size != 16) return fail(SVA_ERR_UNSUPPORTED, "page_size = %d != 16", kv->page_size);
+  if (kv->Hkv < 1) return fail(SVA_ERR_INVALID_ARG, "Hkv = %d", kv->Hkv);
+  if (kv->num_pages < 1) return fail(SVA_ERR_INVALID_ARG, "num_pages = %d", kv->num_pages);
+  if (kv->max_pages_per_seq < 1)
+    return fail(SVA_ERR_INVALID_ARG, "max_pages_per_seq = %d", kv->max_pages_per_seq);
+  if (kv->kv_dtype != SVA_F32 && kv->kv_dtype != SVA_BF16 && kv->kv_dtype != SVA_INT8)
+    return fail(SVA_ERR_UNSUPPORTED, "kv_dtype = %d", kv->kv_dtype);
+  if (need_scales && kv->kv_dtype == SVA_INT8 && (!kv->k_scale || !kv->v_scale))
+    return fail(SVA_ERR_INVALID_ARG, "INT8 cache without k_scale / v_scale");
+  return SVA_OK;
+}
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+const char* sva_status_string(sva_status s) {
+  switch (s) {
+    case SVA_OK: return "SVA_OK";
+    case SVA_ERR_INVALID_ARG: return "SVA_ERR_INVALID_ARG";
+    case SVA_ERR_UNSUPPORTED: return "SVA_ERR_UNSUPPORTED";
+    case SVA_ERR_HIP: return "SVA_ERR_HIP";
+  }
+  return "unknown sva_status";
+}
+
+const char* sva_last_error(void) { return g_last_error.c_str(); }
+
+sva_status sva_kv_quant_int8(const void* x, int32_t src_dtype, int64_t rows, int32_t d,
+                             int8_t* codes, uint16_t* scales, void* stream) {
+  g_last_error.clear();
+  if (rows < 0) return fail(SVA_ERR_INVALID_ARG, "rows = %lld < 0", (long long)rows);
+  if (src_dtype != SVA_F32 && src_dtype != SVA_BF16)
+    return fail(SVA_ERR_UNSUPPORTED, "src_dtype = %d", src_dtype);
+  if (d != 64 && d != 128 && d != 256) return fail(SVA_ERR_UNSUPPORTED, "d = %d", d);
+  if (rows == 0) return SVA_OK;
+  if (!x || !codes || !scales) return fail(SVA_ERR_INVALID_ARG, "NULL pointer");
+  if (!aligned16(x) || !aligned16(codes) || (reinterpret_cast<uintptr_t>(scales) & 1))
+    return fail(SVA_ERR_INVALID_ARG, "x / codes must be 16-byte aligned, scales 2-byte aligned");
+  const DeviceInfo* dev;
+  if (sva_status s = current_device(&dev)) return s;
+  hipError_t e = sva::launch_kv_quant_int8(x, src_dtype, rows, d, codes, scales, as_stream(stream));
+  return e == hipSuccess ? SVA_OK : hip_fail(e, "kv_quant_int8 launch");
+}
+
+sva_status sva_kv_append(const sva_batch* batch, const void* k_new, const void* v_new,
+                         int32_t src_dtype, const sva_paged_kv* kv, void* stream) {
+  g_last_error.clear();
+  if (sva_status s = check_batch(batch)) return s;
+  if (sva_status s = check_kv(kv, true)) return s;
+  if (src_dtype != SVA_F32 && src_dtype != SVA_BF16)
+    return fail(SVA_ERR_UNSUPPORTED, "src_dtype = %d", src_dtype);
+  if (kv->d != 64 && kv->d != 128 && kv->d != 256) return fail(SVA_ERR_UNSUPPORTED, "d = %d", kv->d);
+  if (batch->total_q == 0 || batch->B == 0) return SVA_OK;
+  if (!k_new || !v_new) return fail(SVA_ERR_INVALID_ARG, "k_new / v_new is NULL");
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(kv->k) || !aligned16(kv->v))
+    return fail(SVA_ERR_INVALID_ARG, "K/V buffers must be 16-byte aligned");
+  const DeviceInfo* dev;
+  if (sva_status s = current_device(&dev)) return s;
+  hipError_t e = sva::launch_kv_append(batch, k_new, v_new, src_dtype, kv, as_stream(stream));
+  return e == hipSuccess ? SVA_OK : hip_fail(e, "kv_append launch");
+}
+
+static sva_status check_attn_shape(const sva_batch* batch, const sva_paged_kv* kv, int32_t Hq) {
+  if (sva_status s = check_batch(batch)) return s;
+  if (sva_status s = check_kv(kv, true)) return s;
+  if (kv->d != 64 && kv->d != 128) return fail(SVA_ERR_UNSUPPORTED, "d = %d (64 or 128)", kv->d);
+  if (Hq < 1 || Hq % kv->Hkv != 0)
+    return fail(SVA_ERR_INVALID_ARG, "Hq = %d is not a multiple of Hkv = %d", Hq, kv->Hkv);
+  const int64_t G = Hq / kv->Hkv;
+  if (G * batch->max_q > 128)
+    return fail(SVA_ERR_UNSUPPORTED, "max_q * G = %lld > 128", (long long)(G * batch->max_q));
+  const int64_t pages_ub =
+      int64_t(batch->B) * kv->Hkv * std::min<int64_t>(kv->max_pages_per_seq, (int64_t(batch->max_len) + 15) / 16);
+  if (pages_ub >= (int64_t(1) << 31) - 1)
+    return fail(SVA_ERR_UNSUPPORTED, "B * Hkv * pages = %lld too large", (long long)pages_ub);
+  return SVA_OK;
+}
+
+size_t sva_verify_workspace_bytes(const sva_batch* batch, const sva_paged_kv* kv, int32_t Hq,
+                                  const sva_verify_opts* opts) {
+  g_last_error.clear();
+  if (check_attn_shape(batch, kv, Hq) != SVA_OK) return 0;
+  const DeviceInfo* dev;
+  if (current_device(&dev) != SVA_OK) return 0;
+  return sva::plan_verify_attn(batch, kv, Hq, dev->num_cus, opts).total_bytes;
+}
+
+sva_status sva_spec_verify_attn(const sva_batch* batch, const void* q, int32_t q_dtype,
+                                int32_t Hq, const sva_paged_kv* kv, float softmax_scale,
+                                void* out, int32_t out_dtype, const sva_verify_opts* opts,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  if (sva_status s = check_attn_shape(batch, kv, Hq)) return s;
+  if (q_dtype != SVA_F32 && q_dtype != SVA_BF16)
+    return fail(SVA_ERR_UNSUPPORTED, "q_dtype = %d", q_dtype);
+  if (out_dtype != SVA_F32 && out_dtype != SVA_BF16)
+    return fail(SVA_ERR_UNSUPPORTED, "out_dtype = %d", out_dtype);
+  if (!(softmax_scale == softmax_scale) || softmax_scale == 0.f || !std::isfinite(softmax_scale))
+    return fail(SVA_ERR_INVALID_ARG, "softmax_scale must be finite and non-zero");
+  int path = opts ? opts->path : 0;
+  if (path < 0 || path > 2) return fail(SVA_ERR_INVALID_ARG, "opts->path = %d", path);
+  if (opts && opts->num_workgroups < 0)
+    return fail(SVA_ERR_INVALID_ARG, "opts->num_workgroups = %d", opts->num_workgroups);
+  if (batch->total_q == 0 || batch->B == 0) return SVA_OK;
+  if (!q || !out) return fail(SVA_ERR_INVALID_ARG, "q / out is NULL");
+  if (!aligned16(q) || !aligned16(out) || !aligned16(kv->k) || !aligned16(kv->v))
+    return fail(SVA_ERR_INVALID_ARG, "q / out / K / V must be 16-byte aligned");
+  if (kv->kv_dtype == SVA_INT8 && (!aligned16(kv->k_scale) || !aligned16(kv->v_scale)))
+    return fail(SVA_ERR_INVALID_ARG, "INT8 scales must be 16-byte aligned");
+  const DeviceInfo* dev;
+  if (sva_status s = current_device(&dev)) return s;
+  const sva::AttnPlan plan = sva::plan_verify_attn(batch, kv, Hq, dev->num_cus, opts);
+  if (!workspace || workspace_bytes < plan.total_bytes)
+    return fail(SVA_ERR_INVALID_ARG, "workspace of %zu bytes < %zu needed", workspace_bytes,
+                plan.total_bytes);
+  if (!aligned16(workspace)) return fail(SVA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  hipError_t e = sva::launch_verify_attn(batch, q, q_dtype, Hq, kv, softmax_scale, out, out_dtype,
+                                         path, plan, workspace, as_stream(stream));
+  return e == hipSuccess ? SVA_OK : hip_fail(e, "spec_verify_attn launch");
+}
+
+size_t sva_accept_workspace_bytes(const sva_batch* batch, int32_t V) {
+  g_last_error.clear();
+  if (check_batch(batch) != SVA_OK || V < 1) return 0;
+  return sva::plan_accept(batch, V).total_bytes;
+}
+
+sva_status sva_accept_prefix(const sva_batch* batch, const float* logits, int32_t V,
+                             const int32_t* draft_ids, int32_t* argmax_ids, int32_t* accept_len,
+                             int32_t* next_token, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  g_last_error.clear();
+  if (sva_status s = check_batch(batch)) return s;
+  if (V < 1) return fail(SVA_ERR_INVALID_ARG, "V = %d < 1", V);
+  if (batch->B == 0) return SVA_OK;
+  if (!logits || !argmax_ids || !accept_len || !next_token || (batch->total_q > 0 && !draft_ids))
+    return fail(SVA_ERR_INVALID_ARG, "NULL pointer");
+  const sva::AcceptPlan plan = sva::plan_accept(batch, V);
+  if (!workspace || workspace_bytes < plan.total_bytes)
+    return fail(SVA_ERR_INVALID_ARG, "workspace of %zu bytes < %zu needed", workspace_bytes,
+                plan.total_bytes);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 7) != 0)
+    return fail(SVA_ERR_INVALID_ARG, "workspace must be 8-byte aligned");
+  const DeviceInfo* dev;
+  if (sva_status s = current_device(&dev)) return s;
+  hipError_t e = sva::launch_accept_prefix(batch, logits, V, draft_ids, argmax_ids, accept_len,
+                                           next_token, plan, workspace, as_stream(stream));
+  return e == hipSuccess ? SVA_OK : hip_fail(e, "accept_prefix launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,269 @@
+// INT8 KV quantisation and KV append kernels for gfx950.
+//
+// Quantisation rule ("CXL-SpecKV", Algorithm 2, steps 3 and 5; key
+// observation (4)): per (token, head) row of d values,
+//   a = max|x|, scale = fp16_rne(a / 127), code = clamp(rne(fp32(x / scale)), +-127),
+// all codes 0 when the fp16 scale is 0.  The fp32 divisions are IEEE correctly
+// rounded (HIP's default division; no fast-math anywhere in this library).
+//
+// Layout: a row is handled by a group of 16 lanes, each holding d/16
+// consecutive values, so a wave covers 4 rows and every global access is a
+// contiguous 8..64-byte chunk per lane.
+#include "common.h"
+#include "launch.h"
+
+namespace sva {
+
+constexpr int kRowLanes = 16;
+constexpr int kQuantThreads = 256;
+constexpr int kRowsPerBlock = kQuantThreads / kRowLanes;   // 16
+
+template <typename T, int N>
+struct Chunk;
+template <int N>
+struct Chunk<float, N> {
+  __device__ static void load(const float* p, float* v) {
+    const u32x4* q = reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+    for (int i = 0; i < N / 4; ++i) {
+      u32x4 w = q[i];
+      v[4 * i + 0] = __uint_as_float(w[0]);
+      v[4 * i + 1] = __uint_as_float(w[1]);
+      v[4 * i + 2] = __uint_as_float(w[2]);
+      v[4 * i + 3] = __uint_as_float(w[3]);
+    }
+  }
+  __device__ static void store(float* p, const float* v) {
+    u32x4* q = reinterpret_cast<u32x4*>(p);
+#pragma unroll
+    for (int i = 0; i < N / 4; ++i) {
+      u32x4 w = {__float_as_uint(v[4 * i]), __float_as_uint(v[4 * i + 1]),
+                 __float_as_uint(v[4 * i + 2]), __float_as_uint(v[4 * i + 3])};
+      q[i] = w;
+    }
+  }
+};
+template <int N>
+struct Chunk<uint16_t, N> {   // bf16 bit patterns
+  __device__ static void load(const uint16_t* p, float* v) {
+    if constexpr (N % 8 == 0) {
+      const u32x4* q = reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+      for (int i = 0; i < N / 8; ++i) {
+        u32x4 w = q[i];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          v[8 * i + 2 * j] = bf16_lo(w[j]);
+          v[8 * i + 2 * j + 1] = bf16_hi(w[j]);
+        }
+      }
+    } else {
+      const u32x2* q = reinterpret_cast<const u32x2*>(p);
+      u32x2 w = q[0];
+      v[0] = bf16_lo(w[0]); v[1] = bf16_hi(w[0]);
+      v[2] = bf16_lo(w[1]); v[3] = bf16_hi(w[1]);
+    }
+  }
+  __device__ static void store(uint16_t* p, const float* v) {
+    if constexpr (N % 8 == 0) {
+      u32x4* q = reinterpret_cast<u32x4*>(p);
+#pragma unroll
+      for (int i = 0; i < N / 8; ++i) {
+        u32x4 w;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) w[j] = pack_bf16x2(v[8 * i + 2 * j], v[8 * i + 2 * j + 1]);
+        q[i] = w;
+      }
+    } else {
+      u32x2 w = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+      *reinterpret_cast<u32x2*>(p) = w;
+    }
+  }
+};
+
+// Quantise one row held by a 16-lane group (N = d/16 values per lane).
+// Returns the fp16 scale bits; writes the lane's N codes into `codes`.
+template <int N>
+__device__ __forceinline__ uint16_t quant_row(const float* v, int8_t* codes) {
+  float a = 0.f;
+#pragma unroll
+  for (int i = 0; i < N; ++i) a = fmaxf(a, fabsf(v[i]));
+  a = group_max<kRowLanes>(a);
+  const uint16_t s16 = f32_to_f16_bits(a / 127.0f);
+  const float s = f16_bits_to_f32(s16);
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    float c = 0.f;
+    if (s != 0.f) c = fminf(fmaxf(rintf(v[i] / s), -127.f), 127.f);
+    codes[i] = int8_t(int(c));
+  }
+  return s16;
+}
+
+template <int N>
+__device__ __forceinline__ void store_codes(int8_t* dst, const int8_t* c) {
+  uint32_t w[N / 4];
+#pragma unroll
+  for (int i = 0; i < N / 4; ++i)
+    w[i] = uint32_t(uint8_t(c[4 * i])) | (uint32_t(uint8_t(c[4 * i + 1])) << 8) |
+           (uint32_t(uint8_t(c[4 * i + 2])) << 16) | (uint32_t(uint8_t(c[4 * i + 3])) << 24);
+  if constexpr (N == 4) {
+    *reinterpret_cast<uint32_t*>(dst) = w[0];
+  } else if constexpr (N == 8) {
+    u32x2 x = {w[0], w[1]};
+    *reinterpret_cast<u32x2*>(dst) = x;
+  } else {
+    u32x4 x = {w[0], w[1], w[2], w[3]};
+    *reinterpret_cast<u32x4*>(dst) = x;
+  }
+}
+
+template <typename Src, int D>
+__global__ __launch_bounds__(kQuantThreads) void kv_quant_int8_kernel(
+    const Src* __restrict__ x, int64_t rows, int8_t* __restrict__ codes,
+    uint16_t* __restrict__ scales) {
+  constexpr int N = D / kRowLanes;
+  const int sub = threadIdx.x % kRowLanes;
+  for (int64_t row = int64_t(blockIdx.x) * kRowsPerBlock + threadIdx.x / kRowLanes; row < rows;
+       row += int64_t(gridDim.x) * kRowsPerBlock) {
+    float v[N];
+    Chunk<Src, N>::load(x + row * D + sub * N, v);
+    int8_t c[N];
+    const uint16_t s16 = quant_row<N>(v, c);
+    store_codes<N>(codes + row * D + sub * N, c);
+    if (sub == 0) scales[row] = s16;
+  }
+}
+
+// ---- append ----------------------------------------------------------------
+
+struct AppendParams {
+  const void* k_new;
+  const void* v_new;
+  void* k;
+  void* v;
+  uint16_t* k_scale;
+  uint16_t* v_scale;
+  const int32_t* block_table;
+  const int32_t* ctx_lens;
+  const int32_t* cu_q;
+  int32_t B, T, Hkv, num_pages, max_pages;
+};
+
+constexpr int kMaxLdsSeqs = 4096;
+
+template <typename Src, typename Dst, int D>
+__global__ __launch_bounds__(kQuantThreads) void kv_append_kernel(AppendParams p) {
+  constexpr int N = D / kRowLanes;
+  __shared__ int32_t s_cu[kMaxLdsSeqs + 1];
+  for (int i = threadIdx.x; i <= p.B; i += blockDim.x) s_cu[i] = p.cu_q[i];
+  __syncthreads();
+  const int sub = threadIdx.x % kRowLanes;
+  const int64_t n_rows = int64_t(p.T) * p.Hkv * 2;
+  for (int64_t r = int64_t(blockIdx.x) * kRowsPerBlock + threadIdx.x / kRowLanes; r < n_rows;
+       r += int64_t(gridDim.x) * kRowsPerBlock) {
+    const int which = int(r & 1);                 // 0: K, 1: V
+    const int64_t tg = r >> 1;
+    const int t = int(tg / p.Hkv);
+    const int g = int(tg % p.Hkv);
+    // sequence of draft row t: largest b with cu_q[b] <= t
+    int lo = 0, hi = p.B - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_cu[mid] <= t) lo = mid; else hi = mid - 1;
+    }
+    const int b = lo;
+    const int pos = p.ctx_lens[b] + (t - s_cu[b]);
+    const int lp = pos / kPage;
+    if (pos < 0 || lp >= p.max_pages) continue;   // out of contract: skip
+    const int page = p.block_table[int64_t(b) * p.max_pages + lp];
+    if (page < 0 || page >= p.num_pages) continue;
+    const int64_t dst_row = (int64_t(page) * p.Hkv + g) * kPage + (pos % kPage);
+    const Src* src = static_cast<const Src*>(which ? p.v_new : p.k_new) + tg * D + sub * N;
+    float v[N];
+    Chunk<Src, N>::load(src, v);
+    if constexpr (sizeof(Dst) == 1) {
+      int8_t c[N];
+      const uint16_t s16 = quant_row<N>(v, c);
+      int8_t* dst = static_cast<int8_t*>(which ? p.v : p.k);
+      store_codes<N>(dst + dst_row * D + sub * N, c);
+      if (sub == 0) (which ? p.v_scale : p.k_scale)[dst_row] = s16;
+    } else {
+      Dst* dst = static_cast<Dst*>(which ? p.v : p.k);
+      Chunk<Dst, N>::store(dst + dst_row * D + sub * N, v);
+    }
+  }
+}
+
+// ---- host launchers ----------------------------------------------------------
+
+static int grid_for_rows(int64_t rows) {
+  int64_t blocks = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
+  if (blocks > 65536) blocks = 65536;
+  return int(blocks < 1 ? 1 : blocks);
+}
+
+template <typename Src, int D>
+static hipError_t quant_launch(const void* x, int64_t rows, int8_t* codes, uint16_t* scales,
+                               hipStream_t st) {
+  hipLaunchKernelGGL((kv_quant_int8_kernel<Src, D>), dim3(grid_for_rows(rows)),
+                     dim3(kQuantThreads), 0, st, static_cast<const Src*>(x), rows, codes, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_quant_int8(const void* x, int src_dtype, int64_t rows, int d, int8_t* codes,
+                                uint16_t* scales, hipStream_t st) {
+  if (src_dtype == SVA_F32) {
+    if (d == 64) return quant_launch<float, 64>(x, rows, codes, scales, st);
+    if (d == 128) return quant_launch<float, 128>(x, rows, codes, scales, st);
+    return quant_launch<float, 256>(x, rows, codes, scales, st);
+  }
+  if (d == 64) return quant_launch<uint16_t, 64>(x, rows, codes, scales, st);
+  if (d == 128) return quant_launch<uint16_t, 128>(x, rows, codes, scales, st);
+  return quant_launch<uint16_t, 256>(x, rows, codes, scales, st);
+}
+
+template <typename Src, typename Dst, int D>
+static hipError_t append_launch(const AppendParams& p, hipStream_t st) {
+  const int64_t rows = int64_t(p.T) * p.Hkv * 2;
+  hipLaunchKernelGGL((kv_append_kernel<Src, Dst, D>), dim3(grid_for_rows(rows)),
+                     dim3(kQuantThreads), 0, st, p);
+  return hipGetLastError();
+}
+
+template <typename Src, typename Dst>
+static hipError_t append_d(const AppendParams& p, int d, hipStream_t st) {
+  if (d == 64) return append_launch<Src, Dst, 64>(p, st);
+  if (d == 128) return append_launch<Src, Dst, 128>(p, st);
+  return append_launch<Src, Dst, 256>(p, st);
+}
+
+template <typename Src>
+static hipError_t append_dst(const AppendParams& p, int kv_dtype, int d, hipStream_t st) {
+  if (kv_dtype == SVA_F32) return append_d<Src, float>(p, d, st);
+  if (kv_dtype == SVA_BF16) return append_d<Src, uint16_t>(p, d, st);
+  return append_d<Src, int8_t>(p, d, st);
+}
+
+hipError_t launch_kv_append(const sva_batch* batch, const void* k_new, const void* v_new,
+                            int src_dtype, const sva_paged_kv* kv, hipStream_t st) {
+  AppendParams p;
+  p.k_new = k_new;
+  p.v_new = v_new;
+  p.k = kv->k;
+  p.v = kv->v;
+  p.k_scale = static_cast<uint16_t*>(kv->k_scale);
+  p.v_scale = static_cast<uint16_t*>(kv->v_scale);
+  p.block_table = kv->block_table;
+  p.ctx_lens = batch->ctx_lens;
+  p.cu_q = batch->cu_q;
+  p.B = batch->B;
+  p.T = batch->total_q;
+  p.Hkv = kv->Hkv;
+  p.num_pages = kv->num_pages;
+  p.max_pages = kv->max_pages_per_seq;
+  if (src_dtype == SVA_F32) return append_dst<float>(p, kv->kv_dtype, kv->d, st);
+  return append_dst<uint16_t>(p, kv->kv_dtype, kv->d, st);
+}
+
+}  // namespace sva

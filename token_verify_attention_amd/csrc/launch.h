@@ -1,0 +1,48 @@
+// Internal launchers of libspecverify (host side).  Each enqueues kernels on
+// `st` and returns the launch status; argument checking happens in api.hip.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "specverify.h"
+
+namespace sva {
+
+hipError_t launch_kv_quant_int8(const void* x, int src_dtype, int64_t rows, int d, int8_t* codes,
+                                uint16_t* scales, hipStream_t st);
+
+hipError_t launch_kv_append(const sva_batch* batch, const void* k_new, const void* v_new,
+                            int src_dtype, const sva_paged_kv* kv, hipStream_t st);
+
+// Verification attention.  `num_wg` is the grid size; the workspace holds the
+// completion counters followed by the partial-result slots.
+struct AttnPlan {
+  int num_wg;
+  int slot_rows;
+  size_t counter_bytes;
+  size_t slot_bytes;
+  size_t total_bytes;
+};
+AttnPlan plan_verify_attn(const sva_batch* batch, const sva_paged_kv* kv, int Hq, int num_cus,
+                          const sva_verify_opts* opts);
+hipError_t launch_verify_attn(const sva_batch* batch, const void* q, int q_dtype, int Hq,
+                              const sva_paged_kv* kv, float softmax_scale, void* out,
+                              int out_dtype, int path, const AttnPlan& plan, void* workspace,
+                              hipStream_t st);
+
+// Acceptance: chunked argmax then a per-sequence scan.
+struct AcceptPlan {
+  int rows;
+  int chunks;
+  int chunk_len;
+  size_t total_bytes;
+};
+AcceptPlan plan_accept(const sva_batch* batch, int V);
+hipError_t launch_accept_prefix(const sva_batch* batch, const float* logits, int V,
+                                const int32_t* draft_ids, int32_t* argmax_ids, int32_t* accept_len,
+                                int32_t* next_token, const AcceptPlan& plan, void* workspace,
+                                hipStream_t st);
+
+}  // namespace sva
