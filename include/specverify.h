@@ -93,8 +93,9 @@ typedef struct {
 /* Optional tuning for sva_spec_verify_attn; pass NULL for the defaults.
  *   path            0: per sequence, VALU when k_b*G < 16 else MFMA (default)
  *                   1: VALU for every sequence     2: MFMA for every sequence
- *   num_workgroups  0: chosen from the device and batch; otherwise the grid size
- *                   (must equal the value used for the workspace size query) */
+ *   num_workgroups  0: chosen from the device and batch; otherwise the grid size,
+ *                   1 .. 4096 (must equal the value used for the workspace size
+ *                   query) */
 typedef struct {
   int32_t path;
   int32_t num_workgroups;
@@ -140,12 +141,14 @@ size_t sva_verify_workspace_bytes(const sva_batch *batch, const sva_paged_kv *kv
  *   q           device [T, Hq, d] of q_dtype (SVA_F32 or SVA_BF16)
  *   out         device [T, Hq, d] of out_dtype (SVA_F32 or SVA_BF16), written
  *   workspace   device, >= sva_verify_workspace_bytes(...) bytes.  Its first
- *               part holds completion counters: it must be all-zero before its
- *               first use, and every call leaves it all-zero again.  Calls that
+ *               16 KB hold completion counters (one per workgroup, for any grid
+ *               size): they must be all-zero before the workspace is first
+ *               used, and every call leaves them all-zero again, so one
+ *               workspace serves calls of any shape in stream order.  Calls that
  *               may run concurrently need distinct workspaces.
  * Supported: page_size 16, d in {64, 128}, Hq % Hkv == 0, max_q <= 16,
- * max_q * (Hq / Hkv) <= 128, B <= 4096; SVA_F32 caches use the VALU path and
- * need max_q * (Hq / Hkv) < 16. */
+ * max_q * (Hq / Hkv) <= 128, B <= 4096.  SVA_F32 caches always take the VALU
+ * path (query rows past 16 are handled in further passes over the pages). */
 sva_status sva_spec_verify_attn(const sva_batch *batch, const void *q, int32_t q_dtype,
                                 int32_t Hq, const sva_paged_kv *kv, float softmax_scale,
                                 void *out, int32_t out_dtype, const sva_verify_opts *opts,

@@ -177,6 +177,7 @@ def test_full_size_workloads_sampled(name):
     w = wl.WORKLOADS[name]
     say(f"attn full-size {name}: generating")
     case = wl.make_case(w, device=DEV, with_logits=False)
+    kp, vp = np_(case["k_pool"]), np_(case["v_pool"])        # before the GPU append
     batch = batch_of(case)
     kv = paged_kv(case)
     if w.append:
@@ -187,7 +188,6 @@ def test_full_size_workloads_sampled(name):
     pairs = _sample_pairs(case, 6 if name != "tiny" else 8, 7)
     if name == "tiny":
         pairs = [(b, g) for b in range(w.B) for g in range(w.Hkv)]
-    kp, vp = np_(case["k_pool"]), np_(case["v_pool"])
     ctx, cu, bt = np_(case["ctx_lens"]), np_(case["cu_q"]), np_(case["block_table"])
     if w.append:
         kp, vp, _, _ = oracle.kv_append(np_(case["k_new"]), np_(case["v_new"]), kp, vp, bt, ctx,
@@ -209,3 +209,21 @@ def test_full_size_workloads_sampled(name):
         ref = oracle.spec_verify_attn(qn, kp, vp, bt, ctx, cu, scale, select=pairs)
         assert_close(out, ref, "f32" if w.kv_dtype == "f32" else "bf16", rows)
     assert torch.isfinite(out.float()).all()
+
+
+def test_one_workspace_serves_calls_of_any_grid_size():
+    """Regression: partial slots of a call with a small grid must not land on
+    the completion counters of a later call with a larger grid."""
+    w = _wk("ws-reuse", 32, 8, 128, "bf16", "bf16", ident=64)
+    case = _case(w, [2000, 700, 33, 1500], [4, 8, 2, 3])
+    kv = paged_kv(case)
+    batch = batch_of(case)
+    nmax = max(tva.verify_workspace_bytes(batch, kv, w.Hq, num_workgroups=n)
+               for n in (3, 5, 17, 256, 1024))
+    ws = torch.zeros(nmax, dtype=torch.uint8, device=DEV)
+    ref = oracle_attn(case)
+    for n in (5, 256, 3, 1024, 17, 0):
+        out = tva.spec_verify_attn(batch, case["q"], kv, workspace=ws, num_workgroups=n)
+        torch.cuda.synchronize()
+        assert_close(out, ref, "bf16")
+        assert int(ws[:16384].count_nonzero()) == 0, n

@@ -192,8 +192,8 @@ sva_status sva_spec_verify_attn(const sva_batch* batch, const void* q, int32_t q
     return fail(SVA_ERR_INVALID_ARG, "softmax_scale must be finite and non-zero");
   int path = opts ? opts->path : 0;
   if (path < 0 || path > 2) return fail(SVA_ERR_INVALID_ARG, "opts->path = %d", path);
-  if (opts && opts->num_workgroups < 0)
-    return fail(SVA_ERR_INVALID_ARG, "opts->num_workgroups = %d", opts->num_workgroups);
+  if (opts && (opts->num_workgroups < 0 || opts->num_workgroups > 4096))
+    return fail(SVA_ERR_INVALID_ARG, "opts->num_workgroups = %d (0 .. 4096)", opts->num_workgroups);
   if (batch->total_q == 0 || batch->B == 0) return SVA_OK;
   if (!q || !out) return fail(SVA_ERR_INVALID_ARG, "q / out is NULL");
   if (!aligned16(q) || !aligned16(out) || !aligned16(kv->k) || !aligned16(kv->v))

@@ -88,7 +88,7 @@ __device__ __forceinline__ uint16_t quant_row(const float* v, int8_t* codes) {
   float a = 0.f;
 #pragma unroll
   for (int i = 0; i < N; ++i) a = fmaxf(a, fabsf(v[i]));
-  a = group_max<kRowLanes>(a);
+  a = row16_max(a);                 // a row is one 16-lane DPP row
   const uint16_t s16 = f32_to_f16_bits(a / 127.0f);
   const float s = f16_bits_to_f32(s16);
 #pragma unroll

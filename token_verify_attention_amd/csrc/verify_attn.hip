@@ -5,29 +5,36 @@
 // key observation (1)): for sequence b, draft query i and query head h (kv head
 // g = h / G), softmax(scale * q . K_p) V_p over positions p = 0 .. S_b + i.
 // Split-KV with an online softmax reaches exactly that result; every partial
-// carries (running max m, weight sum l, unnormalised output O).
+// carries (running max m, weight sum l, unnormalised output O), maxima in the
+// log2 domain (scores pre-multiplied by scale * log2 e, exp2 throughout).
 //
 // Work decomposition.  The pages of all (sequence, kv-head) pairs are laid end
-// to end; workgroup w streams the contiguous range [w*N/W, (w+1)*N/W) of
-// that list, which may cover the tail of one pair, whole pairs and the head of
-// another.  Every (b, g) segment is processed by the 4 waves of the workgroup,
-// each taking every 4th page, so the k_b*G query rows of the pair share each
-// K/V page load (the point of verification: one KV read amortised over all
-// drafts, same page, "Decoding Speculative Decoding...", sequence-parallel
-// section).  Waves merge through LDS.  A pair that spans several workgroups
-// leaves partials in the workspace; the last workgroup to finish the pair
-// (device-scope counter) merges them, so the whole call is one kernel.
+// to end; workgroup w streams the contiguous range [w*N/W, (w+1)*N/W) of that
+// list, which may cover the tail of one pair, whole pairs and the head of
+// another, so every workgroup moves the same number of pages.  Each (b, g)
+// segment is shared by the 4 waves of the workgroup, each taking every 4th
+// pair of consecutive pages, so the k_b*G query rows of the pair share every
+// K/V page load (one KV read amortised over all drafts and the GQA group:
+// "Decoding Speculative Decoding...", sequence-parallel section).  Waves merge
+// through LDS; a pair that spans several workgroups leaves partials in the
+// workspace and the last workgroup to finish it (device-scope counter) merges
+// them, so the whole call is one kernel.
 //
-// Per-wave inner loops:
-//  * VALU path (k_b*G < 16): K and V pages staged in LDS; lane = (token,
-//    quarter of d); fp32 dot products, online softmax over 16-lane groups,
-//    P.V with each lane owning d/64 output columns.
-//  * MFMA path (k_b*G >= 16, bf16 or INT8 cache): S^T = K Q^T with
-//    v_mfma_f32_16x16x32_bf16 (K rows loaded straight into the A operand),
-//    softmax in the MFMA output layout (a lane owns one query row and 4
-//    tokens), O^T += V^T P^T with v_mfma_f32_16x16x16_bf16, V^T read from a
-//    swizzled LDS copy of the page.  INT8 codes convert exactly to bf16; the
-//    per-token scales multiply the score (K) and the probability (V).
+// Memory pipeline.  Each wave owns a ring of LDS page slots filled by
+// global_load_lds_dwordx4 (HBM -> LDS without registers, 1 KB per wave
+// instruction, 16-byte chunks permuted per row so later LDS reads are free of
+// bank conflicts).  Steps of 2 pages are issued S steps ahead and waited for
+// with explicit vmcnt counts; page ids come from scalar loads.
+//
+// Inner loops per step (32 tokens):
+//  * VALU path (k_b*G < 16): lane = (token, half of d); bf16 dot2 products
+//    (INT8 codes convert exactly to bf16), online softmax over 32-lane groups,
+//    P.V with bf16 probability pairs and dot2, each lane owning d/64 columns.
+//    fp32 caches use plain fp32 FMAs.
+//  * MFMA path (k_b*G >= 16): S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (a
+//    lane owns one query row and 4 tokens of a page), O^T += V^T P^T with
+//    v_mfma_f32_16x16x16_bf16.  INT8 per-token scales multiply the score (K)
+//    and the probability (V).
 //
 // Positions at or past S_b + k_b (garbage slots of the last page) are masked
 // in the scores and zeroed in V, so NaN garbage never reaches an output.
@@ -40,11 +47,19 @@ namespace sva {
 
 constexpr int kAttnThreads = 256;
 constexpr int kWaves = kAttnThreads / kWave;   // 4
-constexpr int kMaxB = 4096;
+// The workspace starts with one completion counter per possible workgroup, at a
+// fixed size, so partial slots of one call never overlap the counters of a
+// later call with a different grid.
+constexpr int kMaxWorkgroups = 4096;
 constexpr int kMfmaRows = 32;
 constexpr int kValuRows = 16;
+constexpr int kRingBudget = 128 * 1024;        // LDS bytes for the page rings of 4 waves
 constexpr float kNegBig = -1.0e30f;            // finite start value of running maxima
 constexpr float kLog2e = 1.4426950408889634f;
+
+#define AS1 __attribute__((address_space(1)))
+#define AS3 __attribute__((address_space(3)))
+#define AS4 __attribute__((address_space(4)))
 
 struct AttnParams {
   const void* q;
@@ -101,25 +116,22 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// This thread's wave within the workgroup, as a wave-uniform (scalar) value.
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane(int(threadIdx.x) / kWave);
+}
+
 __device__ __forceinline__ int clamp_page(int pid, int num_pages) {
   return min(max(pid, 0), num_pages - 1);
 }
 
-// Page ids of pages j0, j0+4, ..., one per lane (0 past `pe`).
-__device__ __forceinline__ int load_page_ids(const AttnParams& p, const Seg& sg, int j0) {
-  const int j = j0 + kWaves * lane_id();
-  int pid = 0;
-  if (j < sg.pe) pid = p.block_table[int64_t(sg.b) * p.max_pages + j];
-  return clamp_page(pid, p.num_pages);
+// Physical page of logical page j of sequence b (a wave-uniform scalar load).
+__device__ __forceinline__ int page_id(const AttnParams& p, int b, int j) {
+  const AS4 int32_t* bt = (const AS4 int32_t*)p.block_table;
+  return clamp_page(bt[int64_t(b) * p.max_pages + j], p.num_pages);
 }
 
-// Element offset of (page, kv head g) in a [P, Hkv, 16, D] pool.
-template <int D>
-__device__ __forceinline__ int64_t page_off(const AttnParams& p, int pid, int g) {
-  return (int64_t(pid) * p.Hkv + g) * (kPage * D);
-}
-
-// Output / partial-slot addressing -------------------------------------------
+// ---- output and partial-slot addressing -----------------------------------
 
 __device__ __forceinline__ int64_t out_row(const AttnParams& p, const Seg& sg, int r) {
   const int i = r / p.G;
@@ -146,6 +158,479 @@ __device__ __forceinline__ void store_out1(const AttnParams& p, int64_t elem, fl
 }
 
 // ============================================================================
+// page ring: geometry, DMA and waits
+// ============================================================================
+
+template <typename KV, int D>
+struct Geo {
+  static constexpr int ES = int(sizeof(KV));
+  static constexpr int RB = D * ES;                  // bytes per K (or V) row
+  static constexpr int CPR = RB / 16;                // 16-byte chunks per row
+  static constexpr int PAGE = kPage * RB;            // bytes of one page of one head
+  static constexpr int SCALES = ES == 1 ? 64 : 0;    // INT8: 16 K + 16 V fp16 scales
+  static constexpr int SLOT = 2 * PAGE + SCALES;     // one ring slot: K page, V page, scales
+  static constexpr int DMA = PAGE / 1024;            // dwordx4 DMA instructions per page half
+  static constexpr int P = 2 * DMA + (ES == 1 ? 2 : 0);   // DMA instructions per page
+  static constexpr int S_RAW = kRingBudget / (kWaves * 2 * SLOT);
+  static constexpr int S = S_RAW < 1 ? 1 : (S_RAW > 3 ? 3 : S_RAW);   // steps held in the ring
+  static constexpr int RING = 2 * S * SLOT;          // bytes per wave
+};
+
+// Chunk permutations inside a row: K rows are read 16 rows x one chunk at a
+// time (XOR with the row), V rows 4 rows x two chunks (XOR with the row quad).
+template <int CPR>
+__device__ __forceinline__ int swz_k(int rho) { return rho & (CPR - 1); }
+template <int CPR>
+__device__ __forceinline__ int swz_v(int rho) { return ((rho >> 2) & 3) * (CPR >= 8 ? 2 : 1); }
+
+// Global -> LDS copies (lane l's 16 or 4 bytes land at l * 16 or l * 4 past
+// the wave-uniform LDS address in M0).  Issued through asm on purpose: for
+// the builtin, this compiler makes every later LDS read wait for all DMAs in
+// flight (vmcnt(0)), which would drain the ring at each step.  The ring's own
+// waits (wait_steps) order these copies against the reads; M0 is written
+// here, and one wait state separates the write from its use.
+__device__ __forceinline__ uint32_t lds_addr(const void* l) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((AS3 const void*)l));
+}
+__device__ __forceinline__ void dma16(const void* g, void* l) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               ::"v"(g), "s"(lds_addr(l)) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const void* g, void* l) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+               ::"v"(g), "s"(lds_addr(l)) : "memory", "m0");
+}
+
+// Page `pid` of kv head g -> ring slot (K page, V page, INT8 scales).
+template <typename KV, int D>
+__device__ __forceinline__ void dma_page(const AttnParams& p, int pid, int g, char* slot) {
+  using Gm = Geo<KV, D>;
+  const int lane = lane_id();
+  const int64_t off = (int64_t(pid) * p.Hkv + g) * Gm::PAGE;
+  const char* kb = static_cast<const char*>(p.k) + off;
+  const char* vb = static_cast<const char*>(p.v) + off;
+#pragma unroll
+  for (int e = 0; e < Gm::DMA; ++e) {
+    const int phys = kWave * e + lane;
+    const int rho = phys / Gm::CPR, phi = phys % Gm::CPR;
+    dma16(kb + rho * Gm::RB + (phi ^ swz_k<Gm::CPR>(rho)) * 16, slot + 1024 * e);
+    dma16(vb + rho * Gm::RB + (phi ^ swz_v<Gm::CPR>(rho)) * 16, slot + Gm::PAGE + 1024 * e);
+  }
+  if constexpr (Gm::ES == 1) {
+    const int64_t so = (int64_t(pid) * p.Hkv + g) * kPage;
+    if (lane < 8) {
+      dma4(reinterpret_cast<const char*>(p.k_scale + so) + 4 * lane, slot + 2 * Gm::PAGE);
+      dma4(reinterpret_cast<const char*>(p.v_scale + so) + 4 * lane, slot + 2 * Gm::PAGE + 32);
+    }
+  }
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// Wait until at most `pending` later steps (P2 DMA instructions each) are in flight.
+template <int P2, int S>
+__device__ __forceinline__ void wait_steps(int pending) {
+  if constexpr (S >= 3) {
+    if (pending >= 2) { wait_vm<2 * P2>(); return; }
+  }
+  if constexpr (S >= 2) {
+    if (pending >= 1) { wait_vm<P2>(); return; }
+  }
+  wait_vm<0>();
+}
+
+// Streams this wave's pages of the segment through its ring and calls
+// st.step(slot of page a, slot of page a+1, a, page a+1 exists) for each pair
+// of consecutive pages (a = pa + 2u, u = wave, wave + 4, ...).
+template <typename KV, int D>
+__device__ __forceinline__ void issue_step(const AttnParams& p, const Seg& sg, char* ring, int wave,
+                                           int s) {
+  using Gm = Geo<KV, D>;
+  const int a = sg.pa + 2 * (wave + kWaves * s);
+  const int ida = page_id(p, sg.b, a);
+  const int idb = (a + 1 < sg.pe) ? page_id(p, sg.b, a + 1) : ida;
+  char* slots = ring + (s % Gm::S) * 2 * Gm::SLOT;
+  dma_page<KV, D>(p, ida, sg.g, slots);
+  dma_page<KV, D>(p, idb, sg.g, slots + Gm::SLOT);
+}
+
+// Streams this wave's pages of the segment through its ring and calls
+// st.step(p, slot of page a, slot of page a+1, a, page a+1 exists) for each
+// pair of consecutive pages (a = pa + 2u, u = wave, wave + 4, ...).
+template <typename KV, int D, class Step>
+__device__ __forceinline__ void run_pages(const AttnParams& p, const Seg& sg, char* ring,
+                                          Step& st) {
+  using Gm = Geo<KV, D>;
+  constexpr int S = Gm::S, P2 = 2 * Gm::P;
+  const int wave = wave_id();
+  const int npair = (sg.pe - sg.pa + 1) >> 1;
+  const int n = npair > wave ? (npair - wave + kWaves - 1) / kWaves : 0;
+  const int pro = n < S ? n : S;
+  for (int s = 0; s < pro; ++s) issue_step<KV, D>(p, sg, ring, wave, s);
+  st.ready();
+  for (int s = 0; s < n; ++s) {
+    wait_steps<P2, S>(min(S - 1, n - 1 - s));
+    const char* slots = ring + (s % S) * 2 * Gm::SLOT;
+    const int a = sg.pa + 2 * (wave + kWaves * s);
+    st.step(p, slots, slots + Gm::SLOT, a, a + 1 < sg.pe);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // this step's LDS reads are done
+    if (s + S < n) issue_step<KV, D>(p, sg, ring, wave, s + S);
+  }
+}
+
+__device__ __forceinline__ uint32_t ld32(const char* a) { return *reinterpret_cast<const uint32_t*>(a); }
+__device__ __forceinline__ u32x2 ld64(const char* a) { return *reinterpret_cast<const u32x2*>(a); }
+__device__ __forceinline__ u32x4 ld128(const char* a) { return *reinterpret_cast<const u32x4*>(a); }
+
+// Two int8 codes (bytes at bit sh and sh+8 of w) as packed bf16 -- exact: |code| <= 127.
+__device__ __forceinline__ uint32_t codes2_to_bf16x2(uint32_t w, int sh) {
+  const float a = float(int(w << (24 - sh)) >> 24);
+  const float b = float(int(w << (16 - sh)) >> 24);
+  return (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xffff0000u);
+}
+__device__ __forceinline__ uint32_t ints_to_bf16x2(int lo, int hi) {
+  return (__float_as_uint(float(lo)) >> 16) | (__float_as_uint(float(hi)) & 0xffff0000u);
+}
+
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+  typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
+                                         __builtin_bit_cast(bf16x2, b), c, false);
+}
+
+// ============================================================================
+// VALU path
+// ============================================================================
+
+// Query rows r0 .. r0+15 of the pair into LDS.  fp32 caches: floats
+// q[(r*2 + half) * (D/2 + 4) + e]; otherwise bf16 pairs (fp32 Q rounds to
+// nearest even) q[(r*2 + half) * (D/4 + 4) + e].  The +4 pads put the two
+// halves on different banks.
+template <int D, bool F32>
+__device__ __forceinline__ void valu_stage_q(const AttnParams& p, const Seg& sg, int r0,
+                                             uint32_t* qs) {
+  constexpr int HALF = D / 2;
+  if constexpr (F32) {
+    constexpr int QS = HALF + 4;
+    for (int idx = threadIdx.x; idx < kValuRows * D; idx += kAttnThreads) {
+      const int r = idx / D, d = idx % D;
+      float v = 0.f;
+      if (r0 + r < sg.R) {
+        const int64_t e = out_row(p, sg, r0 + r) * D + d;
+        v = p.q_f32 ? static_cast<const float*>(p.q)[e]
+                    : bf16_to_f32(static_cast<const uint16_t*>(p.q)[e]);
+      }
+      qs[(r * 2 + d / HALF) * QS + d % HALF] = __float_as_uint(v);
+    }
+  } else {
+    constexpr int QS = HALF / 2 + 4;
+    for (int idx = threadIdx.x; idx < kValuRows * (D / 2); idx += kAttnThreads) {
+      const int r = idx / (D / 2), d2 = idx % (D / 2);       // pair of d = 2*d2, 2*d2+1
+      uint32_t w = 0;
+      if (r0 + r < sg.R) {
+        const int64_t e = out_row(p, sg, r0 + r) * D + 2 * d2;
+        if (p.q_f32) {
+          const float* qf = static_cast<const float*>(p.q);
+          w = pack_bf16x2(qf[e], qf[e + 1]);
+        } else {
+          w = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(p.q) + e);
+        }
+      }
+      qs[(r * 2 + (2 * d2) / HALF) * QS + d2 % (HALF / 2)] = w;
+    }
+  }
+}
+
+template <typename KV, int D, int RV>
+struct ValuStep {
+  using Gm = Geo<KV, D>;
+  static constexpr bool F32 = sizeof(KV) == 4;
+  static constexpr bool I8 = sizeof(KV) == 1;
+  static constexpr int HALF = D / 2;                  // d values per lane in QK
+  static constexpr int QS = F32 ? HALF + 4 : HALF / 2 + 4;
+  static constexpr int CPL = D / 64;                  // output columns per lane
+
+  const uint32_t* qs;
+  char* ps;                                           // [RV][32] probabilities (f32 or bf16)
+  float scale_log2;
+  float m[RV], l[RV], o[RV][CPL];
+  int lim[RV];
+  int valid_end;
+  int lane, t, h;
+
+  __device__ __forceinline__ ValuStep(const AttnParams& p, const Seg& sg, int r0, const uint32_t* qs_, char* ps_)
+      : qs(qs_), ps(ps_) {
+    scale_log2 = p.scale_log2;
+    lane = lane_id();
+    t = lane & 31;
+    h = lane >> 5;
+    valid_end = sg.S + sg.k;
+#pragma unroll
+    for (int r = 0; r < RV; ++r) {
+      m[r] = kNegBig;
+      l[r] = 0.f;
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) o[r][e] = 0.f;
+      lim[r] = (r0 + r < sg.R) ? sg.S + (r0 + r) / p.G : -1;
+    }
+  }
+
+  // scores of token t for every row: this lane's half of d, both halves summed
+  __device__ __forceinline__ void qk(const char* page, int row, float* s) {
+    const char* kr = page + row * Gm::RB;
+    if constexpr (F32) {
+      float kf[HALF];
+#pragma unroll
+      for (int e = 0; e < Gm::CPR / 2; ++e) {
+        const int kappa = h * (Gm::CPR / 2) + e;
+        const u32x4 w = ld128(kr + (kappa ^ swz_k<Gm::CPR>(row)) * 16);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) kf[4 * e + i] = __uint_as_float(w[i]);
+      }
+#pragma unroll
+      for (int r = 0; r < RV; ++r) {
+        const uint32_t* q = qs + (r * 2 + h) * QS;
+        float a = 0.f;
+#pragma unroll
+        for (int e4 = 0; e4 < HALF / 4; ++e4) {
+          const u32x4 qv = *reinterpret_cast<const u32x4*>(q + 4 * e4);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) a = fmaf(__uint_as_float(qv[i]), kf[4 * e4 + i], a);
+        }
+        s[r] = a;
+      }
+    } else {
+      uint32_t kx[HALF / 2];                          // bf16 pairs of this lane's half row
+      if constexpr (I8) {
+#pragma unroll
+        for (int e = 0; e < Gm::CPR / 2; ++e) {       // 16 codes per chunk
+          const int kappa = h * (Gm::CPR / 2) + e;
+          const u32x4 w = ld128(kr + (kappa ^ swz_k<Gm::CPR>(row)) * 16);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            kx[8 * e + 2 * i] = codes2_to_bf16x2(w[i], 0);
+            kx[8 * e + 2 * i + 1] = codes2_to_bf16x2(w[i], 16);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < Gm::CPR / 2; ++e) {       // 8 bf16 per chunk
+          const int kappa = h * (Gm::CPR / 2) + e;
+          const u32x4 w = ld128(kr + (kappa ^ swz_k<Gm::CPR>(row)) * 16);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) kx[4 * e + i] = w[i];
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < RV; ++r) {
+        const uint32_t* q = qs + (r * 2 + h) * QS;
+        float a = 0.f;
+#pragma unroll
+        for (int e4 = 0; e4 < HALF / 8; ++e4) {
+          const u32x4 qv = *reinterpret_cast<const u32x4*>(q + 4 * e4);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) a = dot2(kx[4 * e4 + i], qv[i], a);
+        }
+        s[r] = a;
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < RV; ++r) s[r] = xrow32_sum(s[r]);      // the two halves of d
+  }
+
+  // O[r][cols] += sum over the 32 tokens of p[r][t] V[t][cols]
+  template <bool kMask>
+  __device__ __forceinline__ void pv(const char* sa, const char* sb, int a, bool second) {
+    if constexpr (F32) {
+      const float* pf = reinterpret_cast<const float*>(ps);
+#pragma unroll
+      for (int t0 = 0; t0 < 32; t0 += 4) {
+        float vv[4][CPL];
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+          const int tok = t0 + tt, row = tok & 15;
+          const char* vr = ((tok < 16) ? sa : sb) + Gm::PAGE + row * Gm::RB;
+          const int cb = lane * CPL * 4;
+          const char* src = vr + ((cb / 16) ^ swz_v<Gm::CPR>(row)) * 16 + cb % 16;
+#pragma unroll
+          for (int e = 0; e < CPL; ++e) vv[tt][e] = reinterpret_cast<const float*>(src)[e];
+          if constexpr (kMask) {
+            const bool ok = (tok < 16 || second) && ((a + (tok >> 4)) * kPage + row < valid_end);
+#pragma unroll
+            for (int e = 0; e < CPL; ++e) vv[tt][e] = ok ? vv[tt][e] : 0.f;
+          }
+        }
+#pragma unroll
+        for (int r = 0; r < RV; ++r) {
+          const f32x4 pw = *reinterpret_cast<const f32x4*>(pf + r * 32 + t0);
+#pragma unroll
+          for (int tt = 0; tt < 4; ++tt) {
+#pragma unroll
+            for (int e = 0; e < CPL; ++e) o[r][e] = fmaf(pw[tt], vv[tt][e], o[r][e]);
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int tq = 0; tq < 16; tq += 4) {            // 4 token pairs = 8 tokens
+        uint32_t vp[4][CPL];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int tok = 2 * (tq + u), row = tok & 15;
+          const char* vr = ((tok < 16) ? sa : sb) + Gm::PAGE;
+          const char* r0p = vr + row * Gm::RB;
+          const char* r1p = vr + (row + 1) * Gm::RB;
+          if constexpr (I8) {
+            const int cb = lane * CPL;                // byte of this lane's first column
+            const int kap = cb / 16, wi = cb % 16;
+            const char* s0 = r0p + (kap ^ swz_v<Gm::CPR>(row)) * 16 + wi;
+            const char* s1 = r1p + (kap ^ swz_v<Gm::CPR>(row + 1)) * 16 + wi;
+            if constexpr (CPL == 2) {
+              const int c00 = reinterpret_cast<const int8_t*>(s0)[0];
+              const int c01 = reinterpret_cast<const int8_t*>(s0)[1];
+              const int c10 = reinterpret_cast<const int8_t*>(s1)[0];
+              const int c11 = reinterpret_cast<const int8_t*>(s1)[1];
+              vp[u][0] = ints_to_bf16x2(c00, c10);
+              vp[u][CPL - 1] = ints_to_bf16x2(c01, c11);
+            } else {
+              vp[u][0] = ints_to_bf16x2(reinterpret_cast<const int8_t*>(s0)[0],
+                                        reinterpret_cast<const int8_t*>(s1)[0]);
+            }
+          } else {
+            const int cb = lane * CPL * 2;
+            const int kap = cb / 16, wi = cb % 16;
+            const char* s0 = r0p + (kap ^ swz_v<Gm::CPR>(row)) * 16 + wi;
+            const char* s1 = r1p + (kap ^ swz_v<Gm::CPR>(row + 1)) * 16 + wi;
+            if constexpr (CPL == 2) {
+              const uint32_t w0 = ld32(s0), w1 = ld32(s1);
+              vp[u][0] = __builtin_amdgcn_perm(w1, w0, 0x05040100u);
+              vp[u][CPL - 1] = __builtin_amdgcn_perm(w1, w0, 0x07060302u);
+            } else {
+              vp[u][0] = uint32_t(*reinterpret_cast<const uint16_t*>(s0)) |
+                         (uint32_t(*reinterpret_cast<const uint16_t*>(s1)) << 16);
+            }
+            if constexpr (kMask) {
+              const int pos0 = (a + (tok >> 4)) * kPage + row;
+              const bool pg_ok = tok < 16 || second;
+              const uint32_t keep = ((pg_ok && pos0 < valid_end) ? 0x0000ffffu : 0u) |
+                                    ((pg_ok && pos0 + 1 < valid_end) ? 0xffff0000u : 0u);
+#pragma unroll
+              for (int e = 0; e < CPL; ++e) vp[u][e] &= keep;
+            }
+          }
+        }
+#pragma unroll
+        for (int r = 0; r < RV; ++r) {
+          const u32x4 pp = ld128(ps + r * 64 + tq * 4);  // probability pairs of 4 token pairs
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+#pragma unroll
+            for (int e = 0; e < CPL; ++e) o[r][e] = dot2(pp[u], vp[u][e], o[r][e]);
+          }
+        }
+      }
+    }
+  }
+
+  __device__ __forceinline__ void step(const AttnParams&, const char* sa, const char* sb, int a,
+                                       bool second) {
+    const char* page = (t < 16) ? sa : sb;
+    const int row = t & 15;
+    const int pos = (a + (t >> 4)) * kPage + row;
+    const bool tok_ok = (t < 16) || second;
+    float s[RV];
+    qk(page, row, s);
+    float ksc = 1.f, vsc = 1.f;
+    if constexpr (I8) {
+      const uint16_t* sc = reinterpret_cast<const uint16_t*>(page + 2 * Gm::PAGE);
+      ksc = f16_bits_to_f32(sc[row]);
+      vsc = (tok_ok && pos < valid_end) ? f16_bits_to_f32(sc[16 + row]) : 0.f;
+    }
+#pragma unroll
+    for (int r = 0; r < RV; ++r) {
+      const float x = (tok_ok && pos <= lim[r]) ? s[r] * scale_log2 * ksc : -INFINITY;
+      const float mx = xrow16_max(row16_max(x));                // over the 32 tokens
+      const float mn = fmaxf(m[r], mx);
+      const float alpha = exp2f(m[r] - mn);
+      m[r] = mn;
+      const float e = exp2f(x - mn);
+      l[r] = l[r] * alpha + e;
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) o[r][c] *= alpha;
+      if (h == 0) {
+        if constexpr (F32) reinterpret_cast<float*>(ps)[r * 32 + t] = e * vsc;
+        else reinterpret_cast<uint16_t*>(ps)[r * 32 + t] = f32_to_bf16(e * vsc);
+      }
+    }
+    wave_sync();
+    // garbage rows exist only in the pair's last page and in a missing second page
+    const bool mask = !second || (a + 2) * kPage > valid_end;
+    if (mask) pv<true>(sa, sb, a, second);
+    else pv<false>(sa, sb, a, second);
+    wave_sync();
+  }
+
+  // Queries come from LDS, nothing to wait for.
+  __device__ __forceinline__ void ready() const {}
+  __device__ __forceinline__ void finish() {
+#pragma unroll
+    for (int r = 0; r < RV; ++r) l[r] = xrow16_sum(row16_sum(l[r]));
+  }
+
+  static constexpr int SLOT_F = RV * kWave * CPL + 2 * RV;
+  __device__ __forceinline__ void store(float* slot) const {
+#pragma unroll
+    for (int r = 0; r < RV; ++r) {
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) slot[(r * kWave + lane) * CPL + e] = o[r][e];
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int r = 0; r < RV; ++r) {
+        slot[RV * kWave * CPL + r] = m[r];
+        slot[RV * kWave * CPL + RV + r] = l[r];
+      }
+    }
+  }
+  __device__ __forceinline__ void combine(const float* slot) {
+#pragma unroll
+    for (int r = 0; r < RV; ++r) {
+      const float mo = slot[RV * kWave * CPL + r];
+      const float lo = slot[RV * kWave * CPL + RV + r];
+      const float M = fmaxf(m[r], mo);
+      const float fa = exp2f(m[r] - M), fb = exp2f(mo - M);
+      l[r] = fa * l[r] + fb * lo;
+      m[r] = M;
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) o[r][e] = fa * o[r][e] + fb * slot[(r * kWave + lane) * CPL + e];
+    }
+  }
+  __device__ __forceinline__ void write(const AttnParams& p, const Seg& sg, int r0) const {
+#pragma unroll
+    for (int r = 0; r < RV; ++r) {
+      const int rr = r0 + r;
+      if (rr >= sg.R) continue;
+      if (sg.full) {
+        const float inv = 1.f / l[r];
+        const int64_t oe = out_row(p, sg, rr) * D + lane * CPL;
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) store_out1(p, oe + e, o[r][e] * inv);
+      } else {
+        float* sb = slot_base<D>(p, sg.slot);
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) sb[int64_t(rr) * D + lane * CPL + e] = o[r][e];
+        if (lane == 0) {
+          sb[int64_t(p.slot_rows) * D + rr] = m[r];
+          sb[int64_t(p.slot_rows) * (D + 1) + rr] = l[r];
+        }
+      }
+    }
+  }
+};
+
+// ============================================================================
 // MFMA path
 // ============================================================================
 
@@ -165,306 +650,241 @@ __device__ __forceinline__ bf16x8 load_q8_bf16(const AttnParams& p, int64_t elem
   return __builtin_bit_cast(bf16x8, w);
 }
 
-// Two int8 codes (low 16 bits of w >> sh) as packed bf16 -- exact: |code| <= 127.
-__device__ __forceinline__ uint32_t codes2_to_bf16x2(uint32_t w, int sh) {
-  const float a = float(int(w << (24 - sh)) >> 24);
-  const float b = float(int(w << (16 - sh)) >> 24);
-  return (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xffff0000u);
-}
-
-// 16 int8 codes (one 16-byte word) -> 16 bf16 (two 16-byte words).
-__device__ __forceinline__ void codes16_to_bf16(u32x4 c, u32x4& lo, u32x4& hi) {
-#pragma unroll
-  for (int e = 0; e < 2; ++e) {
-    lo[2 * e] = codes2_to_bf16x2(c[e], 0);
-    lo[2 * e + 1] = codes2_to_bf16x2(c[e], 16);
-    hi[2 * e] = codes2_to_bf16x2(c[2 + e], 0);
-    hi[2 * e + 1] = codes2_to_bf16x2(c[2 + e], 16);
-  }
-}
-
-// Registers holding one page for one wave (MFMA path).
-//  K: lane (l16, c) holds row l16, d in [c*D/4, (c+1)*D/4)  (D/4 values)
-//  V: 16-byte chunks id = lane + 64*e of the page in row-major order
-template <typename KV, int D>
-struct MfmaPage {
-  static constexpr int KBYTES = (D / 4) * int(sizeof(KV));   // per lane
-  static constexpr int KCH = KBYTES / 16;                    // 16-byte loads for K
-  static constexpr int VCH = kPage * D * int(sizeof(KV)) / 16 / kWave;
-  u32x4 k[KCH];
-  u32x4 v[VCH];
-  f32x4 ksc, vsc;                                            // INT8: tokens 4c..4c+3 (unused otherwise)
-};
-
-template <typename KV, int D>
-__device__ __forceinline__ void mfma_load_page(const AttnParams& p, int pid, int g,
-                                               MfmaPage<KV, D>& pg) {
-  const int lane = lane_id(), l16 = lane & 15, c = lane >> 4;
-  const int64_t off = page_off<D>(p, pid, g);
-  const KV* kb = static_cast<const KV*>(p.k) + off;
-  const KV* vb = static_cast<const KV*>(p.v) + off;
-  const u32x4* kp = reinterpret_cast<const u32x4*>(kb + l16 * D + c * (D / 4));
-#pragma unroll
-  for (int e = 0; e < MfmaPage<KV, D>::KCH; ++e) pg.k[e] = kp[e];
-  const u32x4* vp = reinterpret_cast<const u32x4*>(vb);
-#pragma unroll
-  for (int e = 0; e < MfmaPage<KV, D>::VCH; ++e) pg.v[e] = vp[lane + kWave * e];
-  if constexpr (sizeof(KV) == 1) {
-    const int64_t so = (int64_t(pid) * p.Hkv + g) * kPage + 4 * c;
-    const u32x2 ks = *reinterpret_cast<const u32x2*>(p.k_scale + so);
-    const u32x2 vs = *reinterpret_cast<const u32x2*>(p.v_scale + so);
-    pg.ksc = f32x4{f16_bits_to_f32(uint16_t(ks[0])), f16_bits_to_f32(uint16_t(ks[0] >> 16)),
-                   f16_bits_to_f32(uint16_t(ks[1])), f16_bits_to_f32(uint16_t(ks[1] >> 16))};
-    pg.vsc = f32x4{f16_bits_to_f32(uint16_t(vs[0])), f16_bits_to_f32(uint16_t(vs[0] >> 16)),
-                   f16_bits_to_f32(uint16_t(vs[1])), f16_bits_to_f32(uint16_t(vs[1] >> 16))};
-  }
-}
-
-// V page -> LDS as bf16 [16][D]; logical 16-byte chunk kappa of row rho sits at
-// physical chunk kappa ^ (2 * ((rho >> 2) & 3)), so the transposed reads of the
-// PV step hit distinct banks.  Rows at or past `valid` are written as zeros.
-template <int D>
-__device__ __forceinline__ void v_lds_store_chunk(uint16_t* vl, int rho, int kappa, u32x4 w,
-                                                  bool zero) {
-  constexpr int CPR = D * 2 / 16;
-  if (zero) w = u32x4{0u, 0u, 0u, 0u};
-  const int phys = kappa ^ (2 * ((rho >> 2) & 3));
-  *reinterpret_cast<u32x4*>(vl + rho * D + phys * 8) = w;
-  (void)CPR;
-}
-
-template <typename KV, int D>
-__device__ __forceinline__ void mfma_stage_v(uint16_t* vl, const MfmaPage<KV, D>& pg,
-                                             int valid_in_page) {
-  const int lane = lane_id();
-  if constexpr (sizeof(KV) == 2) {
-    constexpr int CPR = D * 2 / 16;                       // bf16 chunks per row
-#pragma unroll
-    for (int e = 0; e < MfmaPage<KV, D>::VCH; ++e) {
-      const int id = lane + kWave * e;
-      const int rho = id / CPR, kappa = id % CPR;
-      v_lds_store_chunk<D>(vl, rho, kappa, pg.v[e], rho >= valid_in_page);
-    }
-  } else {
-    constexpr int CPR8 = D / 16;                          // int8 chunks per row
-#pragma unroll
-    for (int e = 0; e < MfmaPage<KV, D>::VCH; ++e) {
-      const int id = lane + kWave * e;
-      const int rho = id / CPR8, kappa8 = id % CPR8;
-      u32x4 lo, hi;
-      codes16_to_bf16(pg.v[e], lo, hi);
-      v_lds_store_chunk<D>(vl, rho, 2 * kappa8, lo, rho >= valid_in_page);
-      v_lds_store_chunk<D>(vl, rho, 2 * kappa8 + 1, hi, rho >= valid_in_page);
-    }
-  }
-}
-
-// A operand of S^T = K Q^T for k-step ks: 8 bf16 of this lane's K row.
-template <typename KV, int D>
-__device__ __forceinline__ bf16x8 mfma_k_operand(const MfmaPage<KV, D>& pg, int ks) {
-  if constexpr (sizeof(KV) == 2) {
-    // lane holds D/4 bf16 = KCH 16-byte words; word ks covers d c*D/4 + 8ks .. +8
-    return __builtin_bit_cast(bf16x8, pg.k[ks]);
-  } else {
-    // lane holds D/4 codes; codes 8ks .. 8ks+8 -> bf16
-    const u32x4 w = pg.k[ks / 2];
-    const int base = (ks & 1) * 2;
-    u32x4 r;
-    r[0] = codes2_to_bf16x2(w[base], 0);
-    r[1] = codes2_to_bf16x2(w[base], 16);
-    r[2] = codes2_to_bf16x2(w[base + 1], 0);
-    r[3] = codes2_to_bf16x2(w[base + 1], 16);
-    return __builtin_bit_cast(bf16x8, r);
-  }
-}
-
-template <int NRB, int NDB>
-struct MfmaState {
-  f32x4 acc[NRB][NDB];
-  float m[NRB], l[NRB];
-};
-
-template <int NRB, int NDB>
-__device__ __forceinline__ void mfma_state_store(float* slot, const MfmaState<NRB, NDB>& st) {
-  const int lane = lane_id();
-#pragma unroll
-  for (int rb = 0; rb < NRB; ++rb) {
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-      *reinterpret_cast<f32x4*>(slot + ((rb * NDB + db) * kWave + lane) * 4) = st.acc[rb][db];
-    slot[NRB * NDB * kWave * 4 + rb * kWave + lane] = st.m[rb];
-    slot[NRB * NDB * kWave * 4 + (NRB + rb) * kWave + lane] = st.l[rb];
-  }
-}
-
-template <int NRB, int NDB>
-__device__ __forceinline__ void mfma_state_combine(const float* slot, MfmaState<NRB, NDB>& st) {
-  const int lane = lane_id();
-#pragma unroll
-  for (int rb = 0; rb < NRB; ++rb) {
-    const float mo = slot[NRB * NDB * kWave * 4 + rb * kWave + lane];
-    const float lo = slot[NRB * NDB * kWave * 4 + (NRB + rb) * kWave + lane];
-    const float M = fmaxf(st.m[rb], mo);
-    const float fa = exp2f(st.m[rb] - M), fb = exp2f(mo - M);
-    st.l[rb] = fa * st.l[rb] + fb * lo;
-    st.m[rb] = M;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      const f32x4 o = *reinterpret_cast<const f32x4*>(slot + ((rb * NDB + db) * kWave + lane) * 4);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) st.acc[rb][db][i] = fa * st.acc[rb][db][i] + fb * o[i];
-    }
-  }
-}
-
 template <typename KV, int D, int NRB>
-__device__ __forceinline__ void mfma_pass(const AttnParams& p, const Seg& sg, int r0,
-                                          uint16_t* vl, float* mrg) {
-  constexpr int KS = D / 32;        // 16x16x32 k-steps over d
-  constexpr int NDB = D / 16;       // 16-column blocks of d
-  const int lane = lane_id(), wave = threadIdx.x / kWave;
-  const int l16 = lane & 15, c = lane >> 4;
-  const int G = p.G;
+struct MfmaStep {
+  using Gm = Geo<KV, D>;
+  static constexpr bool I8 = sizeof(KV) == 1;
+  static constexpr int KS = D / 32;       // 16x16x32 k-steps over d
+  static constexpr int NDB = D / 16;      // 16-column blocks of d
 
-  // Q^T operand: lane (l16, c) holds row r0 + 16 rb + l16, d in [c*D/4 + 8ks, +8)
-  bf16x8 qB[NRB][KS];
-  int lim[NRB];                      // last visible position of the lane's row, -1 if padding
-#pragma unroll
-  for (int rb = 0; rb < NRB; ++rb) {
-    const int r = r0 + 16 * rb + l16;
-    lim[rb] = -1;
-    if (r < sg.R) {
-      lim[rb] = sg.S + r / G;
-      const int64_t qe = out_row(p, sg, r) * D + c * (D / 4);
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) qB[rb][ks] = load_q8_bf16(p, qe + 8 * ks);
-    } else {
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) qB[rb][ks] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
-    }
-  }
+  bf16x8 qB[NRB][KS];                     // lane (l16, c): row 16 rb + l16, d c*D/4 + 8ks .. +8
+  f32x4 acc[NRB][NDB];                    // O^T: d 16 db + 4c + i, row 16 rb + l16
+  float m[NRB], l[NRB];
+  int lim[NRB];
+  int valid_end;
+  int lane, l16, c;
+  float scale_log2;
 
-  MfmaState<NRB, NDB> st;
-#pragma unroll
-  for (int rb = 0; rb < NRB; ++rb) {
-    st.m[rb] = kNegBig;
-    st.l[rb] = 0.f;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) st.acc[rb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-
-  const int valid_end = sg.S + sg.k;
-  int j = sg.pa + wave;
-  int ids = 0, id_base = j;
-  MfmaPage<KV, D> cur, nxt;
-  if (j < sg.pe) {
-    ids = load_page_ids(p, sg, id_base);
-    mfma_load_page<KV, D>(p, readlane(ids, 0), sg.g, cur);
-  }
-  for (int e = 0; j < sg.pe; j += kWaves, ++e) {
-    mfma_stage_v<KV, D>(vl, cur, valid_end - j * kPage);
-    const int jn = j + kWaves;
-    if (jn < sg.pe) {
-      if (e + 1 == kWave) {
-        id_base = jn;
-        ids = load_page_ids(p, sg, id_base);
-        e = -1;
-      }
-      mfma_load_page<KV, D>(p, readlane(ids, e + 1), sg.g, nxt);
-    }
-    // ---- scores S^T[token 4c+i][row l16] for every row block
-    f32x4 s[NRB];
-#pragma unroll
-    for (int rb = 0; rb < NRB; ++rb) s[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8 a = mfma_k_operand<KV, D>(cur, ks);
-#pragma unroll
-      for (int rb = 0; rb < NRB; ++rb)
-        s[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qB[rb][ks], s[rb], 0, 0, 0);
-    }
-    // ---- online softmax; the lane owns row l16 (+16 rb) and tokens 4c..4c+3
-    const int pos0 = j * kPage + 4 * c;
-    i16x4 pB[NRB];
+  __device__ __forceinline__ MfmaStep(const AttnParams& p, const Seg& sg, int r0) {
+    scale_log2 = p.scale_log2;
+    lane = lane_id();
+    l16 = lane & 15;
+    c = lane >> 4;
+    valid_end = sg.S + sg.k;
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
-      float sv[4];
-      float mx = -INFINITY;
+      const int r = r0 + 16 * rb + l16;
+      lim[rb] = -1;
+      if (r < sg.R) {
+        lim[rb] = sg.S + r / p.G;
+        const int64_t qe = out_row(p, sg, r) * D + c * (D / 4);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float x = s[rb][i] * p.scale_log2;
-        if constexpr (sizeof(KV) == 1) x *= cur.ksc[i];
-        x = (pos0 + i <= lim[rb]) ? x : -INFINITY;
-        sv[i] = x;
-        mx = fmaxf(mx, x);
+        for (int ks = 0; ks < KS; ++ks) qB[rb][ks] = load_q8_bf16(p, qe + 8 * ks);
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) qB[rb][ks] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-      const float mn = fmaxf(st.m[rb], mx);
-      const float alpha = exp2f(st.m[rb] - mn);
-      st.m[rb] = mn;
-      float ps = 0.f;
-      float pv[4];
+      m[rb] = kNegBig;
+      l[rb] = 0.f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float e2 = exp2f(sv[i] - mn);
-        ps += e2;
-        float w = e2;
-        if constexpr (sizeof(KV) == 1) w = (pos0 + i < valid_end) ? e2 * cur.vsc[i] : 0.f;
-        pv[i] = w;
-      }
-      st.l[rb] = st.l[rb] * alpha + ps;
-      const uint32_t lo = pack_bf16x2(pv[0], pv[1]), hi = pack_bf16x2(pv[2], pv[3]);
-      pB[rb] = __builtin_bit_cast(i16x4, u32x2{lo, hi});
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) st.acc[rb][db][i] *= alpha;
-      }
+      for (int db = 0; db < NDB; ++db) acc[rb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    wave_sync();                     // V page visible in LDS
-    // ---- O^T[d][row] += V^T[d][tokens] P^T[tokens][row]
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      const int kappa = 2 * db + (l16 >> 3);
-      const int phys = kappa ^ (2 * c);             // rows 4c..4c+3 share the swizzle
-      const uint16_t* src = vl + (4 * c) * D + phys * 8 + (l16 & 7);
-      const uint32_t v0 = src[0], v1 = src[D], v2 = src[2 * D], v3 = src[3 * D];
-      const i16x4 a = __builtin_bit_cast(i16x4, u32x2{v0 | (v1 << 16), v2 | (v3 << 16)});
-#pragma unroll
-      for (int rb = 0; rb < NRB; ++rb)
-        st.acc[rb][db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pB[rb], st.acc[rb][db], 0, 0, 0);
-    }
-    wave_sync();                     // reads done before the next page overwrites LDS
-    cur = nxt;
-  }
-  // lane partial sums -> row sums (the 4 lanes of a row differ only in c)
-#pragma unroll
-  for (int rb = 0; rb < NRB; ++rb) {
-    st.l[rb] += __shfl_xor(st.l[rb], 16, kWave);
-    st.l[rb] += __shfl_xor(st.l[rb], 32, kWave);
   }
 
-  // ---- merge the 4 waves: (2,3) -> (0,1) -> 0
-  constexpr int SLOT = NRB * NDB * kWave * 4 + 2 * NRB * kWave;
-  if (wave >= 2) mfma_state_store<NRB, NDB>(mrg + (wave - 2) * SLOT, st);
-  __syncthreads();
-  if (wave < 2) mfma_state_combine<NRB, NDB>(mrg + wave * SLOT, st);
-  __syncthreads();
-  if (wave == 1) mfma_state_store<NRB, NDB>(mrg, st);
-  __syncthreads();
-  if (wave == 0) {
-    mfma_state_combine<NRB, NDB>(mrg, st);
+  // A operand of S^T = K Q^T: 8 bf16 of K row l16, d c*D/4 + 8ks .. +8
+  __device__ __forceinline__ bf16x8 k_operand(const char* page, int ks) const {
+    const char* kr = page + l16 * Gm::RB;
+    if constexpr (I8) {
+      const int byte = c * (D / 4) + 8 * ks;
+      const u32x2 w = ld64(kr + ((byte / 16) ^ swz_k<Gm::CPR>(l16)) * 16 + byte % 16);
+      u32x4 r;
+      r[0] = codes2_to_bf16x2(w[0], 0);
+      r[1] = codes2_to_bf16x2(w[0], 16);
+      r[2] = codes2_to_bf16x2(w[1], 0);
+      r[3] = codes2_to_bf16x2(w[1], 16);
+      return __builtin_bit_cast(bf16x8, r);
+    } else {
+      const int kappa = c * (Gm::CPR / 4) + ks;
+      return __builtin_bit_cast(bf16x8, ld128(kr + (kappa ^ swz_k<Gm::CPR>(l16)) * 16));
+    }
+  }
+
+  // A operand of O^T += V^T P^T: V rows 4c .. 4c+3, column 16 db + l16;
+  // bf16 rows at or past `valid_rows` read as zero (NaN-safe)
+  __device__ __forceinline__ i16x4 v_operand(const char* page, int db, int valid_rows) const {
+    const char* vb = page + Gm::PAGE;
+    uint32_t e[4];
+    if constexpr (I8) {
+      const int col = 16 * db + l16;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int rho = 4 * c + i;
+        const int8_t code = *reinterpret_cast<const int8_t*>(
+            vb + rho * Gm::RB + ((col / 16) ^ swz_v<Gm::CPR>(rho)) * 16 + col % 16);
+        e[i] = __float_as_uint(float(code)) >> 16;
+      }
+    } else {
+      const int kappa = 2 * db + (l16 >> 3);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int rho = 4 * c + i;
+        e[i] = *reinterpret_cast<const uint16_t*>(vb + rho * Gm::RB +
+                                                  (kappa ^ swz_v<Gm::CPR>(rho)) * 16 +
+                                                  2 * (l16 & 7));
+        e[i] = (rho < valid_rows) ? e[i] : 0u;
+      }
+    }
+    return __builtin_bit_cast(i16x4, u32x2{e[0] | (e[1] << 16), e[2] | (e[3] << 16)});
+  }
+
+  __device__ __forceinline__ void step(const AttnParams&, const char* sa, const char* sb, int a,
+                                       bool second) {
+    // Both slots are always multiplied: without a second page, slot B holds a
+    // copy of page A (finite data) whose scores are masked to -inf below.  A
+    // branch around these products would put a read of their accumulators right
+    // after a taken jump, where this compiler omits the MFMA result wait states.
+    const int npg = second ? 2 : 1;
+    f32x4 s[2][NRB];
+#pragma unroll
+    for (int pg = 0; pg < 2; ++pg) {
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb) s[pg][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const char* page = pg ? sb : sa;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 ka = k_operand(page, ks);
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb)
+          s[pg][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qB[rb][ks], s[pg][rb], 0, 0, 0);
+      }
+    }
+    f32x4 ksc[2], vsc[2];
+    if constexpr (I8) {
+#pragma unroll
+      for (int pg = 0; pg < 2; ++pg) {
+        const char* sc = (pg ? sb : sa) + 2 * Gm::PAGE;
+        const u32x2 kw = ld64(sc + 8 * c), vw = ld64(sc + 32 + 8 * c);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          ksc[pg][i] = f16_bits_to_f32(uint16_t(kw[i / 2] >> (16 * (i & 1))));
+          const int pos = (a + pg) * kPage + 4 * c + i;
+          vsc[pg][i] = (pos < valid_end) ? f16_bits_to_f32(uint16_t(vw[i / 2] >> (16 * (i & 1)))) : 0.f;
+        }
+      }
+    }
+    i16x4 pB[2][NRB];
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+      float x[2][4];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int pg = 0; pg < 2; ++pg) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int pos = (a + pg) * kPage + 4 * c + i;
+          float v = s[pg][rb][i] * scale_log2;
+          if constexpr (I8) v *= ksc[pg][i];
+          v = (pg < npg && pos <= lim[rb]) ? v : -INFINITY;
+          x[pg][i] = v;
+          mx = fmaxf(mx, v);
+        }
+      }
+      mx = xrow32_max(xrow16_max(mx));                          // over the 4 lanes of the row
+      const float mn = fmaxf(m[rb], mx);
+      const float alpha = exp2f(m[rb] - mn);
+      m[rb] = mn;
+      float psum = 0.f;
+#pragma unroll
+      for (int pg = 0; pg < 2; ++pg) {
+        float w[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float e = exp2f(x[pg][i] - mn);
+          psum += e;
+          w[i] = e;
+          if constexpr (I8) w[i] = e * vsc[pg][i];
+        }
+        pB[pg][rb] = __builtin_bit_cast(i16x4, u32x2{pack_bf16x2(w[0], w[1]), pack_bf16x2(w[2], w[3])});
+      }
+      l[rb] = l[rb] * alpha + psum;
+      if (__ballot(alpha != 1.f)) {                             // some row's maximum moved
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[rb][db][i] *= alpha;
+        }
+      }
+    }
+    // Without a second page its probabilities are 0 and its V rows are zeroed
+    // (valid_rows <= 0) or scaled by 0, so the product adds nothing.
+#pragma unroll
+    for (int pg = 0; pg < 2; ++pg) {
+      const char* page = pg ? sb : sa;
+      const int valid_rows = valid_end - (a + pg) * kPage;      // < 16 only on the last page
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const i16x4 va = v_operand(page, db, valid_rows);
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb)
+          acc[rb][db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pB[pg][rb], acc[rb][db], 0, 0, 0);
+      }
+    }
+  }
+
+  // Called once the first pages are in flight: the query registers are read
+  // here, so the compiler's wait for their loads lands outside the page loop
+  // (one wait that also covers the first DMAs) instead of inside it.
+  __device__ __forceinline__ void ready() const {
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(qB[rb][ks]));
+    }
+  }
+  __device__ __forceinline__ void finish() {
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) l[rb] = xrow32_sum(xrow16_sum(l[rb]));
+  }
+
+  static constexpr int SLOT_F = NRB * NDB * kWave * 4 + 2 * NRB * kWave;
+  __device__ __forceinline__ void store(float* slot) const {
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+        *reinterpret_cast<f32x4*>(slot + ((rb * NDB + db) * kWave + lane) * 4) = acc[rb][db];
+      slot[NRB * NDB * kWave * 4 + rb * kWave + lane] = m[rb];
+      slot[NRB * NDB * kWave * 4 + (NRB + rb) * kWave + lane] = l[rb];
+    }
+  }
+  __device__ __forceinline__ void combine(const float* slot) {
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+      const float mo = slot[NRB * NDB * kWave * 4 + rb * kWave + lane];
+      const float lo = slot[NRB * NDB * kWave * 4 + (NRB + rb) * kWave + lane];
+      const float M = fmaxf(m[rb], mo);
+      const float fa = exp2f(m[rb] - M), fb = exp2f(mo - M);
+      l[rb] = fa * l[rb] + fb * lo;
+      m[rb] = M;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const f32x4 o = *reinterpret_cast<const f32x4*>(slot + ((rb * NDB + db) * kWave + lane) * 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[rb][db][i] = fa * acc[rb][db][i] + fb * o[i];
+      }
+    }
+  }
+  __device__ __forceinline__ void write(const AttnParams& p, const Seg& sg, int r0) const {
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
       const int r = r0 + 16 * rb + l16;
       if (r >= sg.R) continue;
       if (sg.full) {
-        const float inv = 1.f / st.l[rb];
+        const float inv = 1.f / l[rb];
         const int64_t oe = out_row(p, sg, r) * D;
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-          f32x4 v = st.acc[rb][db];
+          f32x4 v = acc[rb][db];
 #pragma unroll
           for (int i = 0; i < 4; ++i) v[i] *= inv;
           store_out4(p, oe + 16 * db + 4 * c, v);
@@ -473,312 +893,37 @@ __device__ __forceinline__ void mfma_pass(const AttnParams& p, const Seg& sg, in
         float* sb = slot_base<D>(p, sg.slot);
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
-          *reinterpret_cast<f32x4*>(sb + int64_t(r) * D + 16 * db + 4 * c) = st.acc[rb][db];
+          *reinterpret_cast<f32x4*>(sb + int64_t(r) * D + 16 * db + 4 * c) = acc[rb][db];
         if (c == 0) {
-          sb[int64_t(p.slot_rows) * D + r] = st.m[rb];
-          sb[int64_t(p.slot_rows) * (D + 1) + r] = st.l[rb];
+          sb[int64_t(p.slot_rows) * D + r] = m[rb];
+          sb[int64_t(p.slot_rows) * (D + 1) + r] = l[rb];
         }
       }
     }
   }
-  __syncthreads();
-}
-
-// ============================================================================
-// VALU path
-// ============================================================================
-
-template <typename KV, int D>
-struct ValuGeom {
-  static constexpr int RB = D * int(sizeof(KV));      // bytes per row
-  static constexpr int CPR = RB / 16;                 // 16-byte chunks per row
-  static constexpr int NCL = kPage * CPR / kWave;     // chunks per lane per page
-  static constexpr int QD = D / 4;                    // K values per lane
-  static constexpr int CPL = D / 64;                  // output columns per lane
-  static constexpr int PAGE_BYTES = kPage * RB;
 };
 
-// physical chunk of logical chunk kappa in row rho
-template <int CPR>
-__device__ __forceinline__ int valu_swz(int rho, int kappa) {
-  return kappa ^ (rho & (CPR - 1));
-}
-
-template <typename KV, int D>
-__device__ __forceinline__ void valu_load_page(const AttnParams& p, int pid, int g, u32x4* kr,
-                                               u32x4* vr) {
-  using Gm = ValuGeom<KV, D>;
-  const int lane = lane_id();
-  const int64_t off = page_off<D>(p, pid, g);
-  const u32x4* kp = reinterpret_cast<const u32x4*>(static_cast<const KV*>(p.k) + off);
-  const u32x4* vp = reinterpret_cast<const u32x4*>(static_cast<const KV*>(p.v) + off);
-#pragma unroll
-  for (int e = 0; e < Gm::NCL; ++e) {
-    kr[e] = kp[lane + kWave * e];
-    vr[e] = vp[lane + kWave * e];
-  }
-}
-
-template <typename KV, int D>
-__device__ __forceinline__ void valu_stage(char* kl, char* vl, const u32x4* kr, const u32x4* vr,
-                                           int valid_in_page) {
-  using Gm = ValuGeom<KV, D>;
-  const int lane = lane_id();
-#pragma unroll
-  for (int e = 0; e < Gm::NCL; ++e) {
-    const int id = lane + kWave * e;
-    const int rho = id / Gm::CPR, kappa = id % Gm::CPR;
-    const int at = rho * Gm::RB + valu_swz<Gm::CPR>(rho, kappa) * 16;
-    *reinterpret_cast<u32x4*>(kl + at) = kr[e];
-    *reinterpret_cast<u32x4*>(vl + at) = rho < valid_in_page ? vr[e] : u32x4{0, 0, 0, 0};
-  }
-}
-
-// decode 16 bytes of KV into floats
-template <typename KV>
-__device__ __forceinline__ void decode16(u32x4 w, float* f);
-template <>
-__device__ __forceinline__ void decode16<float>(u32x4 w, float* f) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(w[i]);
-}
-template <>
-__device__ __forceinline__ void decode16<uint16_t>(u32x4 w, float* f) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    f[2 * i] = bf16_lo(w[i]);
-    f[2 * i + 1] = bf16_hi(w[i]);
-  }
-}
-template <>
-__device__ __forceinline__ void decode16<int8_t>(u32x4 w, float* f) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-#pragma unroll
-    for (int b = 0; b < 4; ++b) f[4 * i + b] = float(int(w[i] << (24 - 8 * b)) >> 24);
-  }
-}
-
-template <int RV, int CPL>
-struct ValuState {
-  float o[RV][CPL];
-  float m[RV], l[RV];
-};
-
-template <int RV, int CPL>
-__device__ __forceinline__ void valu_state_store(float* slot, const ValuState<RV, CPL>& st) {
-  const int lane = lane_id();
-#pragma unroll
-  for (int r = 0; r < RV; ++r) {
-#pragma unroll
-    for (int e = 0; e < CPL; ++e) slot[(r * kWave + lane) * CPL + e] = st.o[r][e];
-  }
-  if (lane == 0) {
-#pragma unroll
-    for (int r = 0; r < RV; ++r) {
-      slot[RV * kWave * CPL + r] = st.m[r];
-      slot[RV * kWave * CPL + RV + r] = st.l[r];
-    }
-  }
-}
-
-template <int RV, int CPL>
-__device__ __forceinline__ void valu_state_combine(const float* slot, ValuState<RV, CPL>& st) {
-  const int lane = lane_id();
-#pragma unroll
-  for (int r = 0; r < RV; ++r) {
-    const float mo = slot[RV * kWave * CPL + r];
-    const float lo = slot[RV * kWave * CPL + RV + r];
-    const float M = fmaxf(st.m[r], mo);
-    const float fa = exp2f(st.m[r] - M), fb = exp2f(mo - M);
-    st.l[r] = fa * st.l[r] + fb * lo;
-    st.m[r] = M;
-#pragma unroll
-    for (int e = 0; e < CPL; ++e)
-      st.o[r][e] = fa * st.o[r][e] + fb * slot[(r * kWave + lane) * CPL + e];
-  }
-}
-
-// Stage query rows r0 .. r0+RVMAX-1 of the pair into LDS as fp32:
-// qs[(r*4 + quarter) * (D/4 + 4) + e]  (the +4 pad spreads quarters over banks)
-template <int D>
-__device__ __forceinline__ void valu_stage_q(const AttnParams& p, const Seg& sg, int r0,
-                                             float* qs) {
-  constexpr int QD = D / 4, QP = QD + 4;
-  for (int idx = threadIdx.x; idx < kValuRows * D; idx += kAttnThreads) {
-    const int r = idx / D, d = idx % D;
-    float v = 0.f;
-    if (r0 + r < sg.R) {
-      const int64_t e = out_row(p, sg, r0 + r) * D + d;
-      v = p.q_f32 ? static_cast<const float*>(p.q)[e]
-                  : bf16_to_f32(static_cast<const uint16_t*>(p.q)[e]);
-    }
-    qs[(r * 4 + d / QD) * QP + d % QD] = v;
-  }
-}
-
-template <typename KV, int D, int RV>
-__device__ __forceinline__ void valu_pass(const AttnParams& p, const Seg& sg, int r0, char* wl,
-                                          const float* qs, float* mrg) {
-  using Gm = ValuGeom<KV, D>;
-  constexpr int QD = Gm::QD, QP = QD + 4, CPL = Gm::CPL;
-  const int lane = lane_id(), wave = threadIdx.x / kWave;
-  const int t = lane & 15, c = lane >> 4;
-  char* kl = wl;
-  char* vl = wl + Gm::PAGE_BYTES;
-  float* ps = reinterpret_cast<float*>(wl + 2 * Gm::PAGE_BYTES);   // [RV][16]
-  const int G = p.G;
-
-  ValuState<RV, CPL> st;
-  int lim[RV];
-#pragma unroll
-  for (int r = 0; r < RV; ++r) {
-    st.m[r] = kNegBig;
-    st.l[r] = 0.f;
-#pragma unroll
-    for (int e = 0; e < CPL; ++e) st.o[r][e] = 0.f;
-    lim[r] = (r0 + r < sg.R) ? sg.S + (r0 + r) / G : -1;
-  }
-  const int valid_end = sg.S + sg.k;
-  int j = sg.pa + wave;
-  int ids = 0;
-  u32x4 kr[Gm::NCL], vr[Gm::NCL];
-  if (j < sg.pe) {
-    ids = load_page_ids(p, sg, j);
-    valu_load_page<KV, D>(p, readlane(ids, 0), sg.g, kr, vr);
-  }
-  for (int e = 0; j < sg.pe; j += kWaves, ++e) {
-    const int pid_cur = readlane(ids, e);
-    valu_stage<KV, D>(kl, vl, kr, vr, valid_end - j * kPage);
-    const int jn = j + kWaves;
-    if (jn < sg.pe) {
-      if (e + 1 == kWave) {
-        ids = load_page_ids(p, sg, jn);
-        e = -1;
-      }
-      valu_load_page<KV, D>(p, readlane(ids, e + 1), sg.g, kr, vr);
-    }
-    float ksc = 1.f, vsc = 1.f;
-    const int pos = j * kPage + t;
-    if constexpr (sizeof(KV) == 1) {
-      const int64_t so = (int64_t(pid_cur) * p.Hkv + sg.g) * kPage + t;
-      ksc = f16_bits_to_f32(p.k_scale[so]);
-      vsc = pos < valid_end ? f16_bits_to_f32(p.v_scale[so]) : 0.f;
-    }
-    wave_sync();
-    // ---- this lane's quarter of K row t as fp32
-    float kf[QD];
-    constexpr int CQ = Gm::CPR / 4;            // chunks per quarter
-    constexpr int FPC = 16 / int(sizeof(KV));  // floats per chunk
-#pragma unroll
-    for (int e2 = 0; e2 < CQ; ++e2) {
-      const int kappa = c * CQ + e2;
-      const u32x4 w = *reinterpret_cast<const u32x4*>(kl + t * Gm::RB + valu_swz<Gm::CPR>(t, kappa) * 16);
-      decode16<KV>(w, kf + e2 * FPC);
-    }
-    float s[RV];
-#pragma unroll
-    for (int r = 0; r < RV; ++r) {
-      const float* qrow = qs + (r * 4 + c) * QP;
-      float a = 0.f;
-#pragma unroll
-      for (int e4 = 0; e4 < QD / 4; ++e4) {
-        const f32x4 q4 = *reinterpret_cast<const f32x4*>(qrow + 4 * e4);
-        a = fmaf(q4[0], kf[4 * e4], a);
-        a = fmaf(q4[1], kf[4 * e4 + 1], a);
-        a = fmaf(q4[2], kf[4 * e4 + 2], a);
-        a = fmaf(q4[3], kf[4 * e4 + 3], a);
-      }
-      a += __shfl_xor(a, 16, kWave);
-      a += __shfl_xor(a, 32, kWave);
-      s[r] = a;
-    }
-    // ---- online softmax over the 16 tokens of the page (16-lane groups);
-    //      the running output is rescaled as soon as a row's maximum moves
-#pragma unroll
-    for (int r = 0; r < RV; ++r) {
-      const float x = (pos <= lim[r]) ? s[r] * p.scale_log2 * ksc : -INFINITY;
-      const float mx = group_max<16>(x);
-      const float mn = fmaxf(st.m[r], mx);
-      const float alpha = exp2f(st.m[r] - mn);
-      st.m[r] = mn;
-      const float e2 = exp2f(x - mn);
-      st.l[r] = st.l[r] * alpha + e2;
-#pragma unroll
-      for (int e3 = 0; e3 < CPL; ++e3) st.o[r][e3] *= alpha;
-      if (c == 0) ps[r * kPage + t] = e2 * vsc;
-    }
-    wave_sync();
-    // ---- O[r][cols] += sum_t p[r][t] V[t][cols], four tokens at a time
-    const int cb = lane * CPL * int(sizeof(KV));   // byte of this lane's first column
-    const int kappa_v = cb / 16, within = cb % 16;
-#pragma unroll
-    for (int t0 = 0; t0 < kPage; t0 += 4) {
-      float vv[4][CPL];
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
-        const int row = t0 + tt;
-        const char* src = vl + row * Gm::RB + valu_swz<Gm::CPR>(row, kappa_v) * 16 + within;
-        if constexpr (sizeof(KV) == 4) {
-#pragma unroll
-          for (int e2 = 0; e2 < CPL; ++e2) vv[tt][e2] = reinterpret_cast<const float*>(src)[e2];
-        } else if constexpr (sizeof(KV) == 2) {
-          if constexpr (CPL == 2) {
-            const uint32_t w = *reinterpret_cast<const uint32_t*>(src);
-            vv[tt][0] = bf16_lo(w);
-            vv[tt][CPL - 1] = bf16_hi(w);
-          } else {
-            vv[tt][0] = bf16_to_f32(*reinterpret_cast<const uint16_t*>(src));
-          }
-        } else {
-#pragma unroll
-          for (int e2 = 0; e2 < CPL; ++e2)
-            vv[tt][e2] = float(reinterpret_cast<const int8_t*>(src)[e2]);
-        }
-      }
-#pragma unroll
-      for (int r = 0; r < RV; ++r) {
-        const f32x4 pw = *reinterpret_cast<const f32x4*>(ps + r * kPage + t0);
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-#pragma unroll
-          for (int e2 = 0; e2 < CPL; ++e2) st.o[r][e2] = fmaf(pw[tt], vv[tt][e2], st.o[r][e2]);
-        }
-      }
-    }
-    wave_sync();
-  }
-#pragma unroll
-  for (int r = 0; r < RV; ++r) st.l[r] = group_sum<16>(st.l[r]);
-
-  constexpr int SLOT = RV * kWave * CPL + 2 * RV;
-  if (wave >= 2) valu_state_store<RV, CPL>(mrg + (wave - 2) * SLOT, st);
+// One pass over the segment's pages for rows r0.. of the pair: stream, then
+// merge the 4 waves through LDS (the ring is idle by then) and let wave 0
+// write the output rows or the partial slot.
+template <typename KV, int D, class St>
+__device__ __forceinline__ void pass(const AttnParams& p, const Seg& sg, int r0, St& st,
+                                     char* ring_all) {
+  const int wave = wave_id();
+  run_pages<KV, D>(p, sg, ring_all + wave * Geo<KV, D>::RING, st);
+  st.finish();
+  __syncthreads();                                    // every wave is off the ring
+  float* mrg = reinterpret_cast<float*>(ring_all);
+  constexpr int SLOT = St::SLOT_F;
+  if (wave >= 2) st.store(mrg + (wave - 2) * SLOT);
   __syncthreads();
-  if (wave < 2) valu_state_combine<RV, CPL>(mrg + wave * SLOT, st);
+  if (wave < 2) st.combine(mrg + wave * SLOT);
   __syncthreads();
-  if (wave == 1) valu_state_store<RV, CPL>(mrg, st);
+  if (wave == 1) st.store(mrg);
   __syncthreads();
   if (wave == 0) {
-    valu_state_combine<RV, CPL>(mrg, st);
-#pragma unroll
-    for (int r = 0; r < RV; ++r) {
-      const int rr = r0 + r;
-      if (rr >= sg.R) continue;
-      if (sg.full) {
-        const float inv = 1.f / st.l[r];
-        const int64_t oe = out_row(p, sg, rr) * D + lane * CPL;
-#pragma unroll
-        for (int e2 = 0; e2 < CPL; ++e2) store_out1(p, oe + e2, st.o[r][e2] * inv);
-      } else {
-        float* sb = slot_base<D>(p, sg.slot);
-#pragma unroll
-        for (int e2 = 0; e2 < CPL; ++e2) sb[int64_t(rr) * D + lane * CPL + e2] = st.o[r][e2];
-        if (lane == 0) {
-          sb[int64_t(p.slot_rows) * D + rr] = st.m[r];
-          sb[int64_t(p.slot_rows) * (D + 1) + rr] = st.l[r];
-        }
-      }
-    }
+    st.combine(mrg);
+    st.write(p, sg, r0);
   }
   __syncthreads();
 }
@@ -800,7 +945,7 @@ __device__ __forceinline__ int slot_of(int w, int64_t pair_begin, int64_t N, int
 }
 
 template <int D>
-__device__ void merge_pair(const AttnParams& p, const Seg& sg, int64_t pb, int64_t pend,
+__device__ __forceinline__ void merge_pair(const AttnParams& p, const Seg& sg, int64_t pb, int64_t pend,
                            int64_t N) {
   const int wf = wg_of(pb, N, p.W), wl = wg_of(pend - 1, N, p.W);
   const int items = sg.R * (D / 4);
@@ -834,106 +979,129 @@ __device__ void merge_pair(const AttnParams& p, const Seg& sg, int64_t pb, int64
 
 template <typename KV, int D>
 struct AttnLds {
-  using Gm = ValuGeom<KV, D>;
-  static constexpr int VALU_WAVE = 2 * Gm::PAGE_BYTES + kValuRows * kPage * 4;
-  static constexpr int MFMA_WAVE = kPage * D * 2;
-  static constexpr int WAVE = VALU_WAVE > MFMA_WAVE ? VALU_WAVE : MFMA_WAVE;
-  static constexpr int QS = kValuRows * 4 * (D / 4 + 4);
-  static constexpr int MERGE_MFMA = 2 * (D / 16) * kWave * 4 + 4 * kWave;
-  static constexpr int MERGE_VALU = kValuRows * kWave * (D / 64) + 2 * kValuRows;
-  static constexpr int MERGE = 2 * (MERGE_MFMA > MERGE_VALU ? MERGE_MFMA : MERGE_VALU);
+  static constexpr int RING = kWaves * Geo<KV, D>::RING;
+  static constexpr int QS = kValuRows * 2 * (D / 2 + 4);      // dwords (fp32 layout, the larger)
+  static constexpr int PS = kValuRows * 32 * 4;               // bytes per wave
 };
 
 template <typename KV, int D>
-__device__ __forceinline__ void process_segment(const AttnParams& p, const Seg& sg, char* wl,
-                                                float* qs, float* mrg) {
-  bool use_mfma = false;
-  if constexpr (sizeof(KV) != 4) use_mfma = p.path == 2 || (p.path == 0 && sg.R >= 16);
+__device__ __forceinline__ void process_segment(const AttnParams& p, const Seg& sg, char* ring,
+                                                uint32_t* qs, char* ps_all) {
   if constexpr (sizeof(KV) != 4) {
+    const bool use_mfma = p.path == 2 || (p.path == 0 && sg.R >= 16);
     if (use_mfma) {
       for (int r0 = 0; r0 < sg.R; r0 += kMfmaRows) {
-        if (sg.R - r0 > 16)
-          mfma_pass<KV, D, 2>(p, sg, r0, reinterpret_cast<uint16_t*>(wl), mrg);
-        else
-          mfma_pass<KV, D, 1>(p, sg, r0, reinterpret_cast<uint16_t*>(wl), mrg);
+        if (sg.R - r0 > 16) {
+          MfmaStep<KV, D, 2> st(p, sg, r0);
+          pass<KV, D>(p, sg, r0, st, ring);
+        } else {
+          MfmaStep<KV, D, 1> st(p, sg, r0);
+          pass<KV, D>(p, sg, r0, st, ring);
+        }
       }
       return;
     }
   }
-  for (int r0 = 0; r0 < sg.R; r0 += kValuRows) {
-    valu_stage_q<D>(p, sg, r0, qs);
+  // fp32 caches take at most 8 rows per pass (16 fp32 rows exceed the register file)
+  constexpr bool F32 = sizeof(KV) == 4;
+  constexpr int kRows = F32 ? 8 : kValuRows;
+  char* ps = ps_all + wave_id() * AttnLds<KV, D>::PS;
+  for (int r0 = 0; r0 < sg.R; r0 += kRows) {
+    valu_stage_q<D, F32>(p, sg, r0, qs);
     __syncthreads();
     const int rn = sg.R - r0;
-    if (rn <= 4) valu_pass<KV, D, 4>(p, sg, r0, wl, qs, mrg);
-    else if (rn <= 8) valu_pass<KV, D, 8>(p, sg, r0, wl, qs, mrg);
-    else valu_pass<KV, D, 16>(p, sg, r0, wl, qs, mrg);
+    if (rn <= 4) {
+      ValuStep<KV, D, 4> st(p, sg, r0, qs, ps);
+      pass<KV, D>(p, sg, r0, st, ring);
+    } else if (F32 || rn <= 8) {
+      ValuStep<KV, D, 8> st(p, sg, r0, qs, ps);
+      pass<KV, D>(p, sg, r0, st, ring);
+    } else {
+      ValuStep<KV, D, 16> st(p, sg, r0, qs, ps);
+      pass<KV, D>(p, sg, r0, st, ring);
+    }
   }
 }
 
 template <typename KV, int D>
 __global__ __launch_bounds__(kAttnThreads, 1) void verify_attn_kernel(AttnParams p) {
   using L = AttnLds<KV, D>;
-  __shared__ int32_t s_start[kMaxB + 1];
-  __shared__ int32_t s_wtot[kWaves];
+  __shared__ __attribute__((aligned(1024))) char s_ring[L::RING];
+  __shared__ __attribute__((aligned(16))) uint32_t s_q[L::QS];
+  __shared__ __attribute__((aligned(16))) char s_ps[kWaves * L::PS];
+  __shared__ int32_t s_scan[kAttnThreads];
+  __shared__ int32_t s_info[4];
   __shared__ int s_flag;
-  __shared__ __attribute__((aligned(16))) char s_wave[kWaves * L::WAVE];
-  __shared__ __attribute__((aligned(16))) float s_q[L::QS];
-  __shared__ __attribute__((aligned(16))) float s_mrg[L::MERGE];
 
-  const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
-
-  // ---- exclusive prefix over sequences of Hkv * pages
+  const int tid = threadIdx.x;
   const int B = p.B;
+
+  // ---- pages per sequence: each thread sums a contiguous chunk of sequences
   const int per = (B + kAttnThreads - 1) / kAttnThreads;
   int tot = 0;
   for (int e = 0; e < per; ++e) {
     const int b = tid * per + e;
     if (b < B) tot += p.Hkv * seq_info(p, b).np;
   }
-  int incl = tot;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int u = __shfl_up(incl, o, kWave);
-    if (lane >= o) incl += u;
-  }
-  if (lane == kWave - 1) s_wtot[wave] = incl;
+  s_scan[tid] = tot;
   __syncthreads();
-  int base = 0;
-  for (int w = 0; w < wave; ++w) base += s_wtot[w];
-  int run = base + incl - tot;
-  for (int e = 0; e < per; ++e) {
-    const int b = tid * per + e;
-    if (b < B) {
-      s_start[b] = run;
-      run += p.Hkv * seq_info(p, b).np;
+  if (tid < kWave) {                                  // exclusive scan of the chunk sums
+    constexpr int PER_LANE = kAttnThreads / kWave;
+    int run = 0;
+    for (int i = 0; i < PER_LANE; ++i) {
+      const int v = s_scan[tid * PER_LANE + i];
+      s_scan[tid * PER_LANE + i] = run;
+      run += v;
     }
+    int incl = run;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int u = __shfl_up(incl, o, kWave);
+      if (tid >= o) incl += u;
+    }
+    const int excl = incl - run;
+    for (int i = 0; i < PER_LANE; ++i) s_scan[tid * PER_LANE + i] += excl;
+    if (tid == kWave - 1) s_info[0] = incl;           // total pages N
   }
-  if (tid == kAttnThreads - 1) s_start[B] = base + incl;
   __syncthreads();
-  const int64_t N = s_start[B];
+  const int64_t N = s_info[0];
   if (N == 0) return;
 
   // ---- this workgroup's page range; consecutive ranges go to one XCD
-  const int h = blockIdx.x;
-  const int w = (p.W % 8 == 0) ? (h % 8) * (p.W / 8) + h / 8 : h;
+  const int hw = blockIdx.x;
+  const int w = (p.W % 8 == 0) ? (hw % 8) * (p.W / 8) + hw / 8 : hw;
   const int64_t g0 = range_start(w, N, p.W), g1 = range_start(w + 1, N, p.W);
   if (g0 >= g1) return;
 
-  int b = 0;
+  // the sequence holding page g0 and the first page of that sequence
   {
-    int lo = 0, hi = B - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (s_start[mid] <= g0) lo = mid; else hi = mid - 1;
+    const int base = s_scan[tid];
+    if (tot > 0 && base <= g0 && g0 < base + tot) {
+      int run = base;
+      for (int e = 0; e < per; ++e) {
+        const int b = tid * per + e;
+        const int n = p.Hkv * seq_info(p, b).np;
+        if (g0 < run + n) {
+          s_info[1] = b;
+          s_info[2] = run;
+          break;
+        }
+        run += n;
+      }
     }
-    b = lo;
   }
-  char* wl = s_wave + wave * L::WAVE;
+  __syncthreads();
+  int b = s_info[1];
+  int64_t sb = s_info[2];
+  SeqInfo si = seq_info(p, b);
+
   int64_t cur = g0;
   while (cur < g1) {
-    while (b < B - 1 && s_start[b + 1] <= cur) ++b;
-    const SeqInfo si = seq_info(p, b);
-    const int64_t sb = s_start[b];
+    while (cur >= sb + int64_t(p.Hkv) * si.np) {      // next sequence with pages
+      sb += int64_t(p.Hkv) * si.np;
+      ++b;
+      si = seq_info(p, b);
+    }
     const int o = int(cur - sb);
     Seg sg;
     sg.b = b;
@@ -951,7 +1119,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void verify_attn_kernel(AttnParams
     sg.full = (cur == pb) && (se == pend);
     sg.slot = (cur == g0) ? 2 * w : 2 * w + 1;
 
-    process_segment<KV, D>(p, sg, wl, s_q, s_mrg);
+    process_segment<KV, D>(p, sg, s_ring, s_q, s_ps);
 
     if (!sg.full) {
       __threadfence();
@@ -989,14 +1157,15 @@ AttnPlan plan_verify_attn(const sva_batch* batch, const sva_paged_kv* kv, int Hq
   const int64_t pages_ub = int64_t(batch->B) * kv->Hkv * std::max<int64_t>(pages_per_seq, 1);
   int W = 0;
   if (opts && opts->num_workgroups > 0) {
-    W = opts->num_workgroups;
+    W = std::min(opts->num_workgroups, kMaxWorkgroups);
   } else {
     const int64_t want = (pages_ub + 15) / 16;     // at least 4 pages per wave
-    W = int(std::min<int64_t>(std::max(num_cus, 1), std::max<int64_t>(want, 1)));
+    W = int(std::min<int64_t>(std::min(std::max(num_cus, 1), kMaxWorkgroups),
+                              std::max<int64_t>(want, 1)));
   }
   pl.num_wg = W;
   pl.slot_rows = std::max(batch->max_q, 1) * G;
-  pl.counter_bytes = (size_t(W) * 4 + 255) & ~size_t(255);
+  pl.counter_bytes = size_t(kMaxWorkgroups) * 4;
   pl.slot_bytes = size_t(2) * W * pl.slot_rows * (kv->d + 2) * sizeof(float);
   pl.total_bytes = pl.counter_bytes + pl.slot_bytes;
   return pl;
