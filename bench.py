@@ -12,8 +12,11 @@ and agreement rate).
 
 Prints ONE JSON line.  `value` is verified draft tokens per second for whole
 steps (inputs resident in HBM); `roofline` is the attention kernel's KV bytes
-over its own average launch time (HIP events on its stream, inside the timed
-region) against 8 TB/s; `cpu_baseline` is the fp64 oracle on the host.
+over its own average launch time against 8 TB/s; `cpu_baseline` is the fp64
+oracle on the host.  The attention kernel's average launch time comes from the same number of
+back-to-back launches after the timed steps, between one pair of HIP events
+on its stream; `roofline.traffic` is HBM traffic from committed rocprofv3
+counter readings (null when they no longer match the kernel's sources).
 """
 import argparse
 import dataclasses
@@ -48,6 +51,43 @@ def other_bytes(w, ctx, ks, max_pages):
     qe = {"f32": 4, "bf16": 2}[w.q_dtype]
     T = sum(ks)
     return 2 * T * w.Hq * w.d * qe + 4 * len(ctx) * max_pages + 8 * len(ctx)
+
+
+KERNEL_SOURCES = ("verify_attn.hip", "common.h", "launch.h")
+
+
+def kernel_source_hash():
+    """sha256 over the attention kernel's sources, to tell whether stored
+    counter readings still describe the kernel as built."""
+    import hashlib
+    h = hashlib.sha256()
+    base = os.path.join(os.path.dirname(os.path.abspath(__file__)), "token_verify_attention_amd",
+                        "csrc")
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(base, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload, attn_ms):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
+    readings (each scaled by what the counter reads for a plain copy of known
+    size), as a rate over this run's average launch time.  None when no
+    reading exists for the workload or the kernel sources changed since."""
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                        f"verify_attn_{workload}_hbm_counters.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    nbytes = float(kv["traffic_bytes_per_launch"])
+    return {"bytes": nbytes, "gbps": nbytes / (attn_ms * 1e-3) / 1e9}
 
 
 class Inputs:
@@ -202,29 +242,39 @@ def main():
     torch.cuda.synchronize()
 
     ev = lambda: torch.cuda.Event(enable_timing=True)
+    # Timed steps: nothing but the three calls per step on the stream (an event
+    # between kernels costs a cache flush and a few microseconds of idle GPU).
     t_start, t_end = ev(), ev()
-    attn_ev = [(ev(), ev()) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t_start.record(stream)
     for s in range(args.steps):
         inp = sets[s % nsets]
         inp.append()
-        attn_ev[s][0].record(stream)
         inp.attn()
-        attn_ev[s][1].record(stream)
         inp.accept()
     t_end.record(stream)
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
     ms_per_step = total_ms / args.steps
-    attn_ms = [a.elapsed_time(b) for a, b in attn_ev]
-    attn_avg = sum(attn_ms) / len(attn_ms)
-    bytes_all = sum(set_bytes[s % nsets] for s in range(args.steps))
     tokens_all = sum(set_tokens[s % nsets] for s in range(args.steps))
-    kvb = bytes_all / args.steps
-    achieved = bytes_all / (sum(attn_ms) * 1e-3) / 1e9
     value = tokens_all / (total_ms * 1e-3)
     T = tokens_all / args.steps
+
+    # The attention kernel's average launch duration: the same number of
+    # launches back to back on the same stream (same input-set rotation),
+    # between one pair of HIP events.
+    a_start, a_end = ev(), ev()
+    torch.cuda.synchronize()
+    a_start.record(stream)
+    for s in range(args.steps):
+        sets[s % nsets].attn()
+    a_end.record(stream)
+    torch.cuda.synchronize()
+    attn_avg = a_start.elapsed_time(a_end) / args.steps
+    bytes_all = sum(set_bytes[s % nsets] for s in range(args.steps))
+    kvb = bytes_all / args.steps
+    achieved = kvb / (attn_avg * 1e-3) / 1e9
+    traffic = measured_traffic(w.name, attn_avg)
 
     probe = copy_probe_gbps(dev)
     result = {
@@ -253,15 +303,15 @@ def main():
         "kv_hbm_gbps": achieved,
         "kv_frac_of_peak": achieved / HBM_PEAK_GBPS,
         "attn_ms_avg": attn_avg,
-        "attn_ms_min": min(attn_ms),
         "attn_draft_tokens_per_s": T / (attn_avg * 1e-3),
         "draft_tokens_per_step": T,
         "other_bytes_per_launch": other_bytes(w, ctx, ks, max_pages),
         "copy_probe_gbps": probe,
         "roofline": {
             "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-            "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+            "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic and traffic["gbps"],
             "kernel": "verify_attn_kernel",
+            "traffic_bytes_per_launch": traffic and traffic["bytes"],
         },
         "cpu_baseline": None,
     }

@@ -91,8 +91,8 @@ typedef struct {
 } sva_batch;
 
 /* Optional tuning for sva_spec_verify_attn; pass NULL for the defaults.
- *   path            0: per sequence, VALU when k_b*G < 16 else MFMA (default)
- *                   1: VALU for every sequence     2: MFMA for every sequence
+ *   path            0: default -- MFMA for bf16 and INT8 caches, VALU for fp32
+ *                   1: VALU for every sequence     2: MFMA (same as 0)
  *   num_workgroups  0: chosen from the device and batch; otherwise the grid size,
  *                   1 .. 4096 (must equal the value used for the workspace size
  *                   query) */

@@ -27,14 +27,15 @@
 // with explicit vmcnt counts; page ids come from scalar loads.
 //
 // Inner loops per step (32 tokens):
-//  * VALU path (k_b*G < 16): lane = (token, half of d); bf16 dot2 products
-//    (INT8 codes convert exactly to bf16), online softmax over 32-lane groups,
-//    P.V with bf16 probability pairs and dot2, each lane owning d/64 columns.
-//    fp32 caches use plain fp32 FMAs.
-//  * MFMA path (k_b*G >= 16): S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (a
-//    lane owns one query row and 4 tokens of a page), O^T += V^T P^T with
-//    v_mfma_f32_16x16x16_bf16.  INT8 per-token scales multiply the score (K)
-//    and the probability (V).
+//  * MFMA path (bf16 and INT8 caches, any k_b*G; blocks of 16 query rows are
+//    padded, which costs nothing while the loop is HBM-bound): S^T = K Q^T
+//    with v_mfma_f32_16x16x32_bf16 (a lane owns one query row and 4 tokens of
+//    a page), O^T += V^T P^T with v_mfma_f32_16x16x16_bf16.  INT8 per-token
+//    scales multiply the score (K) and the probability (V).
+//  * VALU path (fp32 caches; bf16 / INT8 on request): lane = (token, half of
+//    d); bf16 dot2 products (INT8 codes convert exactly to bf16), online
+//    softmax over 32-lane groups, P.V with bf16 probability pairs and dot2,
+//    each lane owning d/64 columns.  fp32 caches use plain fp32 FMAs.
 //
 // Positions at or past S_b + k_b (garbage slots of the last page) are masked
 // in the scores and zeroed in V, so NaN garbage never reaches an output.
@@ -988,7 +989,7 @@ template <typename KV, int D>
 __device__ __forceinline__ void process_segment(const AttnParams& p, const Seg& sg, char* ring,
                                                 uint32_t* qs, char* ps_all) {
   if constexpr (sizeof(KV) != 4) {
-    const bool use_mfma = p.path == 2 || (p.path == 0 && sg.R >= 16);
+    const bool use_mfma = p.path != 1;
     if (use_mfma) {
       for (int r0 = 0; r0 < sg.R; r0 += kMfmaRows) {
         if (sg.R - r0 > 16) {
