@@ -145,6 +145,25 @@ __device__ __forceinline__ float* slot_base(const AttnParams& p, int slot) {
   return p.partials + int64_t(slot) * p.slot_rows * (D + 2);
 }
 
+// Partial slots and completion counters are shared by workgroups that may sit
+// on different XCDs, each with its own L2.  They are accessed with device-scope
+// relaxed atomics (sc1 loads and stores, coherent across XCDs), so no fence has
+// to write back or invalidate a whole L2: an s_waitcnt on the writer's stores
+// before the counter increment orders them.
+__device__ __forceinline__ void st_dev(float* a, float v) {
+  __hip_atomic_store(a, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_dev(const float* a) {
+  return __hip_atomic_load(const_cast<float*>(a), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev4(float* a, f32x4 v) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) st_dev(a + i, v[i]);
+}
+__device__ __forceinline__ f32x4 ld_dev4(const float* a) {
+  return f32x4{ld_dev(a), ld_dev(a + 1), ld_dev(a + 2), ld_dev(a + 3)};
+}
+
 __device__ __forceinline__ void store_out4(const AttnParams& p, int64_t elem, f32x4 v) {
   if (p.out_f32) {
     *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + elem) = v;
@@ -621,10 +640,10 @@ struct ValuStep {
       } else {
         float* sb = slot_base<D>(p, sg.slot);
 #pragma unroll
-        for (int e = 0; e < CPL; ++e) sb[int64_t(rr) * D + lane * CPL + e] = o[r][e];
+        for (int e = 0; e < CPL; ++e) st_dev(sb + int64_t(rr) * D + lane * CPL + e, o[r][e]);
         if (lane == 0) {
-          sb[int64_t(p.slot_rows) * D + rr] = m[r];
-          sb[int64_t(p.slot_rows) * (D + 1) + rr] = l[r];
+          st_dev(sb + int64_t(p.slot_rows) * D + rr, m[r]);
+          st_dev(sb + int64_t(p.slot_rows) * (D + 1) + rr, l[r]);
         }
       }
     }
@@ -893,11 +912,10 @@ struct MfmaStep {
       } else {
         float* sb = slot_base<D>(p, sg.slot);
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
-          *reinterpret_cast<f32x4*>(sb + int64_t(r) * D + 16 * db + 4 * c) = acc[rb][db];
+        for (int db = 0; db < NDB; ++db) st_dev4(sb + int64_t(r) * D + 16 * db + 4 * c, acc[rb][db]);
         if (c == 0) {
-          sb[int64_t(p.slot_rows) * D + r] = m[rb];
-          sb[int64_t(p.slot_rows) * (D + 1) + r] = l[rb];
+          st_dev(sb + int64_t(p.slot_rows) * D + r, m[rb]);
+          st_dev(sb + int64_t(p.slot_rows) * (D + 1) + r, l[rb]);
         }
       }
     }
@@ -957,9 +975,9 @@ __device__ __forceinline__ void merge_pair(const AttnParams& p, const Seg& sg, i
     for (int w = wf; w <= wl; ++w) {
       if (range_start(w + 1, N, p.W) == range_start(w, N, p.W)) continue;   // empty range
       const float* sb = slot_base<D>(p, slot_of(w, pb, N, p.W));
-      const float ms = sb[int64_t(p.slot_rows) * D + r];
-      const float ls = sb[int64_t(p.slot_rows) * (D + 1) + r];
-      const f32x4 os = *reinterpret_cast<const f32x4*>(sb + int64_t(r) * D + 4 * d4);
+      const float ms = ld_dev(sb + int64_t(p.slot_rows) * D + r);
+      const float ls = ld_dev(sb + int64_t(p.slot_rows) * (D + 1) + r);
+      const f32x4 os = ld_dev4(sb + int64_t(r) * D + 4 * d4);
       const float Mn = fmaxf(M, ms);
       const float fa = exp2f(M - Mn), fb = exp2f(ms - Mn);
       L = fa * L + fb * ls;
@@ -1123,21 +1141,25 @@ __global__ __launch_bounds__(kAttnThreads, 1) void verify_attn_kernel(AttnParams
     process_segment<KV, D>(p, sg, s_ring, s_q, s_ps);
 
     if (!sg.full) {
-      __threadfence();
+      // every thread's partial stores are complete at device scope before the
+      // barrier, so the increment below is ordered after all of them
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
       if (tid == 0) {
         const int wf = wg_of(pb, N, p.W), wlast = wg_of(pend - 1, N, p.W);
         int nseg = 0;
         for (int x = wf; x <= wlast; ++x)
           nseg += range_start(x + 1, N, p.W) > range_start(x, N, p.W);
-        const int old = atomicAdd(p.counters + wf, 1);
+        const int old = __hip_atomic_fetch_add(p.counters + wf, 1, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
         s_flag = (old == nseg - 1);
       }
       __syncthreads();
-      if (s_flag) {
-        __threadfence();
+      if (s_flag) {      // the last workgroup of the pair: all partials are visible
         merge_pair<D>(p, sg, pb, pend, N);
-        if (tid == 0) atomicExch(p.counters + wg_of(pb, N, p.W), 0);
+        if (tid == 0)
+          __hip_atomic_store(p.counters + wg_of(pb, N, p.W), 0, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
       }
       __syncthreads();
     }
