@@ -23,8 +23,12 @@ OBJ_DIR = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-# Packed fp32 VALU ops are kept out of every kernel on purpose.
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Packed fp32 VALU ops are kept out of every kernel on purpose.  MFMA
+# accumulators are kept in architectural VGPRs (the softmax rescales them with
+# VALU ops, which cannot read AGPRs), instead of being copied between register
+# files on every iteration.
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                "-mllvm", "-amdgpu-mfma-vgpr-form"]
 COMMON_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-mcode-object-version=5",
     "-Wall", "-Wno-unused-function", "-I", INCLUDE, "-I", CSRC,

@@ -43,6 +43,7 @@
 #include "launch.h"
 
 #include <algorithm>
+#include <type_traits>
 
 namespace sva {
 
@@ -79,7 +80,6 @@ struct AttnParams {
   int B, T, Hq, Hkv, G, num_pages, max_pages, max_q;
   int slot_rows;        // rows per partial slot (max_q * G)
   int W;                // grid size
-  int path;             // 0 auto, 1 VALU, 2 MFMA
 };
 
 struct SeqInfo {
@@ -194,14 +194,20 @@ struct Geo {
   static constexpr int S_RAW = kRingBudget / (kWaves * 2 * SLOT);
   static constexpr int S = S_RAW < 1 ? 1 : (S_RAW > 3 ? 3 : S_RAW);   // steps held in the ring
   static constexpr int RING = 2 * S * SLOT;          // bytes per wave
-};
 
-// Chunk permutations inside a row: K rows are read 16 rows x one chunk at a
-// time (XOR with the row), V rows 4 rows x two chunks (XOR with the row quad).
-template <int CPR>
-__device__ __forceinline__ int swz_k(int rho) { return rho & (CPR - 1); }
-template <int CPR>
-__device__ __forceinline__ int swz_v(int rho) { return ((rho >> 2) & 3) * (CPR >= 8 ? 2 : 1); }
+  // 16-byte chunks are permuted inside each row (XOR of the chunk index) so
+  // that the LDS reads of a 16-lane group hit distinct banks (a 256-byte bank
+  // window holds RPW rows).
+  static constexpr int RPW = RB >= 256 ? 1 : 256 / RB;
+  // K: 16 lanes read one chunk (or half chunk) of 16 consecutive rows.
+  static __device__ __forceinline__ int swz_k(int rho) { return (rho / RPW) & (CPR - 1); }
+  // V: bf16 -- 4 rows x 32 contiguous bytes (transposing 16-bit reads);
+  // INT8 -- 4 rows x 16 bytes of each of 2 pages (transposing 8-bit reads);
+  // fp32 -- 4-row quads (VALU path).
+  static __device__ __forceinline__ int swz_v(int rho) {
+    return ES == 4 ? ((rho >> 2) & 3) * 2 : (ES == 2 ? 2 * (rho & 3) : (rho & 3));
+  }
+};
 
 // Global -> LDS copies (lane l's 16 or 4 bytes land at l * 16 or l * 4 past
 // the wave-uniform LDS address in M0).  Issued through asm on purpose: for
@@ -233,8 +239,8 @@ __device__ __forceinline__ void dma_page(const AttnParams& p, int pid, int g, ch
   for (int e = 0; e < Gm::DMA; ++e) {
     const int phys = kWave * e + lane;
     const int rho = phys / Gm::CPR, phi = phys % Gm::CPR;
-    dma16(kb + rho * Gm::RB + (phi ^ swz_k<Gm::CPR>(rho)) * 16, slot + 1024 * e);
-    dma16(vb + rho * Gm::RB + (phi ^ swz_v<Gm::CPR>(rho)) * 16, slot + Gm::PAGE + 1024 * e);
+    dma16(kb + rho * Gm::RB + (phi ^ Gm::swz_k(rho)) * 16, slot + 1024 * e);
+    dma16(vb + rho * Gm::RB + (phi ^ Gm::swz_v(rho)) * 16, slot + Gm::PAGE + 1024 * e);
   }
   if constexpr (Gm::ES == 1) {
     const int64_t so = (int64_t(pid) * p.Hkv + g) * kPage;
@@ -405,7 +411,7 @@ struct ValuStep {
 #pragma unroll
       for (int e = 0; e < Gm::CPR / 2; ++e) {
         const int kappa = h * (Gm::CPR / 2) + e;
-        const u32x4 w = ld128(kr + (kappa ^ swz_k<Gm::CPR>(row)) * 16);
+        const u32x4 w = ld128(kr + (kappa ^ Gm::swz_k(row)) * 16);
 #pragma unroll
         for (int i = 0; i < 4; ++i) kf[4 * e + i] = __uint_as_float(w[i]);
       }
@@ -427,7 +433,7 @@ struct ValuStep {
 #pragma unroll
         for (int e = 0; e < Gm::CPR / 2; ++e) {       // 16 codes per chunk
           const int kappa = h * (Gm::CPR / 2) + e;
-          const u32x4 w = ld128(kr + (kappa ^ swz_k<Gm::CPR>(row)) * 16);
+          const u32x4 w = ld128(kr + (kappa ^ Gm::swz_k(row)) * 16);
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             kx[8 * e + 2 * i] = codes2_to_bf16x2(w[i], 0);
@@ -438,7 +444,7 @@ struct ValuStep {
 #pragma unroll
         for (int e = 0; e < Gm::CPR / 2; ++e) {       // 8 bf16 per chunk
           const int kappa = h * (Gm::CPR / 2) + e;
-          const u32x4 w = ld128(kr + (kappa ^ swz_k<Gm::CPR>(row)) * 16);
+          const u32x4 w = ld128(kr + (kappa ^ Gm::swz_k(row)) * 16);
 #pragma unroll
           for (int i = 0; i < 4; ++i) kx[4 * e + i] = w[i];
         }
@@ -473,7 +479,7 @@ struct ValuStep {
           const int tok = t0 + tt, row = tok & 15;
           const char* vr = ((tok < 16) ? sa : sb) + Gm::PAGE + row * Gm::RB;
           const int cb = lane * CPL * 4;
-          const char* src = vr + ((cb / 16) ^ swz_v<Gm::CPR>(row)) * 16 + cb % 16;
+          const char* src = vr + ((cb / 16) ^ Gm::swz_v(row)) * 16 + cb % 16;
 #pragma unroll
           for (int e = 0; e < CPL; ++e) vv[tt][e] = reinterpret_cast<const float*>(src)[e];
           if constexpr (kMask) {
@@ -505,8 +511,8 @@ struct ValuStep {
           if constexpr (I8) {
             const int cb = lane * CPL;                // byte of this lane's first column
             const int kap = cb / 16, wi = cb % 16;
-            const char* s0 = r0p + (kap ^ swz_v<Gm::CPR>(row)) * 16 + wi;
-            const char* s1 = r1p + (kap ^ swz_v<Gm::CPR>(row + 1)) * 16 + wi;
+            const char* s0 = r0p + (kap ^ Gm::swz_v(row)) * 16 + wi;
+            const char* s1 = r1p + (kap ^ Gm::swz_v(row + 1)) * 16 + wi;
             if constexpr (CPL == 2) {
               const int c00 = reinterpret_cast<const int8_t*>(s0)[0];
               const int c01 = reinterpret_cast<const int8_t*>(s0)[1];
@@ -521,8 +527,8 @@ struct ValuStep {
           } else {
             const int cb = lane * CPL * 2;
             const int kap = cb / 16, wi = cb % 16;
-            const char* s0 = r0p + (kap ^ swz_v<Gm::CPR>(row)) * 16 + wi;
-            const char* s1 = r1p + (kap ^ swz_v<Gm::CPR>(row + 1)) * 16 + wi;
+            const char* s0 = r0p + (kap ^ Gm::swz_v(row)) * 16 + wi;
+            const char* s1 = r1p + (kap ^ Gm::swz_v(row + 1)) * 16 + wi;
             if constexpr (CPL == 2) {
               const uint32_t w0 = ld32(s0), w1 = ld32(s1);
               vp[u][0] = __builtin_amdgcn_perm(w1, w0, 0x05040100u);
@@ -670,20 +676,88 @@ __device__ __forceinline__ bf16x8 load_q8_bf16(const AttnParams& p, int64_t elem
   return __builtin_bit_cast(bf16x8, w);
 }
 
+// 8 consecutive Q values as fp16 (the INT8 path's operand type; bf16 and fp32
+// Q round to nearest even).
+__device__ __forceinline__ f16x8 load_q8_f16(const AttnParams& p, int64_t elem) {
+  float v[8];
+  if (p.q_f32) {
+    const f32x4* s = reinterpret_cast<const f32x4*>(static_cast<const float*>(p.q) + elem);
+    const f32x4 a = s[0], b = s[1];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[i] = a[i];
+      v[4 + i] = b[i];
+    }
+  } else {
+    const u32x4 w = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(p.q) + elem);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    r[i] = uint32_t(f32_to_f16_bits(v[2 * i])) | (uint32_t(f32_to_f16_bits(v[2 * i + 1])) << 16);
+  return __builtin_bit_cast(f16x8, r);
+}
+
+// 8 INT8 codes -> fp16 values 1152 + code, exactly: code ^ 0x80 is code + 128
+// as an unsigned byte u, and the fp16 bit pattern 0x6400 | u is 1024 + u.
+__device__ __forceinline__ f16x8 codes8_to_f16(uint32_t w0, uint32_t w1) {
+  const uint32_t a = w0 ^ 0x80808080u, b = w1 ^ 0x80808080u;
+  const uint32_t k = 0x64646464u;
+  const u32x4 r = {__builtin_amdgcn_perm(k, a, 0x04010400u), __builtin_amdgcn_perm(k, a, 0x04030402u),
+                   __builtin_amdgcn_perm(k, b, 0x04010400u), __builtin_amdgcn_perm(k, b, 0x04030402u)};
+  return __builtin_bit_cast(f16x8, r);
+}
+
+// One step of the MFMA path over two pages (32 tokens) for up to 16*NRB query
+// rows.  Lane (l16, c) = (lane % 16, lane / 16).
+//  * S^T = K Q^T, v_mfma_f32_16x16x32: the lane holds tokens 4c..4c+3 of each
+//    page for query row l16.
+//  * Online softmax with a lazy reference maximum: a row's reference moves
+//    (and its accumulators are rescaled) only when a score exceeds it by more
+//    than kLazy in log2 units, so weights stay below 2^kLazy and rescaling is
+//    rare; results are those of the exact maximum up to rounding.
+//  * O^T += V^T P^T, v_mfma_f32_16x16x32 over both pages: k-slot e of lane
+//    group c is token 4c + e%4 of page e/4 on both operands.  V^T comes
+//    straight from LDS with the transposing reads ds_read_b64_tr_b16 (bf16) and
+//    ds_read_b64_tr_b8 (INT8).
+//  * The softmax denominator of the bf16 path comes from the same MFMA with an
+//    all-ones A operand, so it sums exactly the rounded weights P.V uses.
+//  * INT8 caches run fp16 MFMAs on codes offset to 1152 + code (exact); the
+//    offset leaves S through the accumulator's start value -1152 * sum(q) and
+//    leaves O through the MFMA-computed sum of the fp16 weights.
 template <typename KV, int D, int NRB>
 struct MfmaStep {
   using Gm = Geo<KV, D>;
   static constexpr bool I8 = sizeof(KV) == 1;
-  static constexpr int KS = D / 32;       // 16x16x32 k-steps over d
-  static constexpr int NDB = D / 16;      // 16-column blocks of d
+  using Op8 = typename std::conditional<I8, f16x8, bf16x8>::type;
+  static constexpr int KS = D / 32;       // 16x16x32 k-steps over d (S^T)
+  static constexpr int NDB = D / 16;      // 16-column blocks of d (O^T)
+  static constexpr float kLazy = 8.f;
+  static constexpr float kCodeBias = 1152.f;
 
-  bf16x8 qB[NRB][KS];                     // lane (l16, c): row 16 rb + l16, d c*D/4 + 8ks .. +8
+  Op8 qB[NRB][KS];                        // row 16 rb + l16, d 32c + 8ks .. +8
   f32x4 acc[NRB][NDB];                    // O^T: d 16 db + 4c + i, row 16 rb + l16
+  f32x4 sacc[NRB];                        // all-ones MFMA: sum of the weights fed to P.V
   float m[NRB], l[NRB];
+  float s0[NRB];                          // INT8: start value of the S^T accumulator
   int lim[NRB];
   int valid_end;
   int lane, l16, c;
   float scale_log2;
+
+  static __device__ __forceinline__ f32x4 mfma32(Op8 a, Op8 b, f32x4 acc) {
+    if constexpr (I8) return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc, 0, 0, 0);
+    else return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+  }
+  static __device__ __forceinline__ Op8 ones() {
+    const uint32_t one = I8 ? 0x3c003c00u : 0x3f803f80u;
+    return __builtin_bit_cast(Op8, u32x4{one, one, one, one});
+  }
 
   __device__ __forceinline__ MfmaStep(const AttnParams& p, const Seg& sg, int r0) {
     scale_log2 = p.scale_log2;
@@ -695,66 +769,79 @@ struct MfmaStep {
     for (int rb = 0; rb < NRB; ++rb) {
       const int r = r0 + 16 * rb + l16;
       lim[rb] = -1;
+      float qs = 0.f;
       if (r < sg.R) {
         lim[rb] = sg.S + r / p.G;
         const int64_t qe = out_row(p, sg, r) * D + c * (D / 4);
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) qB[rb][ks] = load_q8_bf16(p, qe + 8 * ks);
+        for (int ks = 0; ks < KS; ++ks) {
+          if constexpr (I8) {
+            qB[rb][ks] = load_q8_f16(p, qe + 8 * ks);
+          } else {
+            qB[rb][ks] = load_q8_bf16(p, qe + 8 * ks);
+          }
+        }
       } else {
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) qB[rb][ks] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
+        for (int ks = 0; ks < KS; ++ks) qB[rb][ks] = __builtin_bit_cast(Op8, u32x4{0, 0, 0, 0});
+      }
+      if constexpr (I8) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const u32x4 w = __builtin_bit_cast(u32x4, qB[rb][ks]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            qs += f16_bits_to_f32(uint16_t(w[i])) + f16_bits_to_f32(uint16_t(w[i] >> 16));
+        }
+        s0[rb] = -kCodeBias * xrow32_sum(xrow16_sum(qs));
       }
       m[rb] = kNegBig;
       l[rb] = 0.f;
+      sacc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int db = 0; db < NDB; ++db) acc[rb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
   }
 
-  // A operand of S^T = K Q^T: 8 bf16 of K row l16, d c*D/4 + 8ks .. +8
-  __device__ __forceinline__ bf16x8 k_operand(const char* page, int ks) const {
+  // A operand of S^T = K Q^T: K row l16, d 32c + 8ks .. +8
+  __device__ __forceinline__ Op8 k_operand(const char* page, int ks) const {
     const char* kr = page + l16 * Gm::RB;
     if constexpr (I8) {
       const int byte = c * (D / 4) + 8 * ks;
-      const u32x2 w = ld64(kr + ((byte / 16) ^ swz_k<Gm::CPR>(l16)) * 16 + byte % 16);
-      u32x4 r;
-      r[0] = codes2_to_bf16x2(w[0], 0);
-      r[1] = codes2_to_bf16x2(w[0], 16);
-      r[2] = codes2_to_bf16x2(w[1], 0);
-      r[3] = codes2_to_bf16x2(w[1], 16);
-      return __builtin_bit_cast(bf16x8, r);
+      const u32x2 w = ld64(kr + ((byte / 16) ^ Gm::swz_k(l16)) * 16 + byte % 16);
+      return codes8_to_f16(w[0], w[1]);
     } else {
       const int kappa = c * (Gm::CPR / 4) + ks;
-      return __builtin_bit_cast(bf16x8, ld128(kr + (kappa ^ swz_k<Gm::CPR>(l16)) * 16));
+      return __builtin_bit_cast(bf16x8, ld128(kr + (kappa ^ Gm::swz_k(l16)) * 16));
     }
   }
 
-  // A operand of O^T += V^T P^T: V rows 4c .. 4c+3, column 16 db + l16;
-  // bf16 rows at or past `valid_rows` read as zero (NaN-safe)
-  __device__ __forceinline__ i16x4 v_operand(const char* page, int db, int valid_rows) const {
-    const char* vb = page + Gm::PAGE;
-    uint32_t e[4];
+  // A operand of O^T += V^T P^T for d columns 16db .. 16db+15: lane (l16, c)
+  // receives V[token 4c + e%4 of page e/4][16 db + l16], e = 0..7.
+  __device__ __forceinline__ Op8 v_operand(const char* sa, const char* sb, int db) const {
     if constexpr (I8) {
-      const int col = 16 * db + l16;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int rho = 4 * c + i;
-        const int8_t code = *reinterpret_cast<const int8_t*>(
-            vb + rho * Gm::RB + ((col / 16) ^ swz_v<Gm::CPR>(rho)) * 16 + col % 16);
-        e[i] = __float_as_uint(float(code)) >> 16;
-      }
+      // ds_read_b64_tr_b8: lane j of a 16-lane group receives byte e from the
+      // 8-byte block addressed by lane 2e + j/8, at column j%8.  Lane 2e + h
+      // therefore addresses V[token e][16 db + 8h .. +8].
+      const int e = l16 >> 1, h = l16 & 1;
+      const int rho = 4 * c + (e & 3);
+      const char* src = (e < 4 ? sa : sb) + Gm::PAGE + rho * Gm::RB +
+                        (db ^ Gm::swz_v(rho)) * 16 + 8 * h;
+      const i32x2 w = __builtin_amdgcn_ds_read_tr8_b64_v2i32((AS3 i32x2*)src);
+      return codes8_to_f16(uint32_t(w[0]), uint32_t(w[1]));
     } else {
-      const int kappa = 2 * db + (l16 >> 3);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int rho = 4 * c + i;
-        e[i] = *reinterpret_cast<const uint16_t*>(vb + rho * Gm::RB +
-                                                  (kappa ^ swz_v<Gm::CPR>(rho)) * 16 +
-                                                  2 * (l16 & 7));
-        e[i] = (rho < valid_rows) ? e[i] : 0u;
-      }
+      // ds_read_b64_tr_b16: lane j of a 16-lane group receives element e from
+      // the 8-byte block addressed by lane 4e + j/4, at column j%4.  Lane 4e + q
+      // therefore addresses V[row 4c + e][16 db + 4q .. +4], once per page.
+      const int e = l16 >> 2, q = l16 & 3;
+      const int rho = 4 * c + e;
+      const int off = Gm::PAGE + rho * Gm::RB + ((2 * db + (q >> 1)) ^ Gm::swz_v(rho)) * 16 +
+                      8 * (q & 1);
+      const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((AS3 bf16x4*)(sa + off));
+      const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((AS3 bf16x4*)(sb + off));
+      const u32x2 a = __builtin_bit_cast(u32x2, lo), b = __builtin_bit_cast(u32x2, hi);
+      return __builtin_bit_cast(bf16x8, u32x4{a[0], a[1], b[0], b[1]});
     }
-    return __builtin_bit_cast(i16x4, u32x2{e[0] | (e[1] << 16), e[2] | (e[3] << 16)});
   }
 
   __device__ __forceinline__ void step(const AttnParams&, const char* sa, const char* sb, int a,
@@ -768,31 +855,53 @@ struct MfmaStep {
 #pragma unroll
     for (int pg = 0; pg < 2; ++pg) {
 #pragma unroll
-      for (int rb = 0; rb < NRB; ++rb) s[pg][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int rb = 0; rb < NRB; ++rb) {
+        const float z = I8 ? s0[rb] : 0.f;
+        s[pg][rb] = f32x4{z, z, z, z};
+      }
       const char* page = pg ? sb : sa;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 ka = k_operand(page, ks);
+        const Op8 ka = k_operand(page, ks);
 #pragma unroll
-        for (int rb = 0; rb < NRB; ++rb)
-          s[pg][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qB[rb][ks], s[pg][rb], 0, 0, 0);
+        for (int rb = 0; rb < NRB; ++rb) s[pg][rb] = mfma32(ka, qB[rb][ks], s[pg][rb]);
       }
     }
-    f32x4 ksc[2], vsc[2];
-    if constexpr (I8) {
+    // per-token factors: score scale (times the K scale) and V scale
+    float kf[2][4], vf[2][4];
 #pragma unroll
-      for (int pg = 0; pg < 2; ++pg) {
+    for (int pg = 0; pg < 2; ++pg) {
+      if constexpr (I8) {
         const char* sc = (pg ? sb : sa) + 2 * Gm::PAGE;
         const u32x2 kw = ld64(sc + 8 * c), vw = ld64(sc + 32 + 8 * c);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          ksc[pg][i] = f16_bits_to_f32(uint16_t(kw[i / 2] >> (16 * (i & 1))));
           const int pos = (a + pg) * kPage + 4 * c + i;
-          vsc[pg][i] = (pos < valid_end) ? f16_bits_to_f32(uint16_t(vw[i / 2] >> (16 * (i & 1)))) : 0.f;
+          kf[pg][i] = f16_bits_to_f32(uint16_t(kw[i / 2] >> (16 * (i & 1)))) * scale_log2;
+          vf[pg][i] = (pos < valid_end) ? f16_bits_to_f32(uint16_t(vw[i / 2] >> (16 * (i & 1)))) : 0.f;
         }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) kf[pg][i] = scale_log2;
       }
     }
-    i16x4 pB[2][NRB];
+    // V^T operands, loaded ahead of the softmax
+    Op8 va[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) va[db] = v_operand(sa, sb, db);
+    if constexpr (!I8) {
+      if ((a + 2) * kPage > valid_end) {          // garbage rows (may be NaN) read as zero
+        u32x4 keep;
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          const int p0 = (a + (h >> 1)) * kPage + 4 * c + 2 * (h & 1);
+          keep[h] = (p0 < valid_end ? 0x0000ffffu : 0u) | (p0 + 1 < valid_end ? 0xffff0000u : 0u);
+        }
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+          va[db] = __builtin_bit_cast(Op8, __builtin_bit_cast(u32x4, va[db]) & keep);
+      }
+    }
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
       float x[2][4];
@@ -802,52 +911,53 @@ struct MfmaStep {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int pos = (a + pg) * kPage + 4 * c + i;
-          float v = s[pg][rb][i] * scale_log2;
-          if constexpr (I8) v *= ksc[pg][i];
-          v = (pg < npg && pos <= lim[rb]) ? v : -INFINITY;
-          x[pg][i] = v;
-          mx = fmaxf(mx, v);
+          const float v = s[pg][rb][i] * kf[pg][i];
+          x[pg][i] = (pg < npg && pos <= lim[rb]) ? v : -INFINITY;
+          mx = fmaxf(mx, x[pg][i]);
         }
       }
       mx = xrow32_max(xrow16_max(mx));                          // over the 4 lanes of the row
-      const float mn = fmaxf(m[rb], mx);
-      const float alpha = exp2f(m[rb] - mn);
-      m[rb] = mn;
-      float psum = 0.f;
+      if (__ballot(mx > m[rb] + kLazy)) {                       // some row's reference moves
+        const float mn = (mx > m[rb] + kLazy) ? mx : m[rb];
+        const float alpha = __builtin_amdgcn_exp2f(m[rb] - mn);
+        m[rb] = mn;
+        l[rb] *= alpha;
 #pragma unroll
-      for (int pg = 0; pg < 2; ++pg) {
-        float w[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float e = exp2f(x[pg][i] - mn);
-          psum += e;
-          w[i] = e;
-          if constexpr (I8) w[i] = e * vsc[pg][i];
-        }
-        pB[pg][rb] = __builtin_bit_cast(i16x4, u32x2{pack_bf16x2(w[0], w[1]), pack_bf16x2(w[2], w[3])});
-      }
-      l[rb] = l[rb] * alpha + psum;
-      if (__ballot(alpha != 1.f)) {                             // some row's maximum moved
+        for (int i = 0; i < 4; ++i) sacc[rb][i] *= alpha;
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) acc[rb][db][i] *= alpha;
         }
       }
-    }
-    // Without a second page its probabilities are 0 and its V rows are zeroed
-    // (valid_rows <= 0) or scaled by 0, so the product adds nothing.
+      float w[8];
+      float psum = 0.f;
 #pragma unroll
-    for (int pg = 0; pg < 2; ++pg) {
-      const char* page = pg ? sb : sa;
-      const int valid_rows = valid_end - (a + pg) * kPage;      // < 16 only on the last page
+      for (int pg = 0; pg < 2; ++pg) {
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const i16x4 va = v_operand(page, db, valid_rows);
-#pragma unroll
-        for (int rb = 0; rb < NRB; ++rb)
-          acc[rb][db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pB[pg][rb], acc[rb][db], 0, 0, 0);
+        for (int i = 0; i < 4; ++i) {
+          const float e = __builtin_amdgcn_exp2f(x[pg][i] - m[rb]);
+          if constexpr (I8) {
+            psum += e;
+            w[4 * pg + i] = e * vf[pg][i];
+          } else {
+            w[4 * pg + i] = e;
+          }
+        }
       }
+      u32x4 pw;
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        if constexpr (I8)
+          pw[h] = uint32_t(f32_to_f16_bits(w[2 * h])) | (uint32_t(f32_to_f16_bits(w[2 * h + 1])) << 16);
+        else
+          pw[h] = pack_bf16x2(w[2 * h], w[2 * h + 1]);
+      }
+      const Op8 pb = __builtin_bit_cast(Op8, pw);
+      if constexpr (I8) l[rb] += psum;
+      sacc[rb] = mfma32(ones(), pb, sacc[rb]);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) acc[rb][db] = mfma32(va[db], pb, acc[rb][db]);
     }
   }
 
@@ -863,7 +973,19 @@ struct MfmaStep {
   }
   __device__ __forceinline__ void finish() {
 #pragma unroll
-    for (int rb = 0; rb < NRB; ++rb) l[rb] = xrow32_sum(xrow16_sum(l[rb]));
+    for (int rb = 0; rb < NRB; ++rb) {
+      if constexpr (I8) {
+        l[rb] = xrow32_sum(xrow16_sum(l[rb]));
+        const float off = kCodeBias * sacc[rb][0];             // remove 1152 * sum of weights
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[rb][db][i] -= off;
+        }
+      } else {
+        l[rb] = sacc[rb][0];
+      }
+    }
   }
 
   static constexpr int SLOT_F = NRB * NDB * kWave * 4 + 2 * NRB * kWave;
@@ -996,35 +1118,35 @@ __device__ __forceinline__ void merge_pair(const AttnParams& p, const Seg& sg, i
 // kernel
 // ============================================================================
 
-template <typename KV, int D>
+template <typename KV, int D, bool MF>
 struct AttnLds {
   static constexpr int RING = kWaves * Geo<KV, D>::RING;
-  static constexpr int QS = kValuRows * 2 * (D / 2 + 4);      // dwords (fp32 layout, the larger)
-  static constexpr int PS = kValuRows * 32 * 4;               // bytes per wave
+  // VALU passes stage their query rows and per-wave probabilities in LDS
+  static constexpr int QS = MF ? 4 : kValuRows * 2 * (D / 2 + 4);   // dwords (fp32 layout, the larger)
+  static constexpr int PS = MF ? 16 : kValuRows * 32 * 4;           // bytes per wave
 };
 
-template <typename KV, int D>
+// The MFMA and VALU variants are separate kernels, so that each gets its own
+// register allocation.
+template <typename KV, int D, bool MF>
 __device__ __forceinline__ void process_segment(const AttnParams& p, const Seg& sg, char* ring,
                                                 uint32_t* qs, char* ps_all) {
-  if constexpr (sizeof(KV) != 4) {
-    const bool use_mfma = p.path != 1;
-    if (use_mfma) {
-      for (int r0 = 0; r0 < sg.R; r0 += kMfmaRows) {
-        if (sg.R - r0 > 16) {
-          MfmaStep<KV, D, 2> st(p, sg, r0);
-          pass<KV, D>(p, sg, r0, st, ring);
-        } else {
-          MfmaStep<KV, D, 1> st(p, sg, r0);
-          pass<KV, D>(p, sg, r0, st, ring);
-        }
+  if constexpr (MF) {
+    for (int r0 = 0; r0 < sg.R; r0 += kMfmaRows) {
+      if (sg.R - r0 > 16) {
+        MfmaStep<KV, D, 2> st(p, sg, r0);
+        pass<KV, D>(p, sg, r0, st, ring);
+      } else {
+        MfmaStep<KV, D, 1> st(p, sg, r0);
+        pass<KV, D>(p, sg, r0, st, ring);
       }
-      return;
     }
+    return;
   }
   // fp32 caches take at most 8 rows per pass (16 fp32 rows exceed the register file)
   constexpr bool F32 = sizeof(KV) == 4;
   constexpr int kRows = F32 ? 8 : kValuRows;
-  char* ps = ps_all + wave_id() * AttnLds<KV, D>::PS;
+  char* ps = ps_all + wave_id() * AttnLds<KV, D, MF>::PS;
   for (int r0 = 0; r0 < sg.R; r0 += kRows) {
     valu_stage_q<D, F32>(p, sg, r0, qs);
     __syncthreads();
@@ -1042,9 +1164,9 @@ __device__ __forceinline__ void process_segment(const AttnParams& p, const Seg& 
   }
 }
 
-template <typename KV, int D>
+template <typename KV, int D, bool MF>
 __global__ __launch_bounds__(kAttnThreads, 1) void verify_attn_kernel(AttnParams p) {
-  using L = AttnLds<KV, D>;
+  using L = AttnLds<KV, D, MF>;
   __shared__ __attribute__((aligned(1024))) char s_ring[L::RING];
   __shared__ __attribute__((aligned(16))) uint32_t s_q[L::QS];
   __shared__ __attribute__((aligned(16))) char s_ps[kWaves * L::PS];
@@ -1138,7 +1260,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void verify_attn_kernel(AttnParams
     sg.full = (cur == pb) && (se == pend);
     sg.slot = (cur == g0) ? 2 * w : 2 * w + 1;
 
-    process_segment<KV, D>(p, sg, s_ring, s_q, s_ps);
+    process_segment<KV, D, MF>(p, sg, s_ring, s_q, s_ps);
 
     if (!sg.full) {
       // every thread's partial stores are complete at device scope before the
@@ -1195,8 +1317,14 @@ AttnPlan plan_verify_attn(const sva_batch* batch, const sva_paged_kv* kv, int Hq
 }
 
 template <typename KV, int D>
-static hipError_t attn_launch(const AttnParams& p, hipStream_t st) {
-  hipLaunchKernelGGL((verify_attn_kernel<KV, D>), dim3(p.W), dim3(kAttnThreads), 0, st, p);
+static hipError_t attn_launch(const AttnParams& p, bool mfma, hipStream_t st) {
+  if constexpr (sizeof(KV) == 4) {
+    hipLaunchKernelGGL((verify_attn_kernel<KV, D, false>), dim3(p.W), dim3(kAttnThreads), 0, st, p);
+  } else if (mfma) {
+    hipLaunchKernelGGL((verify_attn_kernel<KV, D, true>), dim3(p.W), dim3(kAttnThreads), 0, st, p);
+  } else {
+    hipLaunchKernelGGL((verify_attn_kernel<KV, D, false>), dim3(p.W), dim3(kAttnThreads), 0, st, p);
+  }
   return hipGetLastError();
 }
 
@@ -1229,12 +1357,13 @@ hipError_t launch_verify_attn(const sva_batch* batch, const void* q, int q_dtype
   p.max_q = batch->max_q;
   p.slot_rows = plan.slot_rows;
   p.W = plan.num_wg;
-  p.path = path;
+  const bool mfma = path != 1;         // fp32 caches always take the VALU kernel
   if (kv->kv_dtype == SVA_F32)
-    return kv->d == 64 ? attn_launch<float, 64>(p, st) : attn_launch<float, 128>(p, st);
+    return kv->d == 64 ? attn_launch<float, 64>(p, false, st) : attn_launch<float, 128>(p, false, st);
   if (kv->kv_dtype == SVA_BF16)
-    return kv->d == 64 ? attn_launch<uint16_t, 64>(p, st) : attn_launch<uint16_t, 128>(p, st);
-  return kv->d == 64 ? attn_launch<int8_t, 64>(p, st) : attn_launch<int8_t, 128>(p, st);
+    return kv->d == 64 ? attn_launch<uint16_t, 64>(p, mfma, st)
+                       : attn_launch<uint16_t, 128>(p, mfma, st);
+  return kv->d == 64 ? attn_launch<int8_t, 64>(p, mfma, st) : attn_launch<int8_t, 128>(p, mfma, st);
 }
 
 }  // namespace sva
