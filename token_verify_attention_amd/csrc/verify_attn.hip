@@ -47,15 +47,20 @@
 
 namespace sva {
 
-constexpr int kAttnThreads = 256;
-constexpr int kWaves = kAttnThreads / kWave;   // 4
+// Waves per workgroup: the INT8 MFMA kernel runs 8 (two per SIMD, so one
+// wave's LDS, conversion and MFMA latencies hide behind the other's work; its
+// pages are small enough for two ring steps per wave), the others 4 (bf16
+// pages fill the ring with 4 waves x 2 steps; the VALU kernels' register use
+// allows one wave per SIMD only).
+constexpr int kWavesInt8 = 8;
+constexpr int kWavesValu = 4;
 // The workspace starts with one completion counter per possible workgroup, at a
 // fixed size, so partial slots of one call never overlap the counters of a
 // later call with a different grid.
 constexpr int kMaxWorkgroups = 4096;
 constexpr int kMfmaRows = 32;
 constexpr int kValuRows = 16;
-constexpr int kRingBudget = 128 * 1024;        // LDS bytes for the page rings of 4 waves
+constexpr int kRingBudget = 136 * 1024;        // LDS bytes for the page rings of all waves
 constexpr float kNegBig = -1.0e30f;            // finite start value of running maxima
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -181,7 +186,7 @@ __device__ __forceinline__ void store_out1(const AttnParams& p, int64_t elem, fl
 // page ring: geometry, DMA and waits
 // ============================================================================
 
-template <typename KV, int D>
+template <typename KV, int D, int NW>
 struct Geo {
   static constexpr int ES = int(sizeof(KV));
   static constexpr int RB = D * ES;                  // bytes per K (or V) row
@@ -191,7 +196,7 @@ struct Geo {
   static constexpr int SLOT = 2 * PAGE + SCALES;     // one ring slot: K page, V page, scales
   static constexpr int DMA = PAGE / 1024;            // dwordx4 DMA instructions per page half
   static constexpr int P = 2 * DMA + (ES == 1 ? 2 : 0);   // DMA instructions per page
-  static constexpr int S_RAW = kRingBudget / (kWaves * 2 * SLOT);
+  static constexpr int S_RAW = kRingBudget / (NW * 2 * SLOT);
   static constexpr int S = S_RAW < 1 ? 1 : (S_RAW > 3 ? 3 : S_RAW);   // steps held in the ring
   static constexpr int RING = 2 * S * SLOT;          // bytes per wave
 
@@ -233,7 +238,7 @@ __device__ __forceinline__ void dma4(const void* g, void* l) {
 // Page `pid` of kv head g -> ring slot (K page, V page, INT8 scales).
 template <typename KV, int D>
 __device__ __forceinline__ void dma_page(const AttnParams& p, int pid, int g, char* slot) {
-  using Gm = Geo<KV, D>;
+  using Gm = Geo<KV, D, kWavesValu>;      // page geometry only
   const int lane = lane_id();
   const int64_t off = (int64_t(pid) * p.Hkv + g) * Gm::PAGE;
   const char* kb = static_cast<const char*>(p.k) + off;
@@ -273,11 +278,11 @@ __device__ __forceinline__ void wait_steps(int pending) {
 // Streams this wave's pages of the segment through its ring and calls
 // st.step(slot of page a, slot of page a+1, a, page a+1 exists) for each pair
 // of consecutive pages (a = pa + 2u, u = wave, wave + 4, ...).
-template <typename KV, int D>
+template <typename KV, int D, int NW>
 __device__ __forceinline__ void issue_step(const AttnParams& p, const Seg& sg, char* ring, int wave,
                                            int s) {
-  using Gm = Geo<KV, D>;
-  const int a = sg.pa + 2 * (wave + kWaves * s);
+  using Gm = Geo<KV, D, NW>;
+  const int a = sg.pa + 2 * (wave + NW * s);
   const int ida = page_id(p, sg.b, a);
   const int idb = (a + 1 < sg.pe) ? page_id(p, sg.b, a + 1) : ida;
   char* slots = ring + (s % Gm::S) * 2 * Gm::SLOT;
@@ -287,25 +292,25 @@ __device__ __forceinline__ void issue_step(const AttnParams& p, const Seg& sg, c
 
 // Streams this wave's pages of the segment through its ring and calls
 // st.step(p, slot of page a, slot of page a+1, a, page a+1 exists) for each
-// pair of consecutive pages (a = pa + 2u, u = wave, wave + 4, ...).
-template <typename KV, int D, class Step>
+// pair of consecutive pages (a = pa + 2u, u = wave, wave + NW, ...).
+template <typename KV, int D, int NW, class Step>
 __device__ __forceinline__ void run_pages(const AttnParams& p, const Seg& sg, char* ring,
                                           Step& st) {
-  using Gm = Geo<KV, D>;
+  using Gm = Geo<KV, D, NW>;
   constexpr int S = Gm::S, P2 = 2 * Gm::P;
   const int wave = wave_id();
   const int npair = (sg.pe - sg.pa + 1) >> 1;
-  const int n = npair > wave ? (npair - wave + kWaves - 1) / kWaves : 0;
+  const int n = npair > wave ? (npair - wave + NW - 1) / NW : 0;
   const int pro = n < S ? n : S;
-  for (int s = 0; s < pro; ++s) issue_step<KV, D>(p, sg, ring, wave, s);
+  for (int s = 0; s < pro; ++s) issue_step<KV, D, NW>(p, sg, ring, wave, s);
   st.ready();
   for (int s = 0; s < n; ++s) {
     wait_steps<P2, S>(min(S - 1, n - 1 - s));
     const char* slots = ring + (s % S) * 2 * Gm::SLOT;
-    const int a = sg.pa + 2 * (wave + kWaves * s);
+    const int a = sg.pa + 2 * (wave + NW * s);
     st.step(p, slots, slots + Gm::SLOT, a, a + 1 < sg.pe);
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // this step's LDS reads are done
-    if (s + S < n) issue_step<KV, D>(p, sg, ring, wave, s + S);
+    if (s + S < n) issue_step<KV, D, NW>(p, sg, ring, wave, s + S);
   }
 }
 
@@ -343,7 +348,7 @@ __device__ __forceinline__ void valu_stage_q(const AttnParams& p, const Seg& sg,
   constexpr int HALF = D / 2;
   if constexpr (F32) {
     constexpr int QS = HALF + 4;
-    for (int idx = threadIdx.x; idx < kValuRows * D; idx += kAttnThreads) {
+    for (int idx = threadIdx.x; idx < kValuRows * D; idx += kWavesValu * kWave) {
       const int r = idx / D, d = idx % D;
       float v = 0.f;
       if (r0 + r < sg.R) {
@@ -355,7 +360,7 @@ __device__ __forceinline__ void valu_stage_q(const AttnParams& p, const Seg& sg,
     }
   } else {
     constexpr int QS = HALF / 2 + 4;
-    for (int idx = threadIdx.x; idx < kValuRows * (D / 2); idx += kAttnThreads) {
+    for (int idx = threadIdx.x; idx < kValuRows * (D / 2); idx += kWavesValu * kWave) {
       const int r = idx / (D / 2), d2 = idx % (D / 2);       // pair of d = 2*d2, 2*d2+1
       uint32_t w = 0;
       if (r0 + r < sg.R) {
@@ -374,7 +379,7 @@ __device__ __forceinline__ void valu_stage_q(const AttnParams& p, const Seg& sg,
 
 template <typename KV, int D, int RV>
 struct ValuStep {
-  using Gm = Geo<KV, D>;
+  using Gm = Geo<KV, D, kWavesValu>;      // page geometry only
   static constexpr bool F32 = sizeof(KV) == 4;
   static constexpr bool I8 = sizeof(KV) == 1;
   static constexpr int HALF = D / 2;                  // d values per lane in QK
@@ -735,7 +740,7 @@ __device__ __forceinline__ f16x8 codes8_to_f16(uint32_t w0, uint32_t w1) {
 //    leaves O through the MFMA-computed sum of the fp16 weights.
 template <typename KV, int D, int NRB>
 struct MfmaStep {
-  using Gm = Geo<KV, D>;
+  using Gm = Geo<KV, D, kWavesValu>;      // page geometry only
   static constexpr bool I8 = sizeof(KV) == 1;
   using Op8 = typename std::conditional<I8, f16x8, bf16x8>::type;
   static constexpr int KS = D / 32;       // 16x16x32 k-steps over d (S^T)
@@ -905,23 +910,31 @@ struct MfmaStep {
           va[db] = __builtin_bit_cast(Op8, __builtin_bit_cast(u32x4, va[db]) & keep);
       }
     }
+    // Masked scores and row maxima of every row block first, then one
+    // wave-uniform decision for all of them, so that the blocks' work stays
+    // straight-line code the compiler can interleave.
+    float x[NRB][2][4], mx[NRB];
+    bool move = false;
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
-      float x[2][4];
-      float mx = -INFINITY;
+      float t = -INFINITY;
 #pragma unroll
       for (int pg = 0; pg < 2; ++pg) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int pos = (a + pg) * kPage + 4 * c + i;
           const float v = s[pg][rb][i] * kf[pg][i];
-          x[pg][i] = (pg < npg && pos <= lim[rb]) ? v : -INFINITY;
-          mx = fmaxf(mx, x[pg][i]);
+          x[rb][pg][i] = (pg < npg && pos <= lim[rb]) ? v : -INFINITY;
+          t = fmaxf(t, x[rb][pg][i]);
         }
       }
-      mx = xrow32_max(xrow16_max(mx));                          // over the 4 lanes of the row
-      if (__ballot(mx > m[rb] + kLazy)) {                       // some row's reference moves
-        const float mn = (mx > m[rb] + kLazy) ? mx : m[rb];
+      mx[rb] = xrow32_max(xrow16_max(t));                       // over the 4 lanes of the row
+      move |= mx[rb] > m[rb] + kLazy;
+    }
+    if (__ballot(move)) {                                       // some row's reference moves
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb) {
+        const float mn = (mx[rb] > m[rb] + kLazy) ? mx[rb] : m[rb];
         const float alpha = __builtin_amdgcn_exp2f(m[rb] - mn);
         m[rb] = mn;
         l[rb] *= alpha;
@@ -933,13 +946,16 @@ struct MfmaStep {
           for (int i = 0; i < 4; ++i) acc[rb][db][i] *= alpha;
         }
       }
+    }
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
       float w[8];
       float psum = 0.f;
 #pragma unroll
       for (int pg = 0; pg < 2; ++pg) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float e = __builtin_amdgcn_exp2f(x[pg][i] - m[rb]);
+          const float e = __builtin_amdgcn_exp2f(x[rb][pg][i] - m[rb]);
           if constexpr (I8) {
             psum += e;
             w[4 * pg + i] = e * vf[pg][i];
@@ -1048,27 +1064,25 @@ struct MfmaStep {
 };
 
 // One pass over the segment's pages for rows r0.. of the pair: stream, then
-// merge the 4 waves through LDS (the ring is idle by then) and let wave 0
-// write the output rows or the partial slot.
-template <typename KV, int D, class St>
+// merge the NW waves pairwise through LDS (the ring is idle by then) and let
+// wave 0 write the output rows or the partial slot.
+template <typename KV, int D, int NW, class St>
 __device__ __forceinline__ void pass(const AttnParams& p, const Seg& sg, int r0, St& st,
                                      char* ring_all) {
   const int wave = wave_id();
-  run_pages<KV, D>(p, sg, ring_all + wave * Geo<KV, D>::RING, st);
+  run_pages<KV, D, NW>(p, sg, ring_all + wave * Geo<KV, D, NW>::RING, st);
   st.finish();
   __syncthreads();                                    // every wave is off the ring
   float* mrg = reinterpret_cast<float*>(ring_all);
   constexpr int SLOT = St::SLOT_F;
-  if (wave >= 2) st.store(mrg + (wave - 2) * SLOT);
-  __syncthreads();
-  if (wave < 2) st.combine(mrg + wave * SLOT);
-  __syncthreads();
-  if (wave == 1) st.store(mrg);
-  __syncthreads();
-  if (wave == 0) {
-    st.combine(mrg);
-    st.write(p, sg, r0);
+#pragma unroll
+  for (int half = NW / 2; half >= 1; half /= 2) {
+    if (wave >= half && wave < 2 * half) st.store(mrg + (wave - half) * SLOT);
+    __syncthreads();
+    if (wave < half) st.combine(mrg + wave * SLOT);
+    __syncthreads();
   }
+  if (wave == 0) st.write(p, sg, r0);
   __syncthreads();
 }
 
@@ -1088,32 +1102,70 @@ __device__ __forceinline__ int slot_of(int w, int64_t pair_begin, int64_t N, int
   return (max(s, pair_begin) == s) ? 2 * w : 2 * w + 1;
 }
 
-template <int D>
+template <int D, int NT>
 __device__ __forceinline__ void merge_pair(const AttnParams& p, const Seg& sg, int64_t pb, int64_t pend,
                            int64_t N) {
+  // Each thread merges up to kItems (row, 4-column) items; the loads of one
+  // slot for all of them are issued together, so the merge costs one
+  // device-scope load latency per slot instead of one per item and slot.
+  constexpr int kItems = 4;
   const int wf = wg_of(pb, N, p.W), wl = wg_of(pend - 1, N, p.W);
   const int items = sg.R * (D / 4);
-  for (int it = threadIdx.x; it < items; it += kAttnThreads) {
-    const int r = it / (D / 4), d4 = it % (D / 4);
-    float M = kNegBig, L = 0.f;
-    f32x4 O = {0.f, 0.f, 0.f, 0.f};
-    for (int w = wf; w <= wl; ++w) {
-      if (range_start(w + 1, N, p.W) == range_start(w, N, p.W)) continue;   // empty range
-      const float* sb = slot_base<D>(p, slot_of(w, pb, N, p.W));
-      const float ms = ld_dev(sb + int64_t(p.slot_rows) * D + r);
-      const float ls = ld_dev(sb + int64_t(p.slot_rows) * (D + 1) + r);
-      const f32x4 os = ld_dev4(sb + int64_t(r) * D + 4 * d4);
-      const float Mn = fmaxf(M, ms);
-      const float fa = exp2f(M - Mn), fb = exp2f(ms - Mn);
-      L = fa * L + fb * ls;
+  for (int base = 0; base < items; base += kItems * NT) {
+    float M[kItems], L[kItems];
+    f32x4 O[kItems];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) O[i] = fa * O[i] + fb * os[i];
-      M = Mn;
+    for (int u = 0; u < kItems; ++u) {
+      M[u] = kNegBig;
+      L[u] = 0.f;
+      O[u] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    const float inv = 1.f / L;
+    // two slots per round (a pair usually spans two workgroups)
+    for (int w0 = wf; w0 <= wl; w0 += 2) {
+      float ms[2][kItems], ls[2][kItems];
+      f32x4 os[2][kItems];
+      bool use[2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) O[i] *= inv;
-    store_out4(p, out_row(p, sg, r) * D + 4 * d4, O);
+      for (int h = 0; h < 2; ++h) {
+        const int w = w0 + h;
+        use[h] = w <= wl && range_start(w + 1, N, p.W) > range_start(w, N, p.W);   // non-empty
+        const float* sb = slot_base<D>(p, slot_of(use[h] ? w : w0, pb, N, p.W));
+#pragma unroll
+        for (int u = 0; u < kItems; ++u) {
+          const int it = base + u * NT + threadIdx.x;
+          const int r = min(it, items - 1) / (D / 4), d4 = min(it, items - 1) % (D / 4);
+          if (use[h]) {
+            ms[h][u] = ld_dev(sb + int64_t(p.slot_rows) * D + r);
+            ls[h][u] = ld_dev(sb + int64_t(p.slot_rows) * (D + 1) + r);
+            os[h][u] = ld_dev4(sb + int64_t(r) * D + 4 * d4);
+          }
+        }
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        if (!use[h]) continue;
+#pragma unroll
+        for (int u = 0; u < kItems; ++u) {
+          const float Mn = fmaxf(M[u], ms[h][u]);
+          const float fa = exp2f(M[u] - Mn), fb = exp2f(ms[h][u] - Mn);
+          L[u] = fa * L[u] + fb * ls[h][u];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) O[u][i] = fa * O[u][i] + fb * os[h][u][i];
+          M[u] = Mn;
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kItems; ++u) {
+      const int it = base + u * NT + threadIdx.x;
+      if (it >= items) continue;
+      const int r = it / (D / 4), d4 = it % (D / 4);
+      const float inv = 1.f / L[u];
+      f32x4 o = O[u];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] *= inv;
+      store_out4(p, out_row(p, sg, r) * D + 4 * d4, o);
+    }
   }
 }
 
@@ -1123,7 +1175,13 @@ __device__ __forceinline__ void merge_pair(const AttnParams& p, const Seg& sg, i
 
 template <typename KV, int D, bool MF>
 struct AttnLds {
-  static constexpr int RING = kWaves * Geo<KV, D>::RING;
+  static constexpr int NW = (MF && sizeof(KV) == 1) ? kWavesInt8 : kWavesValu;
+  static constexpr int NT = NW * kWave;
+  static constexpr int RING = NW * Geo<KV, D, NW>::RING;
+  // the wave merge reuses the ring: NW/2 slots of the largest step state
+  static constexpr int MERGE = (NW / 2) * 4 * (MF ? (2 * (D / 16) * kWave * 4 + 4 * kWave)
+                                                  : (kValuRows * D * 2 + 64));
+  static constexpr int RING_ALLOC = RING > MERGE ? RING : MERGE;
   // VALU passes stage their query rows and per-wave probabilities in LDS
   static constexpr int QS = MF ? 4 : kValuRows * 2 * (D / 2 + 4);   // dwords (fp32 layout, the larger)
   static constexpr int PS = MF ? 16 : kValuRows * 32 * 4;           // bytes per wave
@@ -1138,10 +1196,10 @@ __device__ __forceinline__ void process_segment(const AttnParams& p, const Seg& 
     for (int r0 = 0; r0 < sg.R; r0 += kMfmaRows) {
       if (sg.R - r0 > 16) {
         MfmaStep<KV, D, 2> st(p, sg, r0);
-        pass<KV, D>(p, sg, r0, st, ring);
+        pass<KV, D, AttnLds<KV, D, MF>::NW>(p, sg, r0, st, ring);
       } else {
         MfmaStep<KV, D, 1> st(p, sg, r0);
-        pass<KV, D>(p, sg, r0, st, ring);
+        pass<KV, D, AttnLds<KV, D, MF>::NW>(p, sg, r0, st, ring);
       }
     }
     return;
@@ -1156,24 +1214,25 @@ __device__ __forceinline__ void process_segment(const AttnParams& p, const Seg& 
     const int rn = sg.R - r0;
     if (rn <= 4) {
       ValuStep<KV, D, 4> st(p, sg, r0, qs, ps);
-      pass<KV, D>(p, sg, r0, st, ring);
+      pass<KV, D, AttnLds<KV, D, MF>::NW>(p, sg, r0, st, ring);
     } else if (F32 || rn <= 8) {
       ValuStep<KV, D, 8> st(p, sg, r0, qs, ps);
-      pass<KV, D>(p, sg, r0, st, ring);
+      pass<KV, D, AttnLds<KV, D, MF>::NW>(p, sg, r0, st, ring);
     } else {
       ValuStep<KV, D, 16> st(p, sg, r0, qs, ps);
-      pass<KV, D>(p, sg, r0, st, ring);
+      pass<KV, D, AttnLds<KV, D, MF>::NW>(p, sg, r0, st, ring);
     }
   }
 }
 
 template <typename KV, int D, bool MF>
-__global__ __launch_bounds__(kAttnThreads, 1) void verify_attn_kernel(AttnParams p) {
+__global__ __launch_bounds__((AttnLds<KV, D, MF>::NT), 1) void verify_attn_kernel(AttnParams p) {
   using L = AttnLds<KV, D, MF>;
-  __shared__ __attribute__((aligned(1024))) char s_ring[L::RING];
+  constexpr int NT = L::NT;
+  __shared__ __attribute__((aligned(1024))) char s_ring[L::RING_ALLOC];
   __shared__ __attribute__((aligned(16))) uint32_t s_q[L::QS];
-  __shared__ __attribute__((aligned(16))) char s_ps[kWaves * L::PS];
-  __shared__ int32_t s_scan[kAttnThreads];
+  __shared__ __attribute__((aligned(16))) char s_ps[L::NW * L::PS];
+  __shared__ int32_t s_scan[NT];
   __shared__ int32_t s_info[4];
   __shared__ int s_flag;
 
@@ -1181,7 +1240,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void verify_attn_kernel(AttnParams
   const int B = p.B;
 
   // ---- pages per sequence: each thread sums a contiguous chunk of sequences
-  const int per = (B + kAttnThreads - 1) / kAttnThreads;
+  const int per = (B + NT - 1) / NT;
   int tot = 0;
   for (int e = 0; e < per; ++e) {
     const int b = tid * per + e;
@@ -1190,7 +1249,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void verify_attn_kernel(AttnParams
   s_scan[tid] = tot;
   __syncthreads();
   if (tid < kWave) {                                  // exclusive scan of the chunk sums
-    constexpr int PER_LANE = kAttnThreads / kWave;
+    constexpr int PER_LANE = NT / kWave;
     int run = 0;
     for (int i = 0; i < PER_LANE; ++i) {
       const int v = s_scan[tid * PER_LANE + i];
@@ -1281,7 +1340,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void verify_attn_kernel(AttnParams
       }
       __syncthreads();
       if (s_flag) {      // the last workgroup of the pair: all partials are visible
-        merge_pair<D>(p, sg, pb, pend, N);
+        merge_pair<D, NT>(p, sg, pb, pend, N);
         if (tid == 0)
           __hip_atomic_store(p.counters + wg_of(pb, N, p.W), 0, __ATOMIC_RELAXED,
                              __HIP_MEMORY_SCOPE_AGENT);
@@ -1322,11 +1381,14 @@ AttnPlan plan_verify_attn(const sva_batch* batch, const sva_paged_kv* kv, int Hq
 template <typename KV, int D>
 static hipError_t attn_launch(const AttnParams& p, bool mfma, hipStream_t st) {
   if constexpr (sizeof(KV) == 4) {
-    hipLaunchKernelGGL((verify_attn_kernel<KV, D, false>), dim3(p.W), dim3(kAttnThreads), 0, st, p);
+    hipLaunchKernelGGL((verify_attn_kernel<KV, D, false>), dim3(p.W),
+                       dim3(AttnLds<KV, D, false>::NT), 0, st, p);
   } else if (mfma) {
-    hipLaunchKernelGGL((verify_attn_kernel<KV, D, true>), dim3(p.W), dim3(kAttnThreads), 0, st, p);
+    hipLaunchKernelGGL((verify_attn_kernel<KV, D, true>), dim3(p.W),
+                       dim3(AttnLds<KV, D, true>::NT), 0, st, p);
   } else {
-    hipLaunchKernelGGL((verify_attn_kernel<KV, D, false>), dim3(p.W), dim3(kAttnThreads), 0, st, p);
+    hipLaunchKernelGGL((verify_attn_kernel<KV, D, false>), dim3(p.W),
+                       dim3(AttnLds<KV, D, false>::NT), 0, st, p);
   }
   return hipGetLastError();
 }
