@@ -161,12 +161,17 @@ __device__ __forceinline__ void st_dev(float* a, float v) {
 __device__ __forceinline__ float ld_dev(const float* a) {
   return __hip_atomic_load(const_cast<float*>(a), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ void st_dev4(float* a, f32x4 v) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) st_dev(a + i, v[i]);
+// 16-byte variants through a buffer resource over one partial slot: the same
+// sc1 (device-coherent) policy in one instruction instead of four.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t slot_rsrc(float* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(base, 0, bytes, 0x00020000);
 }
-__device__ __forceinline__ f32x4 ld_dev4(const float* a) {
-  return f32x4{ld_dev(a), ld_dev(a + 1), ld_dev(a + 2), ld_dev(a + 3)};
+constexpr int kCpolSc1 = 16;
+__device__ __forceinline__ void st_dev4(__amdgpu_buffer_rsrc_t r, int byte_off, f32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, byte_off, 0, kCpolSc1);
+}
+__device__ __forceinline__ f32x4 ld_dev4(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, kCpolSc1);
 }
 
 __device__ __forceinline__ void store_out4(const AttnParams& p, int64_t elem, f32x4 v) {
@@ -226,13 +231,15 @@ struct Geo {
 __device__ __forceinline__ uint32_t lds_addr(const void* l) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((AS3 const void*)l));
 }
-__device__ __forceinline__ void dma16(const void* g, void* l) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt"
-               ::"v"(g), "s"(lds_addr(l)) : "memory", "m0");
+// The global address is a wave-uniform base in SGPRs plus a 32-bit per-lane
+// offset (the saddr form), so issuing a page costs no 64-bit vector adds.
+__device__ __forceinline__ void dma16(const void* base, uint32_t off, void* l) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
+               ::"v"(off), "s"(base), "s"(lds_addr(l)) : "memory", "m0");
 }
-__device__ __forceinline__ void dma4(const void* g, void* l) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off nt"
-               ::"v"(g), "s"(lds_addr(l)) : "memory", "m0");
+__device__ __forceinline__ void dma4(const void* base, uint32_t off, void* l) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1 nt"
+               ::"v"(off), "s"(base), "s"(lds_addr(l)) : "memory", "m0");
 }
 
 // Page `pid` of kv head g -> ring slot (K page, V page, INT8 scales).
@@ -247,14 +254,14 @@ __device__ __forceinline__ void dma_page(const AttnParams& p, int pid, int g, ch
   for (int e = 0; e < Gm::DMA; ++e) {
     const int phys = kWave * e + lane;
     const int rho = phys / Gm::CPR, phi = phys % Gm::CPR;
-    dma16(kb + rho * Gm::RB + (phi ^ Gm::swz_k(rho)) * 16, slot + 1024 * e);
-    dma16(vb + rho * Gm::RB + (phi ^ Gm::swz_v(rho)) * 16, slot + Gm::PAGE + 1024 * e);
+    dma16(kb, uint32_t(rho * Gm::RB + (phi ^ Gm::swz_k(rho)) * 16), slot + 1024 * e);
+    dma16(vb, uint32_t(rho * Gm::RB + (phi ^ Gm::swz_v(rho)) * 16), slot + Gm::PAGE + 1024 * e);
   }
   if constexpr (Gm::ES == 1) {
     const int64_t so = (int64_t(pid) * p.Hkv + g) * kPage;
     if (lane < 8) {
-      dma4(reinterpret_cast<const char*>(p.k_scale + so) + 4 * lane, slot + 2 * Gm::PAGE);
-      dma4(reinterpret_cast<const char*>(p.v_scale + so) + 4 * lane, slot + 2 * Gm::PAGE + 32);
+      dma4(p.k_scale + so, uint32_t(4 * lane), slot + 2 * Gm::PAGE);
+      dma4(p.v_scale + so, uint32_t(4 * lane), slot + 2 * Gm::PAGE + 32);
     }
   }
 }
@@ -290,6 +297,45 @@ __device__ __forceinline__ void issue_step(const AttnParams& p, const Seg& sg, c
   dma_page<KV, D>(p, idb, sg.g, slots + Gm::SLOT);
 }
 
+// Steps of a step type that separates its LDS reads (load) from its arithmetic
+// (compute).  Wave w takes units (pairs of pages) w, w + NW, w + 2 NW, ... of
+// the segment -- a fixed assignment, so results are reproducible bit for bit.
+// q[0 .. S-1] are the units this wave has in flight, oldest first (-1: none);
+// q[0] is processed.  Once the step's reads have landed, its slot is free and
+// the copy of unit q[0] + NW * S into it is issued before the softmax and P.V
+// work, so it has that work's time to arrive.  EDGE = false runs while q[0] is
+// at most ulim (steps that need no masks) and EDGE = true runs the rest.
+template <typename KV, int D, int NW, bool EDGE, class Step, int S>
+__device__ __forceinline__ void unit_steps(const AttnParams& p, const Seg& sg, char* ring, Step& st,
+                                           int npair, int ulim, int (&q)[S], int& s) {
+  using Gm = Geo<KV, D, NW>;
+  constexpr int P2 = 2 * Gm::P;
+  while (q[0] >= 0 && (EDGE || q[0] <= ulim)) {
+    // The unit for the slot this step frees: its page ids are loaded first,
+    // while the step's LDS reads are in flight.
+    const int un = q[0] + NW * S < npair ? q[0] + NW * S : -1;
+    const int an = min(sg.pa + 2 * max(un, 0), sg.pe - 1);
+    const int ida = page_id(p, sg.b, an), idb = page_id(p, sg.b, min(an + 1, sg.pe - 1));
+    int pending = 0;
+#pragma unroll
+    for (int i = 1; i < S; ++i) pending += q[i] >= 0;
+    wait_steps<P2, S>(pending);
+    char* slots = ring + (s % S) * 2 * Gm::SLOT;
+    const int a = sg.pa + 2 * q[0];
+    st.load(slots, slots + Gm::SLOT);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // LDS reads and page ids
+    if (un >= 0) {
+      dma_page<KV, D>(p, ida, sg.g, slots);
+      dma_page<KV, D>(p, idb, sg.g, slots + Gm::SLOT);
+    }
+    st.template compute<EDGE>(a, a + 1 < sg.pe);
+#pragma unroll
+    for (int i = 0; i + 1 < S; ++i) q[i] = q[i + 1];
+    q[S - 1] = un;
+    ++s;
+  }
+}
+
 // Streams this wave's pages of the segment through its ring and calls
 // st.step(p, slot of page a, slot of page a+1, a, page a+1 exists) for each
 // pair of consecutive pages (a = pa + 2u, u = wave, wave + NW, ...).
@@ -300,17 +346,34 @@ __device__ __forceinline__ void run_pages(const AttnParams& p, const Seg& sg, ch
   constexpr int S = Gm::S, P2 = 2 * Gm::P;
   const int wave = wave_id();
   const int npair = (sg.pe - sg.pa + 1) >> 1;
-  const int n = npair > wave ? (npair - wave + NW - 1) / NW : 0;
-  const int pro = n < S ? n : S;
-  for (int s = 0; s < pro; ++s) issue_step<KV, D, NW>(p, sg, ring, wave, s);
-  st.ready();
-  for (int s = 0; s < n; ++s) {
-    wait_steps<P2, S>(min(S - 1, n - 1 - s));
-    const char* slots = ring + (s % S) * 2 * Gm::SLOT;
-    const int a = sg.pa + 2 * (wave + NW * s);
-    st.step(p, slots, slots + Gm::SLOT, a, a + 1 < sg.pe);
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // this step's LDS reads are done
-    if (s + S < n) issue_step<KV, D, NW>(p, sg, ring, wave, s + S);
+  if constexpr (Step::kSplit) {
+    int q[S];
+#pragma unroll
+    for (int i = 0; i < S; ++i) {
+      q[i] = wave + NW * i < npair ? wave + NW * i : -1;
+      if (q[i] >= 0) issue_step<KV, D, NW>(p, sg, ring, wave, i);
+    }
+    st.ready();
+    // units whose two pages lie inside the committed context (and inside the
+    // segment) need no masks
+    const int amax = min(sg.S / kPage, sg.pe) - 2;      // last such first page
+    const int ulim = amax >= sg.pa ? (amax - sg.pa) >> 1 : -1;
+    int s = 0;
+    unit_steps<KV, D, NW, false>(p, sg, ring, st, npair, ulim, q, s);
+    unit_steps<KV, D, NW, true>(p, sg, ring, st, npair, ulim, q, s);
+  } else {
+    const int n = npair > wave ? (npair - wave + NW - 1) / NW : 0;
+    const int pro = n < S ? n : S;
+    for (int s = 0; s < pro; ++s) issue_step<KV, D, NW>(p, sg, ring, wave, s);
+    st.ready();
+    for (int s = 0; s < n; ++s) {
+      wait_steps<P2, S>(min(S - 1, n - 1 - s));
+      const char* slots = ring + (s % S) * 2 * Gm::SLOT;
+      const int a = sg.pa + 2 * (wave + NW * s);
+      st.step(p, slots, slots + Gm::SLOT, a, a + 1 < sg.pe);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // this step's LDS reads are done
+      if (s + S < n) issue_step<KV, D, NW>(p, sg, ring, wave, s + S);
+    }
   }
 }
 
@@ -385,6 +448,7 @@ struct ValuStep {
   static constexpr int HALF = D / 2;                  // d values per lane in QK
   static constexpr int QS = F32 ? HALF + 4 : HALF / 2 + 4;
   static constexpr int CPL = D / 64;                  // output columns per lane
+  static constexpr bool kSplit = false;               // LDS reads run through the whole step
 
   const uint32_t* qs;
   char* ps;                                           // [RV][32] probabilities (f32 or bf16)
@@ -684,6 +748,16 @@ __device__ __forceinline__ bf16x8 load_q8_bf16(const AttnParams& p, int64_t elem
   return __builtin_bit_cast(bf16x8, w);
 }
 
+// 8 bf16 values (as packed words) -> fp16, round to nearest even.
+__device__ __forceinline__ f16x8 bf16x8_to_f16(u32x4 w) {
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    r[i] = uint32_t(f32_to_f16_bits(__uint_as_float(w[i] << 16))) |
+           (uint32_t(f32_to_f16_bits(__uint_as_float(w[i] & 0xffff0000u))) << 16);
+  return __builtin_bit_cast(f16x8, r);
+}
+
 // 8 consecutive Q values as fp16 (the INT8 path's operand type; bf16 and fp32
 // Q round to nearest even).
 __device__ __forceinline__ f16x8 load_q8_f16(const AttnParams& p, int64_t elem) {
@@ -747,6 +821,9 @@ struct MfmaStep {
   static constexpr int NDB = D / 16;      // 16-column blocks of d (O^T)
   static constexpr float kLazy = 8.f;
   static constexpr float kCodeBias = 1152.f;
+  static constexpr bool kSplit = true;
+  // V^T operand as read from LDS: bf16 -- the operand itself; INT8 -- 8 codes
+  using VRaw = typename std::conditional<I8, i32x2, bf16x8>::type;
 
   Op8 qB[NRB][KS];                        // row 16 rb + l16, d 32c + 8ks .. +8
   f32x4 acc[NRB][NDB];                    // O^T: d 16 db + 4c + i, row 16 rb + l16
@@ -756,7 +833,12 @@ struct MfmaStep {
   int lim[NRB];
   int valid_end;
   int lane, l16, c;
+  bool qbf16;                             // INT8 with bf16 Q: qB holds bf16 until ready()
   float scale_log2;
+  // carried from load() to compute()
+  f32x4 s[2][NRB];                        // S^T of both pages (unscaled)
+  VRaw vr[NDB];                           // V^T operands (INT8: codes)
+  u32x2 kw[2], vw[2];                     // INT8: K and V scales of lane's 4 tokens
 
   static __device__ __forceinline__ f32x4 mfma32(Op8 a, Op8 b, f32x4 acc) {
     if constexpr (I8) return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc, 0, 0, 0);
@@ -773,35 +855,29 @@ struct MfmaStep {
     l16 = lane & 15;
     c = lane >> 4;
     valid_end = sg.S + sg.k;
+    // bf16 Q is only loaded here (raw words); work that needs the values waits
+    // for ready(), after the first page copies are issued.
+    qbf16 = I8 && !p.q_f32;
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
       const int r = r0 + 16 * rb + l16;
       lim[rb] = -1;
-      float qs = 0.f;
       if (r < sg.R) {
         lim[rb] = sg.S + r / p.G;
         const int64_t qe = out_row(p, sg, r) * D + c * (D / 4);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          if constexpr (I8) {
-            qB[rb][ks] = load_q8_f16(p, qe + 8 * ks);
+          if (p.q_f32) {
+            if constexpr (I8) qB[rb][ks] = load_q8_f16(p, qe + 8 * ks);
+            else qB[rb][ks] = load_q8_bf16(p, qe + 8 * ks);
           } else {
-            qB[rb][ks] = load_q8_bf16(p, qe + 8 * ks);
+            qB[rb][ks] = __builtin_bit_cast(
+                Op8, *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(p.q) + qe + 8 * ks));
           }
         }
       } else {
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) qB[rb][ks] = __builtin_bit_cast(Op8, u32x4{0, 0, 0, 0});
-      }
-      if constexpr (I8) {
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const u32x4 w = __builtin_bit_cast(u32x4, qB[rb][ks]);
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            qs += f16_bits_to_f32(uint16_t(w[i])) + f16_bits_to_f32(uint16_t(w[i] >> 16));
-        }
-        s0[rb] = -kCodeBias * xrow32_sum(xrow16_sum(qs));
       }
       m[rb] = kNegBig;
       l[rb] = 0.f;
@@ -826,7 +902,7 @@ struct MfmaStep {
 
   // A operand of O^T += V^T P^T for d columns 16db .. 16db+15: lane (l16, c)
   // receives V[token 4c + e%4 of page e/4][16 db + l16], e = 0..7.
-  __device__ __forceinline__ Op8 v_operand(const char* sa, const char* sb, int db) const {
+  __device__ __forceinline__ VRaw v_raw(const char* sa, const char* sb, int db) const {
     if constexpr (I8) {
       // ds_read_b64_tr_b8: lane j of a 16-lane group receives byte e from the
       // 8-byte block addressed by lane 2e + j/8, at column j%8.  Lane 2e + h
@@ -835,8 +911,7 @@ struct MfmaStep {
       const int rho = 4 * c + (e & 3);
       const char* src = (e < 4 ? sa : sb) + Gm::PAGE + rho * Gm::RB +
                         (db ^ Gm::swz_v(rho)) * 16 + 8 * h;
-      const i32x2 w = __builtin_amdgcn_ds_read_tr8_b64_v2i32((AS3 i32x2*)src);
-      return codes8_to_f16(uint32_t(w[0]), uint32_t(w[1]));
+      return __builtin_amdgcn_ds_read_tr8_b64_v2i32((AS3 i32x2*)src);
     } else {
       // ds_read_b64_tr_b16: lane j of a 16-lane group receives element e from
       // the 8-byte block addressed by lane 4e + j/4, at column j%4.  Lane 4e + q
@@ -847,19 +922,22 @@ struct MfmaStep {
                       8 * (q & 1);
       const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((AS3 bf16x4*)(sa + off));
       const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((AS3 bf16x4*)(sb + off));
-      const u32x2 a = __builtin_bit_cast(u32x2, lo), b = __builtin_bit_cast(u32x2, hi);
-      return __builtin_bit_cast(bf16x8, u32x4{a[0], a[1], b[0], b[1]});
+      const u32x2 x = __builtin_bit_cast(u32x2, lo), y = __builtin_bit_cast(u32x2, hi);
+      return __builtin_bit_cast(bf16x8, u32x4{x[0], x[1], y[0], y[1]});
     }
   }
+  static __device__ __forceinline__ Op8 v_operand(VRaw r) {
+    if constexpr (I8) return codes8_to_f16(uint32_t(r[0]), uint32_t(r[1]));
+    else return r;
+  }
 
-  __device__ __forceinline__ void step(const AttnParams&, const char* sa, const char* sb, int a,
-                                       bool second) {
-    // Both slots are always multiplied: without a second page, slot B holds a
-    // copy of page A (finite data) whose scores are masked to -inf below.  A
-    // branch around these products would put a read of their accumulators right
-    // after a taken jump, where this compiler omits the MFMA result wait states.
-    const int npg = second ? 2 : 1;
-    f32x4 s[2][NRB];
+  // Every LDS read of a step: K operands (fed straight into the S^T MFMAs),
+  // the V^T operands and the INT8 scales.  Both slots are always multiplied:
+  // without a second page, slot B holds a copy of page A (finite data) whose
+  // scores are masked to -inf later.  A branch around these products would put
+  // a read of their accumulators right after a taken jump, where this compiler
+  // omits the MFMA result wait states.
+  __device__ __forceinline__ void load(const char* sa, const char* sb) {
 #pragma unroll
     for (int pg = 0; pg < 2; ++pg) {
 #pragma unroll
@@ -875,29 +953,63 @@ struct MfmaStep {
         for (int rb = 0; rb < NRB; ++rb) s[pg][rb] = mfma32(ka, qB[rb][ks], s[pg][rb]);
       }
     }
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) vr[db] = v_raw(sa, sb, db);
+    if constexpr (I8) {
+#pragma unroll
+      for (int pg = 0; pg < 2; ++pg) {
+        const char* sc = (pg ? sb : sa) + 2 * Gm::PAGE;
+        kw[pg] = ld64(sc + 8 * c);
+        vw[pg] = ld64(sc + 32 + 8 * c);
+      }
+    }
+  }
+
+  // Softmax and P.V of the step over pages a, a+1.  EDGE = false: all 32
+  // tokens lie inside the committed context, so every query row sees them and
+  // none is a garbage row -- no masks.
+  template <bool EDGE>
+  __device__ __forceinline__ void compute(int a, bool second) {
+    // The values the rest depends on pass through an empty asm here, so none
+    // of this work is hoisted above the copy issued just before it.
+#pragma unroll
+    for (int pg = 0; pg < 2; ++pg) {
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb) asm volatile("" : "+v"(s[pg][rb]));
+    }
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) asm volatile("" : "+v"(vr[db]));
+    if constexpr (I8) {
+#pragma unroll
+      for (int pg = 0; pg < 2; ++pg) asm volatile("" : "+v"(kw[pg]), "+v"(vw[pg]));
+    }
+    softmax_pv<EDGE>(a, second);
+  }
+
+  template <bool EDGE>
+  __device__ __forceinline__ void softmax_pv(int a, bool second) {
+    const int npg = second ? 2 : 1;
     // per-token factors: score scale (times the K scale) and V scale
     float kf[2][4], vf[2][4];
 #pragma unroll
     for (int pg = 0; pg < 2; ++pg) {
       if constexpr (I8) {
-        const char* sc = (pg ? sb : sa) + 2 * Gm::PAGE;
-        const u32x2 kw = ld64(sc + 8 * c), vw = ld64(sc + 32 + 8 * c);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int pos = (a + pg) * kPage + 4 * c + i;
-          kf[pg][i] = f16_bits_to_f32(uint16_t(kw[i / 2] >> (16 * (i & 1)))) * scale_log2;
-          vf[pg][i] = (pos < valid_end) ? f16_bits_to_f32(uint16_t(vw[i / 2] >> (16 * (i & 1)))) : 0.f;
+          kf[pg][i] = f16_bits_to_f32(uint16_t(kw[pg][i / 2] >> (16 * (i & 1)))) * scale_log2;
+          const float sv = f16_bits_to_f32(uint16_t(vw[pg][i / 2] >> (16 * (i & 1))));
+          vf[pg][i] = (!EDGE || pos < valid_end) ? sv : 0.f;
         }
       } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i) kf[pg][i] = scale_log2;
       }
     }
-    // V^T operands, loaded ahead of the softmax
     Op8 va[NDB];
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) va[db] = v_operand(sa, sb, db);
-    if constexpr (!I8) {
+    for (int db = 0; db < NDB; ++db) va[db] = v_operand(vr[db]);
+    if constexpr (!I8 && EDGE) {
       if ((a + 2) * kPage > valid_end) {          // garbage rows (may be NaN) read as zero
         u32x4 keep;
 #pragma unroll
@@ -924,7 +1036,7 @@ struct MfmaStep {
         for (int i = 0; i < 4; ++i) {
           const int pos = (a + pg) * kPage + 4 * c + i;
           const float v = s[pg][rb][i] * kf[pg][i];
-          x[rb][pg][i] = (pg < npg && pos <= lim[rb]) ? v : -INFINITY;
+          x[rb][pg][i] = (!EDGE || (pg < npg && pos <= lim[rb])) ? v : -INFINITY;
           t = fmaxf(t, x[rb][pg][i]);
         }
       }
@@ -983,9 +1095,25 @@ struct MfmaStep {
   // Called once the first pages are in flight: the query registers are read
   // here, so the compiler's wait for their loads lands outside the page loop
   // (one wait that also covers the first DMAs) instead of inside it.
-  __device__ __forceinline__ void ready() const {
+  // INT8: fp16 operands from bf16 Q, and the S^T start value -1152 * sum(q).
+  __device__ __forceinline__ void ready() {
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
+      if constexpr (I8) {
+        if (qbf16) {
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) qB[rb][ks] = bf16x8_to_f16(__builtin_bit_cast(u32x4, qB[rb][ks]));
+        }
+        float qs = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const u32x4 w = __builtin_bit_cast(u32x4, qB[rb][ks]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            qs += f16_bits_to_f32(uint16_t(w[i])) + f16_bits_to_f32(uint16_t(w[i] >> 16));
+        }
+        s0[rb] = -kCodeBias * xrow32_sum(xrow16_sum(qs));
+      }
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(qB[rb][ks]));
     }
@@ -1052,8 +1180,9 @@ struct MfmaStep {
         }
       } else {
         float* sb = slot_base<D>(p, sg.slot);
+        const auto rs = slot_rsrc(sb, p.slot_rows * D * 4);
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) st_dev4(sb + int64_t(r) * D + 16 * db + 4 * c, acc[rb][db]);
+        for (int db = 0; db < NDB; ++db) st_dev4(rs, (r * D + 16 * db + 4 * c) * 4, acc[rb][db]);
         if (c == 0) {
           st_dev(sb + int64_t(p.slot_rows) * D + r, m[rb]);
           st_dev(sb + int64_t(p.slot_rows) * (D + 1) + r, l[rb]);
@@ -1129,7 +1258,8 @@ __device__ __forceinline__ void merge_pair(const AttnParams& p, const Seg& sg, i
       for (int h = 0; h < 2; ++h) {
         const int w = w0 + h;
         use[h] = w <= wl && range_start(w + 1, N, p.W) > range_start(w, N, p.W);   // non-empty
-        const float* sb = slot_base<D>(p, slot_of(use[h] ? w : w0, pb, N, p.W));
+        float* sb = slot_base<D>(p, slot_of(use[h] ? w : w0, pb, N, p.W));
+        const auto rs = slot_rsrc(sb, p.slot_rows * D * 4);
 #pragma unroll
         for (int u = 0; u < kItems; ++u) {
           const int it = base + u * NT + threadIdx.x;
@@ -1137,7 +1267,7 @@ __device__ __forceinline__ void merge_pair(const AttnParams& p, const Seg& sg, i
           if (use[h]) {
             ms[h][u] = ld_dev(sb + int64_t(p.slot_rows) * D + r);
             ls[h][u] = ld_dev(sb + int64_t(p.slot_rows) * (D + 1) + r);
-            os[h][u] = ld_dev4(sb + int64_t(r) * D + 4 * d4);
+            os[h][u] = ld_dev4(rs, (r * D + 4 * d4) * 4);
           }
         }
       }
