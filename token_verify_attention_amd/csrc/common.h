@@ -37,6 +37,22 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+// Two floats as packed fp16, round to nearest even (v_cvt_pk_f16_f32).
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
+}
+// Element-wise product of two packed fp16 pairs (v_pk_mul_f16).
+__device__ __forceinline__ uint32_t mul_f16x2(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, a) * __builtin_bit_cast(f16x2_t, b));
+}
+// Half `hi` of a packed fp16 pair, widened to fp32 (folds into v_fma_mix_f32).
+__device__ __forceinline__ float f16x2_half(uint32_t w, int hi) {
+  return float(__builtin_bit_cast(f16x2_t, w)[hi]);
+}
+
 __device__ __forceinline__ float f16_bits_to_f32(uint16_t h) {
   return float(__builtin_bit_cast(_Float16, h));
 }

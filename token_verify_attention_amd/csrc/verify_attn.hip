@@ -748,19 +748,19 @@ __device__ __forceinline__ bf16x8 load_q8_bf16(const AttnParams& p, int64_t elem
   return __builtin_bit_cast(bf16x8, w);
 }
 
-// 8 bf16 values (as packed words) -> fp16, round to nearest even.
-__device__ __forceinline__ f16x8 bf16x8_to_f16(u32x4 w) {
+// 8 bf16 values (as packed words) times `mul` -> fp16, one rounding to nearest
+// even from the fp32 product.
+__device__ __forceinline__ f16x8 bf16x8_to_f16(u32x4 w, float mul) {
   u32x4 r;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
-    r[i] = uint32_t(f32_to_f16_bits(__uint_as_float(w[i] << 16))) |
-           (uint32_t(f32_to_f16_bits(__uint_as_float(w[i] & 0xffff0000u))) << 16);
+    r[i] = pack_f16x2(__uint_as_float(w[i] << 16) * mul, __uint_as_float(w[i] & 0xffff0000u) * mul);
   return __builtin_bit_cast(f16x8, r);
 }
 
-// 8 consecutive Q values as fp16 (the INT8 path's operand type; bf16 and fp32
-// Q round to nearest even).
-__device__ __forceinline__ f16x8 load_q8_f16(const AttnParams& p, int64_t elem) {
+// 8 consecutive Q values times `mul` as fp16 (the INT8 path's operand type;
+// one rounding to nearest even from the fp32 product).
+__device__ __forceinline__ f16x8 load_q8_f16(const AttnParams& p, int64_t elem, float mul) {
   float v[8];
   if (p.q_f32) {
     const f32x4* s = reinterpret_cast<const f32x4*>(static_cast<const float*>(p.q) + elem);
@@ -780,8 +780,7 @@ __device__ __forceinline__ f16x8 load_q8_f16(const AttnParams& p, int64_t elem) 
   }
   u32x4 r;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    r[i] = uint32_t(f32_to_f16_bits(v[2 * i])) | (uint32_t(f32_to_f16_bits(v[2 * i + 1])) << 16);
+  for (int i = 0; i < 4; ++i) r[i] = pack_f16x2(v[2 * i] * mul, v[2 * i + 1] * mul);
   return __builtin_bit_cast(f16x8, r);
 }
 
@@ -811,7 +810,11 @@ __device__ __forceinline__ f16x8 codes8_to_f16(uint32_t w0, uint32_t w1) {
 //    all-ones A operand, so it sums exactly the rounded weights P.V uses.
 //  * INT8 caches run fp16 MFMAs on codes offset to 1152 + code (exact); the
 //    offset leaves S through the accumulator's start value -1152 * sum(q) and
-//    leaves O through the MFMA-computed sum of the fp16 weights.
+//    leaves O through the MFMA-computed sum of the fp16 weights.  Q is
+//    converted once, pre-multiplied by softmax_scale * log2 e, so the per-token
+//    K scale is the only factor left on each score; the V scale multiplies the
+//    fp16 weight pairs, and the denominator is a second all-ones MFMA over the
+//    unscaled weights.
 template <typename KV, int D, int NRB>
 struct MfmaStep {
   using Gm = Geo<KV, D, kWavesValu>;      // page geometry only
@@ -828,6 +831,7 @@ struct MfmaStep {
   Op8 qB[NRB][KS];                        // row 16 rb + l16, d 32c + 8ks .. +8
   f32x4 acc[NRB][NDB];                    // O^T: d 16 db + 4c + i, row 16 rb + l16
   f32x4 sacc[NRB];                        // all-ones MFMA: sum of the weights fed to P.V
+  f32x4 lsum[NRB];                        // INT8: all-ones MFMA over the unscaled weights
   float m[NRB], l[NRB];
   float s0[NRB];                          // INT8: start value of the S^T accumulator
   int lim[NRB];
@@ -868,7 +872,7 @@ struct MfmaStep {
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
           if (p.q_f32) {
-            if constexpr (I8) qB[rb][ks] = load_q8_f16(p, qe + 8 * ks);
+            if constexpr (I8) qB[rb][ks] = load_q8_f16(p, qe + 8 * ks, scale_log2);
             else qB[rb][ks] = load_q8_bf16(p, qe + 8 * ks);
           } else {
             qB[rb][ks] = __builtin_bit_cast(
@@ -882,6 +886,7 @@ struct MfmaStep {
       m[rb] = kNegBig;
       l[rb] = 0.f;
       sacc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      lsum[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int db = 0; db < NDB; ++db) acc[rb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
@@ -983,33 +988,100 @@ struct MfmaStep {
 #pragma unroll
       for (int pg = 0; pg < 2; ++pg) asm volatile("" : "+v"(kw[pg]), "+v"(vw[pg]));
     }
-    softmax_pv<EDGE>(a, second);
+    if constexpr (I8) softmax_pv_i8<EDGE>(a, second);
+    else softmax_pv<EDGE>(a, second);
   }
 
+  // INT8 caches.  Q carries softmax_scale * log2 e, so a token's score in log2
+  // units is s * k_scale, and y = s * k_scale - m is one v_fma_mix_f32 with the
+  // fp16 scale as an operand.  Weights: e = 2^y packed to fp16 (the unscaled
+  // weights, whose all-ones MFMA gives the denominator), then times the fp16
+  // V scale pair (the P operand, whose all-ones MFMA gives the sum that
+  // removes the code offset).
   template <bool EDGE>
-  __device__ __forceinline__ void softmax_pv(int a, bool second) {
+  __device__ __forceinline__ void softmax_pv_i8(int a, bool second) {
     const int npg = second ? 2 : 1;
-    // per-token factors: score scale (times the K scale) and V scale
-    float kf[2][4], vf[2][4];
-#pragma unroll
-    for (int pg = 0; pg < 2; ++pg) {
-      if constexpr (I8) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int pos = (a + pg) * kPage + 4 * c + i;
-          kf[pg][i] = f16_bits_to_f32(uint16_t(kw[pg][i / 2] >> (16 * (i & 1)))) * scale_log2;
-          const float sv = f16_bits_to_f32(uint16_t(vw[pg][i / 2] >> (16 * (i & 1))));
-          vf[pg][i] = (!EDGE || pos < valid_end) ? sv : 0.f;
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) kf[pg][i] = scale_log2;
-      }
-    }
     Op8 va[NDB];
 #pragma unroll
     for (int db = 0; db < NDB; ++db) va[db] = v_operand(vr[db]);
-    if constexpr (!I8 && EDGE) {
+    // V scales of the lane's tokens as fp16 pairs, in k-slot order
+    uint32_t vs[4] = {vw[0][0], vw[0][1], vw[1][0], vw[1][1]};
+    if constexpr (EDGE) {
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {        // garbage rows (scale may be NaN) weigh zero
+        const int p0 = (a + (h >> 1)) * kPage + 4 * c + 2 * (h & 1);
+        vs[h] &= (p0 < valid_end ? 0x0000ffffu : 0u) | (p0 + 1 < valid_end ? 0xffff0000u : 0u);
+      }
+    }
+    float y[NRB][8];
+    bool move = false;
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+      float t = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int pg = j >> 2, i = j & 3;
+        const int pos = (a + pg) * kPage + 4 * c + i;
+        const float v = fmaf(s[pg][rb][i], f16x2_half(kw[pg][i >> 1], i & 1), -m[rb]);
+        y[rb][j] = (!EDGE || (pg < npg && pos <= lim[rb])) ? v : -INFINITY;
+        t = fmaxf(t, y[rb][j]);
+      }
+      move |= xrow32_max(xrow16_max(t)) > kLazy;
+    }
+    if (__ballot(move)) {          // some row's reference moves: exact maxima of this step
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb) {
+        float x[8], t = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int pg = j >> 2, i = j & 3;
+          const int pos = (a + pg) * kPage + 4 * c + i;
+          const float v = s[pg][rb][i] * f16x2_half(kw[pg][i >> 1], i & 1);
+          x[j] = (!EDGE || (pg < npg && pos <= lim[rb])) ? v : -INFINITY;
+          t = fmaxf(t, x[j]);
+        }
+        const float xm = xrow32_max(xrow16_max(t));
+        const float mn = (xm > m[rb] + kLazy) ? xm : m[rb];
+        const float alpha = __builtin_amdgcn_exp2f(m[rb] - mn);
+        m[rb] = mn;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          sacc[rb][i] *= alpha;
+          lsum[rb][i] *= alpha;
+        }
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[rb][db][i] *= alpha;
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) y[rb][j] = x[j] - mn;
+      }
+    }
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+      u32x4 pe, pw;
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        pe[h] = pack_f16x2(__builtin_amdgcn_exp2f(y[rb][2 * h]), __builtin_amdgcn_exp2f(y[rb][2 * h + 1]));
+        pw[h] = mul_f16x2(pe[h], vs[h]);
+      }
+      const Op8 pb = __builtin_bit_cast(Op8, pw);
+      lsum[rb] = mfma32(ones(), __builtin_bit_cast(Op8, pe), lsum[rb]);
+      sacc[rb] = mfma32(ones(), pb, sacc[rb]);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) acc[rb][db] = mfma32(va[db], pb, acc[rb][db]);
+    }
+  }
+
+  // bf16 caches: scores times scale * log2 e, lazy maximum, bf16 weights.
+  template <bool EDGE>
+  __device__ __forceinline__ void softmax_pv(int a, bool second) {
+    const int npg = second ? 2 : 1;
+    Op8 va[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) va[db] = v_operand(vr[db]);
+    if constexpr (EDGE) {
       if ((a + 2) * kPage > valid_end) {          // garbage rows (may be NaN) read as zero
         u32x4 keep;
 #pragma unroll
@@ -1035,7 +1107,7 @@ struct MfmaStep {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int pos = (a + pg) * kPage + 4 * c + i;
-          const float v = s[pg][rb][i] * kf[pg][i];
+          const float v = s[pg][rb][i] * scale_log2;
           x[rb][pg][i] = (!EDGE || (pg < npg && pos <= lim[rb])) ? v : -INFINITY;
           t = fmaxf(t, x[rb][pg][i]);
         }
@@ -1049,7 +1121,6 @@ struct MfmaStep {
         const float mn = (mx[rb] > m[rb] + kLazy) ? mx[rb] : m[rb];
         const float alpha = __builtin_amdgcn_exp2f(m[rb] - mn);
         m[rb] = mn;
-        l[rb] *= alpha;
 #pragma unroll
         for (int i = 0; i < 4; ++i) sacc[rb][i] *= alpha;
 #pragma unroll
@@ -1061,31 +1132,12 @@ struct MfmaStep {
     }
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
-      float w[8];
-      float psum = 0.f;
-#pragma unroll
-      for (int pg = 0; pg < 2; ++pg) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float e = __builtin_amdgcn_exp2f(x[rb][pg][i] - m[rb]);
-          if constexpr (I8) {
-            psum += e;
-            w[4 * pg + i] = e * vf[pg][i];
-          } else {
-            w[4 * pg + i] = e;
-          }
-        }
-      }
       u32x4 pw;
 #pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        if constexpr (I8)
-          pw[h] = uint32_t(f32_to_f16_bits(w[2 * h])) | (uint32_t(f32_to_f16_bits(w[2 * h + 1])) << 16);
-        else
-          pw[h] = pack_bf16x2(w[2 * h], w[2 * h + 1]);
-      }
+      for (int h = 0; h < 4; ++h)
+        pw[h] = pack_bf16x2(__builtin_amdgcn_exp2f(x[rb][h >> 1][2 * (h & 1)] - m[rb]),
+                            __builtin_amdgcn_exp2f(x[rb][h >> 1][2 * (h & 1) + 1] - m[rb]));
       const Op8 pb = __builtin_bit_cast(Op8, pw);
-      if constexpr (I8) l[rb] += psum;
       sacc[rb] = mfma32(ones(), pb, sacc[rb]);
 #pragma unroll
       for (int db = 0; db < NDB; ++db) acc[rb][db] = mfma32(va[db], pb, acc[rb][db]);
@@ -1095,14 +1147,16 @@ struct MfmaStep {
   // Called once the first pages are in flight: the query registers are read
   // here, so the compiler's wait for their loads lands outside the page loop
   // (one wait that also covers the first DMAs) instead of inside it.
-  // INT8: fp16 operands from bf16 Q, and the S^T start value -1152 * sum(q).
+  // INT8: fp16 operands from bf16 Q (times softmax_scale * log2 e), and the S^T
+  // start value -1152 * sum(q).
   __device__ __forceinline__ void ready() {
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
       if constexpr (I8) {
         if (qbf16) {
 #pragma unroll
-          for (int ks = 0; ks < KS; ++ks) qB[rb][ks] = bf16x8_to_f16(__builtin_bit_cast(u32x4, qB[rb][ks]));
+          for (int ks = 0; ks < KS; ++ks)
+            qB[rb][ks] = bf16x8_to_f16(__builtin_bit_cast(u32x4, qB[rb][ks]), scale_log2);
         }
         float qs = 0.f;
 #pragma unroll
@@ -1122,7 +1176,7 @@ struct MfmaStep {
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
       if constexpr (I8) {
-        l[rb] = xrow32_sum(xrow16_sum(l[rb]));
+        l[rb] = lsum[rb][0];
         const float off = kCodeBias * sacc[rb][0];             // remove 1152 * sum of weights
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
@@ -1146,46 +1200,47 @@ struct MfmaStep {
       slot[NRB * NDB * kWave * 4 + (NRB + rb) * kWave + lane] = l[rb];
     }
   }
-  __device__ __forceinline__ void combine(const float* slot) {
+  // Merge of the NW waves' states stored at mrg + w * SLOT_F (store()
+  // layout), spread over every thread of the workgroup: thread items are
+  // (row, 4 columns), rows varying fastest so that a wave's 16-byte LDS reads
+  // spread over all banks; each combines the NW partials in a fixed order and
+  // writes the normalised output rows, or the unnormalised partial (O, m, l)
+  // of a segment that is not the whole pair.
+  static __device__ __forceinline__ void merge_write(const AttnParams& p, const Seg& sg, int r0,
+                                                     const float* mrg, int nw) {
+    constexpr int D4 = D / 4;
+    constexpr int ITEMS = 16 * NRB * D4;
+    constexpr int MOFF = NRB * NDB * kWave * 4;
+    for (int it = threadIdx.x; it < ITEMS; it += nw * kWave) {
+      const int r = it % (16 * NRB), d4 = it / (16 * NRB);
+      const int rb = r >> 4, l16 = r & 15;
+      const int oidx = ((rb * NDB + (d4 >> 2)) * kWave + l16 + 16 * (d4 & 3)) * 4;
+      const int midx = MOFF + rb * kWave + l16;
+      float M = kNegBig;
+      for (int w = 0; w < nw; ++w) M = fmaxf(M, mrg[w * SLOT_F + midx]);
+      float L = 0.f;
+      f32x4 O = {0.f, 0.f, 0.f, 0.f};
+      for (int w = 0; w < nw; ++w) {
+        const float* sl = mrg + w * SLOT_F;
+        const float f = exp2f(sl[midx] - M);
+        L += f * sl[midx + NRB * kWave];
+        const f32x4 o = *reinterpret_cast<const f32x4*>(sl + oidx);
 #pragma unroll
-    for (int rb = 0; rb < NRB; ++rb) {
-      const float mo = slot[NRB * NDB * kWave * 4 + rb * kWave + lane];
-      const float lo = slot[NRB * NDB * kWave * 4 + (NRB + rb) * kWave + lane];
-      const float M = fmaxf(m[rb], mo);
-      const float fa = exp2f(m[rb] - M), fb = exp2f(mo - M);
-      l[rb] = fa * l[rb] + fb * lo;
-      m[rb] = M;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const f32x4 o = *reinterpret_cast<const f32x4*>(slot + ((rb * NDB + db) * kWave + lane) * 4);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[rb][db][i] = fa * acc[rb][db][i] + fb * o[i];
+        for (int i = 0; i < 4; ++i) O[i] += f * o[i];
       }
-    }
-  }
-  __device__ __forceinline__ void write(const AttnParams& p, const Seg& sg, int r0) const {
-#pragma unroll
-    for (int rb = 0; rb < NRB; ++rb) {
-      const int r = r0 + 16 * rb + l16;
-      if (r >= sg.R) continue;
+      const int row = r0 + r;
+      if (row >= sg.R) continue;                    // padding rows of the last block
       if (sg.full) {
-        const float inv = 1.f / l[rb];
-        const int64_t oe = out_row(p, sg, r) * D;
+        const float inv = 1.f / L;
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          f32x4 v = acc[rb][db];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) v[i] *= inv;
-          store_out4(p, oe + 16 * db + 4 * c, v);
-        }
+        for (int i = 0; i < 4; ++i) O[i] *= inv;
+        store_out4(p, out_row(p, sg, row) * D + 4 * d4, O);
       } else {
         float* sb = slot_base<D>(p, sg.slot);
-        const auto rs = slot_rsrc(sb, p.slot_rows * D * 4);
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) st_dev4(rs, (r * D + 16 * db + 4 * c) * 4, acc[rb][db]);
-        if (c == 0) {
-          st_dev(sb + int64_t(p.slot_rows) * D + r, m[rb]);
-          st_dev(sb + int64_t(p.slot_rows) * (D + 1) + r, l[rb]);
+        st_dev4(slot_rsrc(sb, p.slot_rows * D * 4), (row * D + 4 * d4) * 4, O);
+        if (d4 == 0) {
+          st_dev(sb + int64_t(p.slot_rows) * D + row, M);
+          st_dev(sb + int64_t(p.slot_rows) * (D + 1) + row, L);
         }
       }
     }
@@ -1193,8 +1248,10 @@ struct MfmaStep {
 };
 
 // One pass over the segment's pages for rows r0.. of the pair: stream, then
-// merge the NW waves pairwise through LDS (the ring is idle by then) and let
-// wave 0 write the output rows or the partial slot.
+// merge the NW waves through LDS (the ring is idle by then).  MFMA steps store
+// every wave's state at once and merge in one round spread over all threads;
+// VALU steps merge pairwise and wave 0 writes the output rows or the partial
+// slot.
 template <typename KV, int D, int NW, class St>
 __device__ __forceinline__ void pass(const AttnParams& p, const Seg& sg, int r0, St& st,
                                      char* ring_all) {
@@ -1204,15 +1261,22 @@ __device__ __forceinline__ void pass(const AttnParams& p, const Seg& sg, int r0,
   __syncthreads();                                    // every wave is off the ring
   float* mrg = reinterpret_cast<float*>(ring_all);
   constexpr int SLOT = St::SLOT_F;
-#pragma unroll
-  for (int half = NW / 2; half >= 1; half /= 2) {
-    if (wave >= half && wave < 2 * half) st.store(mrg + (wave - half) * SLOT);
+  if constexpr (St::kSplit) {                         // MFMA steps: one merge round
+    st.store(mrg + wave * SLOT);
     __syncthreads();
-    if (wave < half) st.combine(mrg + wave * SLOT);
+    St::merge_write(p, sg, r0, mrg, NW);
+    __syncthreads();
+  } else {
+#pragma unroll
+    for (int half = NW / 2; half >= 1; half /= 2) {
+      if (wave >= half && wave < 2 * half) st.store(mrg + (wave - half) * SLOT);
+      __syncthreads();
+      if (wave < half) st.combine(mrg + wave * SLOT);
+      __syncthreads();
+    }
+    if (wave == 0) st.write(p, sg, r0);
     __syncthreads();
   }
-  if (wave == 0) st.write(p, sg, r0);
-  __syncthreads();
 }
 
 // ============================================================================
@@ -1308,9 +1372,10 @@ struct AttnLds {
   static constexpr int NW = (MF && sizeof(KV) == 1) ? kWavesInt8 : kWavesValu;
   static constexpr int NT = NW * kWave;
   static constexpr int RING = NW * Geo<KV, D, NW>::RING;
-  // the wave merge reuses the ring: NW/2 slots of the largest step state
-  static constexpr int MERGE = (NW / 2) * 4 * (MF ? (2 * (D / 16) * kWave * 4 + 4 * kWave)
-                                                  : (kValuRows * D * 2 + 64));
+  // the wave merge reuses the ring: NW slots (MFMA) or NW/2 slots (VALU) of the
+  // largest step state
+  static constexpr int MERGE = MF ? NW * 4 * (2 * (D / 16) * kWave * 4 + 4 * kWave)
+                                  : (NW / 2) * 4 * (kValuRows * D * 2 + 64);
   static constexpr int RING_ALLOC = RING > MERGE ? RING : MERGE;
   // VALU passes stage their query rows and per-wave probabilities in LDS
   static constexpr int QS = MF ? 4 : kValuRows * 2 * (D / 2 + 4);   // dwords (fp32 layout, the larger)
