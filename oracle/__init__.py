@@ -26,19 +26,27 @@ What each function follows (pages cited by title and section):
   First Principles", section "Speculating to get sequence parallelism during
   decode": reject at the first disagreement, keep the target's token, and the
   last row gives the +1 bonus token (1 to n+1 tokens per pass).
+* ``ancestor_masks`` / ``accept_tree`` / ``commit_path`` and the
+  ``draft_mask`` argument of ``spec_verify_attn`` -- the same page, section
+  "Tree based verification": tree attention over each draft's lineage, the
+  longest branch the target agrees with, and the surviving branch made
+  contiguous in the cache.
 
 Pins (tests marked ``not gpu``): a torch float64 SDPA with an explicit mask and
 a pure-Python triple loop for attention; closed forms (constant V rows,
 identical keys, k=1 decode) and invariants (prefix invariance, page
 permutation, GQA = MHA on repeated KV); a brute-force exact-rational INT8
 quantiser, hand-derived tie cases and the round-trip bound; numpy.argmax and
-constructed tie / NaN / signed-zero rows for acceptance.  No function here is
+constructed tie / NaN / signed-zero rows for acceptance; for trees, a boolean
+transitive closure for the masks, torch SDPA with the tree mask, brute-force
+path enumeration and chain trees reducing to the causal case.  No function here is
 "parity unpinned".
 """
 from .attention import spec_verify_attn
 from .kv_quant import kv_quant_int8, dequant_int8, round_to_bf16
 from .kv_append import kv_append
 from .accept import argmax_rows, accept_prefix
+from .tree import ancestor_masks, accept_tree, commit_path
 
 __all__ = [
     "spec_verify_attn",
@@ -48,4 +56,7 @@ __all__ = [
     "kv_append",
     "argmax_rows",
     "accept_prefix",
+    "ancestor_masks",
+    "accept_tree",
+    "commit_path",
 ]

@@ -16,6 +16,12 @@ For every sequence b, query i, head h (kv head g = h // G, G = Hq / Hkv):
     w_p = exp(s_p - max s) / sum exp(s - max s)
     out_{i,h} = sum_p w_p V_p
 
+Tree-structured verification ("Decoding Speculative Decoding from First
+Principles", section "Tree based verification": tree attention relates a draft
+only to its own lineage) replaces the causal draft mask by a per-draft bitmask:
+with ``draft_mask`` given, draft i sees the committed rows 0 .. S_b-1 and the
+draft rows S_b + j (j < k_b) whose bit j is set in draft_mask[cu_q[b] + i].
+
 All arithmetic is float64.  float32 / bf16 inputs and int8 codes times fp16
 scales convert to float64 exactly, so the only rounding is the fp64 arithmetic
 itself.
@@ -31,7 +37,8 @@ def _dequant(pool, scale, pages, g, slots):
 
 
 def spec_verify_attn(q, k_pool, v_pool, block_table, ctx_lens, cu_q, softmax_scale,
-                     k_scale=None, v_scale=None, select=None, return_weights=False):
+                     k_scale=None, v_scale=None, select=None, return_weights=False,
+                     draft_mask=None):
     """Plain-definition verification attention.
 
     q            [T, Hq, d] float (float32 values, or bf16 values held in float32)
@@ -41,8 +48,9 @@ def spec_verify_attn(q, k_pool, v_pool, block_table, ctx_lens, cu_q, softmax_sca
     ctx_lens     [B] committed rows S_b (the k_b draft rows come after them)
     cu_q         [B+1] prefix sums of k_b
     select       optional iterable of (b, g) pairs; other rows stay NaN
+    draft_mask   optional [T] int bitmasks (tree attention; see module doc)
     Returns out [T, Hq, d] float64 (and, if asked, a dict mapping
-    (b, i, h) -> the weight vector over keys 0..S_b+i).
+    (b, i, h) -> the weight vector over the visible keys in position order).
     """
     q = np.asarray(q)
     T, Hq, d = q.shape
@@ -65,14 +73,19 @@ def spec_verify_attn(q, k_pool, v_pool, block_table, ctx_lens, cu_q, softmax_sca
         K = _dequant(k_pool, k_scale, pages, g, slots)   # [S+k, d]
         V = _dequant(v_pool, v_scale, pages, g, slots)
         for i in range(k):
-            n = S + i + 1                                  # keys 0 .. S+i
+            if draft_mask is None:
+                keys = np.arange(S + i + 1)                # keys 0 .. S+i
+            else:
+                m = int(draft_mask[q0 + i])
+                keys = np.concatenate([np.arange(S),
+                                       [S + j for j in range(k) if (m >> j) & 1]]).astype(np.int64)
             for j in range(G):
                 h = g * G + j
                 qv = q[q0 + i, h].astype(np.float64)
-                s = float(softmax_scale) * (K[:n] @ qv)
+                s = float(softmax_scale) * (K[keys] @ qv)
                 e = np.exp(s - s.max())
                 w = e / e.sum()
-                out[q0 + i, h] = w @ V[:n]
+                out[q0 + i, h] = w @ V[keys]
                 if weights is not None:
                     weights[(b, i, h)] = w
     if return_weights:
