@@ -3,7 +3,8 @@
 One step = one pass of the whole hot path over one synthetic batch:
   kv_append (the k new K/V rows of every sequence; INT8 caches quantise on
   write) -> spec_verify_attn -> accept_prefix (argmax over the vocabulary and
-  the longest accepted prefix).
+  the longest accepted prefix).  Token-tree workloads (--workload tree8b) run
+  kv_append -> tree_masks -> tree attention -> accept_tree -> kv_commit_path.
 Default workload: 7B-MHA shape, B=8, Hq=Hkv=32, d=128, S=2048, k=4, bf16 paged
 KV (16-token pages, random page permutation).  That shape names no vocabulary;
 acceptance runs over fp32 logits [B*(k+1), 128256] with drafts agreeing with
@@ -94,7 +95,12 @@ class Inputs:
     """One resident input set and the prepared calls of one step."""
 
     def __init__(self, tva, wl, w, seed_offset, dev):
-        self.case = case = wl.make_case(w, device=dev, seed_offset=seed_offset)
+        tree = w.name in wl.TREE_WORKLOADS
+        self.case = case = wl.make_case(w, device=dev, seed_offset=seed_offset, with_logits=not tree)
+        if tree:
+            case["parents"] = wl.make_tree(case["k_host"], device=dev, seed=w.ident + 97 * seed_offset)
+            case.update(wl.make_tree_logits(w, case["k_host"], case["parents"], device=dev,
+                                            seed_offset=seed_offset))
         self.batch = tva.Batch(case["ctx_lens"], case["cu_q"], total_q=case["T"],
                                max_q=case["max_q"], max_len=case["max_len"])
         if w.kv_dtype == "int8":
@@ -109,9 +115,34 @@ class Inputs:
         self.alen = torch.empty(B, dtype=torch.int32, device=dev)
         self.nxt = torch.empty(B, dtype=torch.int32, device=dev)
         self.append = tva.prepare_kv_append(self.batch, case["k_new"], case["v_new"], self.kv)
-        self.attn = tva.prepare_spec_verify_attn(self.batch, case["q"], self.kv, self.out)
-        self.accept = tva.prepare_accept_prefix(self.batch, case["logits"], case["draft_ids"],
-                                                self.ids, self.alen, self.nxt)
+        if tree:
+            self.masks = torch.empty(case["T"], dtype=torch.int32, device=dev)
+            self.path = torch.empty(case["T"], dtype=torch.int32, device=dev)
+            self.tree_masks = tva.prepare_tree_masks(self.batch, case["parents"], self.masks)
+            self.tree_masks()
+            self.attn = tva.prepare_spec_verify_attn(self.batch, case["q"], self.kv, self.out,
+                                                     draft_mask=self.masks)
+            acc = tva.prepare_accept_tree(self.batch, case["logits"], case["draft_ids"],
+                                          case["parents"], self.ids, self.alen, self.nxt,
+                                          self.path)
+            commit = tva.prepare_kv_commit_path(self.batch, self.alen, self.path, self.kv)
+
+            def accept(stream=None):
+                acc(stream)
+                commit(stream)
+            self.accept = accept
+            attn = self.attn
+            masks_call = self.tree_masks
+
+            def step_attn(stream=None):
+                masks_call(stream)
+                attn(stream)
+            self.step_attn = step_attn
+        else:
+            self.attn = tva.prepare_spec_verify_attn(self.batch, case["q"], self.kv, self.out)
+            self.accept = tva.prepare_accept_prefix(self.batch, case["logits"], case["draft_ids"],
+                                                    self.ids, self.alen, self.nxt)
+            self.step_attn = self.attn
 
 
 def copy_probe_gbps(dev, nbytes=1 << 30, reps=10):
@@ -138,8 +169,13 @@ def cpu_baseline(wl, w, dev, budget_s):
     import oracle
     from threadpoolctl import threadpool_limits
 
-    case = wl.make_case(w, device=dev, seed_offset=0)
+    tree = w.name in wl.TREE_WORKLOADS
+    case = wl.make_case(w, device=dev, seed_offset=0, with_logits=not tree)
     np_ = lambda t: (t.float() if t.dtype == torch.bfloat16 else t).cpu().numpy()
+    if tree:
+        case["parents"] = wl.make_tree(case["k_host"], device=dev, seed=w.ident)
+        case.update(wl.make_tree_logits(w, case["k_host"], case["parents"], device=dev))
+        parents = np_(case["parents"])
     kp, vp = np_(case["k_pool"]), np_(case["v_pool"])
     bt, ctx, cu = np_(case["block_table"]), np_(case["ctx_lens"]), np_(case["cu_q"])
     qn = np_(case["q"])
@@ -167,6 +203,8 @@ def cpu_baseline(wl, w, dev, budget_s):
             kp, vp, _, _ = oracle.kv_append(kn, vn, kp, vp, bt, ctx, cu, w.kv_dtype)
         t_append = time.perf_counter() - t0
         t0 = time.perf_counter()
+        if tree:
+            sc["draft_mask"] = oracle.ancestor_masks(parents, cu)
         for pair in pairs:
             oracle.spec_verify_attn(qn, kp, vp, bt, ctx, cu, scale, select=[pair], **sc)
             done_pairs += 1
@@ -177,8 +215,14 @@ def cpu_baseline(wl, w, dev, budget_s):
         t0 = time.perf_counter()
         for b in seqs:
             r0, r1 = int(cu[b]) + b, int(cu[b + 1]) + b + 1
-            oracle.accept_prefix(logits[r0:r1], drafts[int(cu[b]):int(cu[b + 1])],
-                                 np.array([0, int(cu[b + 1] - cu[b])]))
+            one = np.array([0, int(cu[b + 1] - cu[b])])
+            if tree:
+                _, n, _, path = oracle.accept_tree(logits[r0:r1], drafts[int(cu[b]):int(cu[b + 1])],
+                                                   parents[int(cu[b]):int(cu[b + 1])], one)
+                for pool in (kp, vp):
+                    oracle.commit_path(pool, bt[b:b + 1], ctx[b:b + 1], one, n, path)
+            else:
+                oracle.accept_prefix(logits[r0:r1], drafts[int(cu[b]):int(cu[b + 1])], one)
         t_acc = time.perf_counter() - t0
     frac_pairs = done_pairs / len(pairs)
     frac_seqs = len(seqs) / B
@@ -187,8 +231,9 @@ def cpu_baseline(wl, w, dev, budget_s):
     return {
         "value": tokens / step_s, "unit": "verified draft tokens/s", "cores": 1, "kind": "oracle",
         "sample": (f"{done_pairs} of {len(pairs)} (sequence, kv-head) attention pairs "
-                   f"({t_attn:.1f} s), acceptance for {len(seqs)} of {B} sequences, the whole "
-                   f"append; scaled to the full batch; numpy BLAS limited to 1 thread"),
+                   f"({t_attn:.1f} s), acceptance{' and branch commit' if tree else ''} for "
+                   f"{len(seqs)} of {B} sequences, the whole append; scaled to the full batch; "
+                   f"numpy BLAS limited to 1 thread"),
         "seconds_per_step_estimate": step_s,
     }
 
@@ -237,7 +282,7 @@ def main():
     for s in range(args.warmup):
         inp = sets[s % nsets]
         inp.append()
-        inp.attn()
+        inp.step_attn()
         inp.accept()
     torch.cuda.synchronize()
 
@@ -250,7 +295,7 @@ def main():
     for s in range(args.steps):
         inp = sets[s % nsets]
         inp.append()
-        inp.attn()
+        inp.step_attn()
         inp.accept()
     t_end.record(stream)
     torch.cuda.synchronize()
@@ -292,7 +337,9 @@ def main():
         "data": "synthetic (seeded torch Philox; no dataset)",
         "config": {
             "workload": (f"{w.name}: B={w.B}, Hq={w.Hq}, Hkv={w.Hkv}, d={w.d}, "
-                         f"S={w.ctx}, k={w.k}, {w.kv_dtype} paged KV (16-token pages, random "
+                         f"S={w.ctx}, k={w.k}"
+                         f"{' token-tree nodes' if w.name in wl.TREE_WORKLOADS else ''}, "
+                         f"{w.kv_dtype} paged KV (16-token pages, random "
                          f"page permutation); acceptance over fp32 logits "
                          f"[sum(k_b+1), {w.vocab}]"),
             "global_batch": w.B, "seq_len": w.ctx if isinstance(w.ctx, int) else list(w.ctx),

@@ -180,6 +180,70 @@ sva_status sva_accept_prefix(const sva_batch *batch, const float *logits, int32_
                              int32_t *next_token, void *workspace, size_t workspace_bytes,
                              void *stream);
 
+/* ---- Token trees ------------------------------------------------------------
+ * "Decoding Speculative Decoding from First Principles", section "Tree based
+ * verification" (SpecInfer, EAGLE-2, DDTree): the drafter proposes a tree of
+ * continuations, tree attention relates each draft only to its own lineage,
+ * and the accepted continuation is the longest branch the target agrees with.
+ * A tree of k_b <= 16 nodes is given per sequence as
+ *   parents   device [T] int32, rows ordered by cu_q: the parent of node i is
+ *             -1 (a child of the last committed token) or an earlier node
+ *             0 .. i-1 (topological order); any other value is read as -1.
+ * Node i's K/V row sits at position S_b + i (sva_kv_append writes it there).
+ * A chain (parent i-1) is the causal case of the calls above. */
+
+/* Ancestor masks: masks[cu_q[b] + i] gets bit j set when node j of sequence b
+ * is node i or one of its ancestors (bits >= k_b are zero).  One call per
+ * verification step; the masks serve every layer's attention call.
+ *   masks   device [T] uint32 (written) */
+sva_status sva_tree_masks(const sva_batch *batch, const int32_t *parents, uint32_t *masks,
+                          void *stream);
+
+/* Tree attention: sva_spec_verify_attn with the causal draft mask replaced by
+ *   draft_mask  device [T] uint32: draft i of sequence b sees the committed
+ *               positions 0 .. S_b - 1 and the drafts j < k_b whose bit j is
+ *               set in draft_mask[cu_q[b] + i] (normally sva_tree_masks'
+ *               output).  Every other argument, the workspace included, is as
+ *               for sva_spec_verify_attn; a row that sees no key at all
+ *               (S_b = 0 and an empty mask) has no defined output. */
+sva_status sva_spec_verify_attn_tree(const sva_batch *batch, const void *q, int32_t q_dtype,
+                                     int32_t Hq, const sva_paged_kv *kv,
+                                     const uint32_t *draft_mask, float softmax_scale, void *out,
+                                     int32_t out_dtype, const sva_verify_opts *opts,
+                                     void *workspace, size_t workspace_bytes, void *stream);
+
+/* Greedy tree acceptance.  Logit rows as for sva_accept_prefix: sequence b
+ * owns k_b + 1 rows from cu_q[b] + b; row 0 scores the token after the
+ * committed context, row 1 + i the token after node i.  From the root, the
+ * walk moves to the child whose draft token equals the argmax of the current
+ * node's row (the lowest index when several children carry it) and stops
+ * when none does.
+ *   argmax_ids   device [T + B] int32 (written), as for sva_accept_prefix
+ *   accept_len   device [B] int32 (written): n_b, nodes on the accepted branch
+ *   next_token   device [B] int32 (written): the target's token at the last
+ *                accepted node (the root when n_b = 0)
+ *   accept_path  device [T] int32 (written): entries cu_q[b] .. cu_q[b]+n_b-1
+ *                hold the accepted nodes from the root down, the rest -1
+ *   workspace    >= sva_accept_workspace_bytes(batch, V) bytes
+ * The step emits the branch's draft tokens, then next_token: n_b + 1 tokens. */
+sva_status sva_accept_tree(const sva_batch *batch, const float *logits, int32_t V,
+                           const int32_t *draft_ids, const int32_t *parents, int32_t *argmax_ids,
+                           int32_t *accept_len, int32_t *next_token, int32_t *accept_path,
+                           void *workspace, size_t workspace_bytes, void *stream);
+
+/* Commit of the accepted branch: for every sequence and kv head, the K/V rows
+ * (and INT8 scales) at positions S_b + accept_path[cu_q[b] + j] move to
+ * S_b + j, j < accept_len[b], so the cache holds one linear sequence again
+ * ("HeteroReason", KVMU: rejected speculative history is discarded by a
+ * pointer move; the surviving branch is first made contiguous).  Rows are
+ * read before any is written, so overlapping moves are safe.  Path entries
+ * outside j+1 .. k_b-1 leave row j in place (a chain's path is the
+ * identity).  ctx_lens is not changed: the caller commits
+ * S_b += n_b.  The pages of positions S_b .. S_b + k_b - 1 must belong to
+ * sequence b alone. */
+sva_status sva_kv_commit_path(const sva_batch *batch, const int32_t *accept_len,
+                              const int32_t *accept_path, const sva_paged_kv *kv, void *stream);
+
 const char *sva_status_string(sva_status status);
 const char *sva_last_error(void);
 

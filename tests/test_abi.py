@@ -59,6 +59,13 @@ def test_host_checked_errors_need_no_gpu():
                                     None, 0, None) == 1
     assert lib.sva_kv_append(None, None, None, 0, None, None) == 1
     assert lib.sva_accept_prefix(None, None, 10, None, None, None, None, None, 0, None) == 1
+    # token-tree entry points
+    assert lib.sva_tree_masks(None, None, None, None) == 1
+    assert lib.sva_spec_verify_attn_tree(None, None, 0, 8, None, None, ctypes.c_float(1.0), None,
+                                         0, None, None, 0, None) == 1
+    assert lib.sva_accept_tree(None, None, 10, None, None, None, None, None, None, None, 0,
+                               None) == 1
+    assert lib.sva_kv_commit_path(None, None, None, None, None) == 1
 
 
 def test_batch_and_cache_shape_checks():
@@ -85,6 +92,11 @@ def test_batch_and_cache_shape_checks():
     kv.kv_dtype = tva.SVA_INT8                             # INT8 without scales
     assert call(4) == 1
     assert b"scale" in lib.sva_last_error()
+    kv.kv_dtype = tva.SVA_BF16                             # tree call without its mask
+    assert lib.sva_spec_verify_attn_tree(
+        ctypes.byref(b), ctypes.c_void_p(64), 1, 4, ctypes.byref(kv), None, ctypes.c_float(0.1),
+        ctypes.c_void_p(64), 1, None, ctypes.c_void_p(64), 1 << 30, None) == 1
+    assert b"draft_mask" in lib.sva_last_error()
 
 
 def test_build_flags_keep_ieee_division_and_no_packed_fp32():

@@ -22,6 +22,7 @@ import torch
 __all__ = [
     "load", "SvaError", "Batch", "PagedKV", "kv_quant_int8", "kv_append", "spec_verify_attn",
     "verify_workspace_bytes", "accept_prefix", "accept_workspace_bytes", "LIB_PATH",
+    "tree_masks", "accept_tree", "kv_commit_path",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "_lib", "libspecverify.so")
@@ -86,6 +87,15 @@ def load():
         lib.sva_accept_workspace_bytes.argtypes = [vp, i32]
         lib.sva_accept_prefix.restype = ctypes.c_int
         lib.sva_accept_prefix.argtypes = [vp, vp, i32, vp, vp, vp, vp, vp, sz, vp]
+        lib.sva_tree_masks.restype = ctypes.c_int
+        lib.sva_tree_masks.argtypes = [vp, vp, vp, vp]
+        lib.sva_spec_verify_attn_tree.restype = ctypes.c_int
+        lib.sva_spec_verify_attn_tree.argtypes = [vp, vp, i32, i32, vp, vp, ctypes.c_float, vp,
+                                                  i32, vp, vp, sz, vp]
+        lib.sva_accept_tree.restype = ctypes.c_int
+        lib.sva_accept_tree.argtypes = [vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        lib.sva_kv_commit_path.restype = ctypes.c_int
+        lib.sva_kv_commit_path.argtypes = [vp, vp, vp, vp, vp]
         _lib = lib
     return _lib
 
@@ -304,10 +314,23 @@ def _zeroed_workspace(device, nbytes):
     return ws
 
 
+def _check_mask(batch, draft_mask, dev):
+    if draft_mask is None:
+        return
+    _need(draft_mask, "draft_mask", 1)
+    if draft_mask.dtype not in (torch.int32, torch.uint32):
+        raise TypeError("draft_mask must be int32 or uint32 bit patterns")
+    _shape(draft_mask, (batch.total_q,), "draft_mask")
+    _same_device(draft_mask, dev)
+
+
 def spec_verify_attn(batch, q, kv, softmax_scale=None, out=None, out_dtype=None,
-                     workspace=None, path=PATH_AUTO, num_workgroups=0, stream=None):
-    """Causal verification attention of the drafts q [T, Hq, d] over the paged
-    cache.  Returns out [T, Hq, d] (dtype of q unless out_dtype is given).
+                     workspace=None, path=PATH_AUTO, num_workgroups=0, stream=None,
+                     draft_mask=None):
+    """Verification attention of the drafts q [T, Hq, d] over the paged
+    cache: causal among the drafts, or tree attention when draft_mask [T]
+    (bit j: draft j of the sequence is visible, see tree_masks) is given.
+    Returns out [T, Hq, d] (dtype of q unless out_dtype is given).
     A caller-provided workspace must be zero-filled before its first use."""
     lib = load()
     _need(q, "q", 3)
@@ -317,16 +340,24 @@ def spec_verify_attn(batch, q, kv, softmax_scale=None, out=None, out_dtype=None,
     if out is None:
         out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
     _check_attn(batch, q, kv, out)
+    _check_mask(batch, draft_mask, q)
     nbytes = verify_workspace_bytes(batch, kv, Hq, path, num_workgroups)
     if workspace is None:
         workspace = _zeroed_workspace(q.device, nbytes)
     _need(workspace, "workspace")
     cb, ckv, co = batch._c(), kv._c(), _opts(path, num_workgroups)
-    _check("sva_spec_verify_attn", lib.sva_spec_verify_attn(
-        ctypes.byref(cb), _ptr(q), _dtype_code(q, "q"), Hq, ctypes.byref(ckv),
-        float(softmax_scale), _ptr(out), _dtype_code(out, "out"), ctypes.byref(co),
-        _ptr(workspace), workspace.numel() * workspace.element_size(),
-        _stream(stream, q.device)))
+    if draft_mask is None:
+        _check("sva_spec_verify_attn", lib.sva_spec_verify_attn(
+            ctypes.byref(cb), _ptr(q), _dtype_code(q, "q"), Hq, ctypes.byref(ckv),
+            float(softmax_scale), _ptr(out), _dtype_code(out, "out"), ctypes.byref(co),
+            _ptr(workspace), workspace.numel() * workspace.element_size(),
+            _stream(stream, q.device)))
+    else:
+        _check("sva_spec_verify_attn_tree", lib.sva_spec_verify_attn_tree(
+            ctypes.byref(cb), _ptr(q), _dtype_code(q, "q"), Hq, ctypes.byref(ckv),
+            _ptr(draft_mask), float(softmax_scale), _ptr(out), _dtype_code(out, "out"),
+            ctypes.byref(co), _ptr(workspace), workspace.numel() * workspace.element_size(),
+            _stream(stream, q.device)))
     return out
 
 
@@ -362,6 +393,78 @@ def accept_prefix(batch, logits, draft_ids, argmax_ids=None, accept_len=None, ne
     return argmax_ids, accept_len, next_token
 
 
+def _int32_vec(t, n, what):
+    _need(t, what, 1)
+    if t.dtype != torch.int32:
+        raise TypeError(f"{what} must be int32")
+    _shape(t, (n,), what)
+
+
+def tree_masks(batch, parents, masks=None, stream=None):
+    """Ancestor bitmasks of token trees: parents [T] int32 (-1: child of the
+    last committed token, else an earlier node of the same sequence).
+    Returns masks [T] int32 (bit patterns; bit j: node j is the node itself
+    or one of its ancestors)."""
+    lib = load()
+    _int32_vec(parents, batch.total_q, "parents")
+    if masks is None:
+        masks = torch.empty(batch.total_q, dtype=torch.int32, device=parents.device)
+    _int32_vec(masks, batch.total_q, "masks")
+    _same_device(parents, masks, batch.cu_q)
+    cb = batch._c()
+    _check("sva_tree_masks", lib.sva_tree_masks(ctypes.byref(cb), _ptr(parents), _ptr(masks),
+                                                _stream(stream, parents.device)))
+    return masks
+
+
+def accept_tree(batch, logits, draft_ids, parents, argmax_ids=None, accept_len=None,
+                next_token=None, accept_path=None, workspace=None, stream=None):
+    """Greedy acceptance over token trees.  logits [T+B, V] float32 (row 0 of a
+    sequence: after the context, row 1+i: after node i), draft_ids and parents
+    [T] int32.  Returns (argmax_ids [T+B], accept_len [B], next_token [B],
+    accept_path [T]); accept_path lists each sequence's accepted nodes from the
+    root down, then -1."""
+    lib = load()
+    _need(logits, "logits", 2)
+    dev = logits.device
+    V = int(logits.shape[1])
+    if argmax_ids is None:
+        argmax_ids = torch.empty(logits.shape[0], dtype=torch.int32, device=dev)
+    if accept_len is None:
+        accept_len = torch.empty(batch.B, dtype=torch.int32, device=dev)
+    if next_token is None:
+        next_token = torch.empty(batch.B, dtype=torch.int32, device=dev)
+    if accept_path is None:
+        accept_path = torch.empty(batch.total_q, dtype=torch.int32, device=dev)
+    _check_accept(batch, logits, draft_ids, argmax_ids, accept_len, next_token)
+    _int32_vec(parents, batch.total_q, "parents")
+    _int32_vec(accept_path, batch.total_q, "accept_path")
+    _same_device(logits, parents, accept_path)
+    if workspace is None:
+        workspace = torch.empty(max(accept_workspace_bytes(batch, V), 8), dtype=torch.uint8,
+                                device=dev)
+    cb = batch._c()
+    _check("sva_accept_tree", lib.sva_accept_tree(
+        ctypes.byref(cb), _ptr(logits), V, _ptr(draft_ids), _ptr(parents), _ptr(argmax_ids),
+        _ptr(accept_len), _ptr(next_token), _ptr(accept_path), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream, dev)))
+    return argmax_ids, accept_len, next_token, accept_path
+
+
+def kv_commit_path(batch, accept_len, accept_path, kv, stream=None):
+    """Move each sequence's accepted branch (accept_path, from accept_tree) to
+    the positions right after its committed context, every kv head."""
+    lib = load()
+    _int32_vec(accept_len, batch.B, "accept_len")
+    _int32_vec(accept_path, batch.total_q, "accept_path")
+    _check_batch_kv(batch, kv)
+    _same_device(accept_len, accept_path, kv.k)
+    cb, ckv = batch._c(), kv._c()
+    _check("sva_kv_commit_path", lib.sva_kv_commit_path(
+        ctypes.byref(cb), _ptr(accept_len), _ptr(accept_path), ctypes.byref(ckv),
+        _stream(stream, kv.k.device)))
+
+
 class _Prepared:
     """A call with every argument marshalled once; calling it only enqueues
     the C entry point on the stream (current stream of the device by default)."""
@@ -385,9 +488,10 @@ def prepare_kv_append(batch, k_new, v_new, kv):
 
 
 def prepare_spec_verify_attn(batch, q, kv, out, softmax_scale=None, workspace=None,
-                             path=PATH_AUTO, num_workgroups=0):
+                             path=PATH_AUTO, num_workgroups=0, draft_mask=None):
     lib = load()
     _check_attn(batch, q, kv, out)
+    _check_mask(batch, draft_mask, q)
     Hq, d = int(q.shape[1]), int(q.shape[2])
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(d)
@@ -395,6 +499,12 @@ def prepare_spec_verify_attn(batch, q, kv, out, softmax_scale=None, workspace=No
     if workspace is None:
         workspace = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=q.device)
     cb, ckv, co = batch._c(), kv._c(), _opts(path, num_workgroups)
+    if draft_mask is not None:
+        args = (ctypes.byref(cb), _ptr(q), _dtype_code(q, "q"), Hq, ctypes.byref(ckv),
+                _ptr(draft_mask), float(softmax_scale), _ptr(out), _dtype_code(out, "out"),
+                ctypes.byref(co), _ptr(workspace), workspace.numel() * workspace.element_size())
+        return _Prepared("sva_spec_verify_attn_tree", lib.sva_spec_verify_attn_tree, args,
+                         q.device, (cb, ckv, co, batch, q, kv, out, workspace, draft_mask))
     args = (ctypes.byref(cb), _ptr(q), _dtype_code(q, "q"), Hq, ctypes.byref(ckv),
             float(softmax_scale), _ptr(out), _dtype_code(out, "out"), ctypes.byref(co),
             _ptr(workspace), workspace.numel() * workspace.element_size())
@@ -419,4 +529,44 @@ def prepare_accept_prefix(batch, logits, draft_ids, argmax_ids, accept_len, next
                       workspace))
 
 
-__all__ += ["prepare_kv_append", "prepare_spec_verify_attn", "prepare_accept_prefix"]
+def prepare_tree_masks(batch, parents, masks):
+    lib = load()
+    _int32_vec(parents, batch.total_q, "parents")
+    _int32_vec(masks, batch.total_q, "masks")
+    cb = batch._c()
+    return _Prepared("sva_tree_masks", lib.sva_tree_masks, (ctypes.byref(cb), _ptr(parents),
+                     _ptr(masks)), parents.device, (cb, batch, parents, masks))
+
+
+def prepare_accept_tree(batch, logits, draft_ids, parents, argmax_ids, accept_len, next_token,
+                        accept_path, workspace=None):
+    lib = load()
+    _check_accept(batch, logits, draft_ids, argmax_ids, accept_len, next_token)
+    _int32_vec(parents, batch.total_q, "parents")
+    _int32_vec(accept_path, batch.total_q, "accept_path")
+    V = int(logits.shape[1])
+    if workspace is None:
+        workspace = torch.empty(max(accept_workspace_bytes(batch, V), 8), dtype=torch.uint8,
+                                device=logits.device)
+    cb = batch._c()
+    args = (ctypes.byref(cb), _ptr(logits), V, _ptr(draft_ids), _ptr(parents), _ptr(argmax_ids),
+            _ptr(accept_len), _ptr(next_token), _ptr(accept_path), _ptr(workspace),
+            workspace.numel() * workspace.element_size())
+    return _Prepared("sva_accept_tree", lib.sva_accept_tree, args, logits.device,
+                     (cb, batch, logits, draft_ids, parents, argmax_ids, accept_len, next_token,
+                      accept_path, workspace))
+
+
+def prepare_kv_commit_path(batch, accept_len, accept_path, kv):
+    lib = load()
+    _int32_vec(accept_len, batch.B, "accept_len")
+    _int32_vec(accept_path, batch.total_q, "accept_path")
+    _check_batch_kv(batch, kv)
+    cb, ckv = batch._c(), kv._c()
+    args = (ctypes.byref(cb), _ptr(accept_len), _ptr(accept_path), ctypes.byref(ckv))
+    return _Prepared("sva_kv_commit_path", lib.sva_kv_commit_path, args, kv.k.device,
+                     (cb, ckv, batch, accept_len, accept_path, kv))
+
+
+__all__ += ["prepare_kv_append", "prepare_spec_verify_attn", "prepare_accept_prefix",
+            "prepare_tree_masks", "prepare_accept_tree", "prepare_kv_commit_path"]

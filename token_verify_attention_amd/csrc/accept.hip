@@ -124,11 +124,8 @@ AcceptPlan plan_accept(const sva_batch* batch, int V) {
   return p;
 }
 
-hipError_t launch_accept_prefix(const sva_batch* batch, const float* logits, int V,
-                                const int32_t* draft_ids, int32_t* argmax_ids, int32_t* accept_len,
-                                int32_t* next_token, const AcceptPlan& plan, void* workspace,
-                                hipStream_t st) {
-  uint64_t* keys = static_cast<uint64_t*>(workspace);
+hipError_t launch_argmax_keys(const float* logits, int V, const AcceptPlan& plan,
+                              uint64_t* keys, hipStream_t st) {
   const bool vec4 = (V % 4 == 0) && ((reinterpret_cast<uintptr_t>(logits) & 15) == 0);
   const dim3 grid(unsigned(plan.rows) * plan.chunks);
   if (vec4)
@@ -137,7 +134,15 @@ hipError_t launch_accept_prefix(const sva_batch* batch, const float* logits, int
   else
     hipLaunchKernelGGL(argmax_chunks_kernel<false>, grid, dim3(kArgThreads), 0, st, logits, V,
                        plan.chunks, plan.chunk_len, keys);
-  hipError_t e = hipGetLastError();
+  return hipGetLastError();
+}
+
+hipError_t launch_accept_prefix(const sva_batch* batch, const float* logits, int V,
+                                const int32_t* draft_ids, int32_t* argmax_ids, int32_t* accept_len,
+                                int32_t* next_token, const AcceptPlan& plan, void* workspace,
+                                hipStream_t st) {
+  uint64_t* keys = static_cast<uint64_t*>(workspace);
+  hipError_t e = launch_argmax_keys(logits, V, plan, keys, st);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(accept_scan_kernel, dim3(batch->B), dim3(kWave), 0, st, keys, plan.chunks,
                      batch->cu_q, batch->total_q, batch->max_q, draft_ids, argmax_ids, accept_len,

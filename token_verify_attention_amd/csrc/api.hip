@@ -178,11 +178,11 @@ size_t sva_verify_workspace_bytes(const sva_batch* batch, const sva_paged_kv* kv
   return sva::plan_verify_attn(batch, kv, Hq, dev->num_cus, opts).total_bytes;
 }
 
-sva_status sva_spec_verify_attn(const sva_batch* batch, const void* q, int32_t q_dtype,
-                                int32_t Hq, const sva_paged_kv* kv, float softmax_scale,
-                                void* out, int32_t out_dtype, const sva_verify_opts* opts,
-                                void* workspace, size_t workspace_bytes, void* stream) {
-  g_last_error.clear();
+static sva_status verify_attn(const sva_batch* batch, const void* q, int32_t q_dtype, int32_t Hq,
+                              const sva_paged_kv* kv, const uint32_t* draft_mask,
+                              float softmax_scale, void* out, int32_t out_dtype,
+                              const sva_verify_opts* opts, void* workspace,
+                              size_t workspace_bytes, void* stream) {
   if (sva_status s = check_attn_shape(batch, kv, Hq)) return s;
   if (q_dtype != SVA_F32 && q_dtype != SVA_BF16)
     return fail(SVA_ERR_UNSUPPORTED, "q_dtype = %d", q_dtype);
@@ -207,9 +207,42 @@ sva_status sva_spec_verify_attn(const sva_batch* batch, const void* q, int32_t q
     return fail(SVA_ERR_INVALID_ARG, "workspace of %zu bytes < %zu needed", workspace_bytes,
                 plan.total_bytes);
   if (!aligned16(workspace)) return fail(SVA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
-  hipError_t e = sva::launch_verify_attn(batch, q, q_dtype, Hq, kv, softmax_scale, out, out_dtype,
-                                         path, plan, workspace, as_stream(stream));
+  hipError_t e = sva::launch_verify_attn(batch, q, q_dtype, Hq, kv, draft_mask, softmax_scale, out,
+                                         out_dtype, path, plan, workspace, as_stream(stream));
   return e == hipSuccess ? SVA_OK : hip_fail(e, "spec_verify_attn launch");
+}
+
+sva_status sva_spec_verify_attn(const sva_batch* batch, const void* q, int32_t q_dtype,
+                                int32_t Hq, const sva_paged_kv* kv, float softmax_scale,
+                                void* out, int32_t out_dtype, const sva_verify_opts* opts,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  return verify_attn(batch, q, q_dtype, Hq, kv, nullptr, softmax_scale, out, out_dtype, opts,
+                     workspace, workspace_bytes, stream);
+}
+
+sva_status sva_spec_verify_attn_tree(const sva_batch* batch, const void* q, int32_t q_dtype,
+                                     int32_t Hq, const sva_paged_kv* kv,
+                                     const uint32_t* draft_mask, float softmax_scale, void* out,
+                                     int32_t out_dtype, const sva_verify_opts* opts,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  if (batch && batch->total_q > 0 && !draft_mask)
+    return fail(SVA_ERR_INVALID_ARG, "draft_mask is NULL");
+  return verify_attn(batch, q, q_dtype, Hq, kv, draft_mask, softmax_scale, out, out_dtype, opts,
+                     workspace, workspace_bytes, stream);
+}
+
+sva_status sva_tree_masks(const sva_batch* batch, const int32_t* parents, uint32_t* masks,
+                          void* stream) {
+  g_last_error.clear();
+  if (sva_status s = check_batch(batch)) return s;
+  if (batch->total_q == 0 || batch->B == 0) return SVA_OK;
+  if (!parents || !masks) return fail(SVA_ERR_INVALID_ARG, "parents / masks is NULL");
+  const DeviceInfo* dev;
+  if (sva_status s = current_device(&dev)) return s;
+  hipError_t e = sva::launch_tree_masks(batch, parents, masks, as_stream(stream));
+  return e == hipSuccess ? SVA_OK : hip_fail(e, "tree_masks launch");
 }
 
 size_t sva_accept_workspace_bytes(const sva_batch* batch, int32_t V) {
@@ -239,6 +272,49 @@ sva_status sva_accept_prefix(const sva_batch* batch, const float* logits, int32_
   hipError_t e = sva::launch_accept_prefix(batch, logits, V, draft_ids, argmax_ids, accept_len,
                                            next_token, plan, workspace, as_stream(stream));
   return e == hipSuccess ? SVA_OK : hip_fail(e, "accept_prefix launch");
+}
+
+sva_status sva_accept_tree(const sva_batch* batch, const float* logits, int32_t V,
+                           const int32_t* draft_ids, const int32_t* parents, int32_t* argmax_ids,
+                           int32_t* accept_len, int32_t* next_token, int32_t* accept_path,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  if (sva_status s = check_batch(batch)) return s;
+  if (V < 1) return fail(SVA_ERR_INVALID_ARG, "V = %d < 1", V);
+  if (batch->B == 0) return SVA_OK;
+  if (!logits || !argmax_ids || !accept_len || !next_token ||
+      (batch->total_q > 0 && (!draft_ids || !parents || !accept_path)))
+    return fail(SVA_ERR_INVALID_ARG, "NULL pointer");
+  const sva::AcceptPlan plan = sva::plan_accept(batch, V);
+  if (!workspace || workspace_bytes < plan.total_bytes)
+    return fail(SVA_ERR_INVALID_ARG, "workspace of %zu bytes < %zu needed", workspace_bytes,
+                plan.total_bytes);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 7) != 0)
+    return fail(SVA_ERR_INVALID_ARG, "workspace must be 8-byte aligned");
+  const DeviceInfo* dev;
+  if (sva_status s = current_device(&dev)) return s;
+  hipError_t e = sva::launch_accept_tree(batch, logits, V, draft_ids, parents, argmax_ids,
+                                         accept_len, next_token, accept_path, plan, workspace,
+                                         as_stream(stream));
+  return e == hipSuccess ? SVA_OK : hip_fail(e, "accept_tree launch");
+}
+
+sva_status sva_kv_commit_path(const sva_batch* batch, const int32_t* accept_len,
+                              const int32_t* accept_path, const sva_paged_kv* kv, void* stream) {
+  g_last_error.clear();
+  if (sva_status s = check_batch(batch)) return s;
+  if (sva_status s = check_kv(kv, true)) return s;
+  if (kv->d != 64 && kv->d != 128 && kv->d != 256) return fail(SVA_ERR_UNSUPPORTED, "d = %d", kv->d);
+  if (batch->total_q == 0 || batch->B == 0) return SVA_OK;
+  if (!accept_len || !accept_path) return fail(SVA_ERR_INVALID_ARG, "accept_len / accept_path is NULL");
+  if (!aligned16(kv->k) || !aligned16(kv->v))
+    return fail(SVA_ERR_INVALID_ARG, "K/V buffers must be 16-byte aligned");
+  if (int64_t(batch->B) * kv->Hkv > 0x7fffffff)
+    return fail(SVA_ERR_UNSUPPORTED, "B * Hkv too large");
+  const DeviceInfo* dev;
+  if (sva_status s = current_device(&dev)) return s;
+  hipError_t e = sva::launch_kv_commit_path(batch, accept_len, accept_path, kv, as_stream(stream));
+  return e == hipSuccess ? SVA_OK : hip_fail(e, "kv_commit_path launch");
 }
 
 }  // extern "C"

@@ -27,10 +27,12 @@ struct AttnPlan {
 };
 AttnPlan plan_verify_attn(const sva_batch* batch, const sva_paged_kv* kv, int Hq, int num_cus,
                           const sva_verify_opts* opts);
+// draft_mask: [T] tree attention masks (bit j: draft j of the sequence is
+// visible), or NULL for causal drafts.
 hipError_t launch_verify_attn(const sva_batch* batch, const void* q, int q_dtype, int Hq,
-                              const sva_paged_kv* kv, float softmax_scale, void* out,
-                              int out_dtype, int path, const AttnPlan& plan, void* workspace,
-                              hipStream_t st);
+                              const sva_paged_kv* kv, const uint32_t* draft_mask,
+                              float softmax_scale, void* out, int out_dtype, int path,
+                              const AttnPlan& plan, void* workspace, hipStream_t st);
 
 // Acceptance: chunked argmax then a per-sequence scan.
 struct AcceptPlan {
@@ -40,9 +42,26 @@ struct AcceptPlan {
   size_t total_bytes;
 };
 AcceptPlan plan_accept(const sva_batch* batch, int V);
+// Kernel 1 of acceptance: per (row, chunk) the 64-bit key of the chunk's
+// first maximum (order-preserving float bits above the complemented index).
+hipError_t launch_argmax_keys(const float* logits, int V, const AcceptPlan& plan, uint64_t* keys,
+                              hipStream_t st);
 hipError_t launch_accept_prefix(const sva_batch* batch, const float* logits, int V,
                                 const int32_t* draft_ids, int32_t* argmax_ids, int32_t* accept_len,
                                 int32_t* next_token, const AcceptPlan& plan, void* workspace,
                                 hipStream_t st);
+
+// Token trees: ancestor masks, greedy tree acceptance, and the move of the
+// accepted branch's K/V rows to the positions right after the context.
+hipError_t launch_tree_masks(const sva_batch* batch, const int32_t* parents, uint32_t* masks,
+                             hipStream_t st);
+hipError_t launch_accept_tree(const sva_batch* batch, const float* logits, int V,
+                              const int32_t* draft_ids, const int32_t* parents,
+                              int32_t* argmax_ids, int32_t* accept_len, int32_t* next_token,
+                              int32_t* accept_path, const AcceptPlan& plan, void* workspace,
+                              hipStream_t st);
+hipError_t launch_kv_commit_path(const sva_batch* batch, const int32_t* accept_len,
+                                 const int32_t* accept_path, const sva_paged_kv* kv,
+                                 hipStream_t st);
 
 }  // namespace sva

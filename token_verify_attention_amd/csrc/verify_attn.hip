@@ -77,6 +77,7 @@ struct AttnParams {
   const int32_t* block_table;
   const int32_t* ctx_lens;
   const int32_t* cu_q;
+  const uint32_t* draft_mask;   // [T] tree attention masks, or NULL (causal drafts)
   void* out;
   float* partials;
   int32_t* counters;
@@ -90,6 +91,17 @@ struct AttnParams {
 struct SeqInfo {
   int S, k, q0, np;
 };
+
+// Keys a query row sees: the committed context 0 .. S-1 and the drafts j < k
+// whose bit j is set in the row's draft mask.  Causal drafts: draft i's mask
+// is bits 0 .. i (positions 0 .. S + i).  Tree attention: the caller's mask.
+// One register per row; the draft range end S + k is the segment's.
+__device__ __forceinline__ uint32_t row_mask(const AttnParams& p, int q0, int i) {
+  return p.draft_mask ? p.draft_mask[q0 + i] : (2u << i) - 1u;
+}
+__device__ __forceinline__ bool key_visible(int pos, int S, int end, uint32_t mask) {
+  return pos < S || (pos < end && ((mask >> ((pos - S) & 31)) & 1u));
+}
 
 // Sequence b with every device-resident value clamped into the buffers.
 __device__ __forceinline__ SeqInfo seq_info(const AttnParams& p, int b) {
@@ -454,7 +466,8 @@ struct ValuStep {
   char* ps;                                           // [RV][32] probabilities (f32 or bf16)
   float scale_log2;
   float m[RV], l[RV], o[RV][CPL];
-  int lim[RV];
+  uint32_t vis[RV];                                   // draft masks of the rows
+  int ctx;                                            // S of the sequence
   int valid_end;
   int lane, t, h;
 
@@ -465,13 +478,14 @@ struct ValuStep {
     t = lane & 31;
     h = lane >> 5;
     valid_end = sg.S + sg.k;
+    ctx = sg.S;
 #pragma unroll
     for (int r = 0; r < RV; ++r) {
       m[r] = kNegBig;
       l[r] = 0.f;
 #pragma unroll
       for (int e = 0; e < CPL; ++e) o[r][e] = 0.f;
-      lim[r] = (r0 + r < sg.R) ? sg.S + (r0 + r) / p.G : -1;
+      vis[r] = (r0 + r < sg.R) ? row_mask(p, sg.q0, (r0 + r) / p.G) : 0u;
     }
   }
 
@@ -648,7 +662,7 @@ struct ValuStep {
     }
 #pragma unroll
     for (int r = 0; r < RV; ++r) {
-      const float x = (tok_ok && pos <= lim[r]) ? s[r] * scale_log2 * ksc : -INFINITY;
+      const float x = (tok_ok && key_visible(pos, ctx, valid_end, vis[r])) ? s[r] * scale_log2 * ksc : -INFINITY;
       const float mx = xrow16_max(row16_max(x));                // over the 32 tokens
       const float mn = fmaxf(m[r], mx);
       const float alpha = exp2f(m[r] - mn);
@@ -834,7 +848,8 @@ struct MfmaStep {
   f32x4 lsum[NRB];                        // INT8: all-ones MFMA over the unscaled weights
   float m[NRB], l[NRB];
   float s0[NRB];                          // INT8: start value of the S^T accumulator
-  int lim[NRB];
+  uint32_t vis[NRB];                      // draft masks of the rows
+  int ctx;                                // S of the sequence
   int valid_end;
   int lane, l16, c;
   bool qbf16;                             // INT8 with bf16 Q: qB holds bf16 until ready()
@@ -859,15 +874,16 @@ struct MfmaStep {
     l16 = lane & 15;
     c = lane >> 4;
     valid_end = sg.S + sg.k;
+    ctx = sg.S;
     // bf16 Q is only loaded here (raw words); work that needs the values waits
     // for ready(), after the first page copies are issued.
     qbf16 = I8 && !p.q_f32;
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
       const int r = r0 + 16 * rb + l16;
-      lim[rb] = -1;
+      vis[rb] = 0u;
       if (r < sg.R) {
-        lim[rb] = sg.S + r / p.G;
+        vis[rb] = row_mask(p, sg.q0, r / p.G);
         const int64_t qe = out_row(p, sg, r) * D + c * (D / 4);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
@@ -1023,7 +1039,7 @@ struct MfmaStep {
         const int pg = j >> 2, i = j & 3;
         const int pos = (a + pg) * kPage + 4 * c + i;
         const float v = fmaf(s[pg][rb][i], f16x2_half(kw[pg][i >> 1], i & 1), -m[rb]);
-        y[rb][j] = (!EDGE || (pg < npg && pos <= lim[rb])) ? v : -INFINITY;
+        y[rb][j] = (!EDGE || (pg < npg && key_visible(pos, ctx, valid_end, vis[rb]))) ? v : -INFINITY;
         t = fmaxf(t, y[rb][j]);
       }
       move |= xrow32_max(xrow16_max(t)) > kLazy;
@@ -1037,7 +1053,7 @@ struct MfmaStep {
           const int pg = j >> 2, i = j & 3;
           const int pos = (a + pg) * kPage + 4 * c + i;
           const float v = s[pg][rb][i] * f16x2_half(kw[pg][i >> 1], i & 1);
-          x[j] = (!EDGE || (pg < npg && pos <= lim[rb])) ? v : -INFINITY;
+          x[j] = (!EDGE || (pg < npg && key_visible(pos, ctx, valid_end, vis[rb]))) ? v : -INFINITY;
           t = fmaxf(t, x[j]);
         }
         const float xm = xrow32_max(xrow16_max(t));
@@ -1108,7 +1124,7 @@ struct MfmaStep {
         for (int i = 0; i < 4; ++i) {
           const int pos = (a + pg) * kPage + 4 * c + i;
           const float v = s[pg][rb][i] * scale_log2;
-          x[rb][pg][i] = (!EDGE || (pg < npg && pos <= lim[rb])) ? v : -INFINITY;
+          x[rb][pg][i] = (!EDGE || (pg < npg && key_visible(pos, ctx, valid_end, vis[rb]))) ? v : -INFINITY;
           t = fmaxf(t, x[rb][pg][i]);
         }
       }
@@ -1589,11 +1605,12 @@ static hipError_t attn_launch(const AttnParams& p, bool mfma, hipStream_t st) {
 }
 
 hipError_t launch_verify_attn(const sva_batch* batch, const void* q, int q_dtype, int Hq,
-                              const sva_paged_kv* kv, float softmax_scale, void* out,
-                              int out_dtype, int path, const AttnPlan& plan, void* workspace,
-                              hipStream_t st) {
+                              const sva_paged_kv* kv, const uint32_t* draft_mask,
+                              float softmax_scale, void* out, int out_dtype, int path,
+                              const AttnPlan& plan, void* workspace, hipStream_t st) {
   AttnParams p;
   p.q = q;
+  p.draft_mask = draft_mask;
   p.k = kv->k;
   p.v = kv->v;
   p.k_scale = static_cast<const uint16_t*>(kv->k_scale);

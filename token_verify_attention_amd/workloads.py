@@ -23,6 +23,17 @@ for are not available, and none of their items are reproduced):
 * ``ragged``      B=64, S_b ~ U[256, 16384], k_b ~ U{1..8}, Hq=32, Hkv=8,
                   d=128, bf16; acceptance logits [sum(k_b+1), 128256] ~ N(0,1),
                   drafts agree with the target argmax with probability 0.8.
+* ``tree8b``      the 8B GQA shape with a token tree of 8 nodes per sequence
+                  instead of a chain (B=32, Hq=32, Hkv=8, d=128, S=4096, bf16);
+                  acceptance logits [sum(k_b+1), 128256], node tokens agree
+                  with the target argmax at their parent with probability 0.8.
+
+Token trees (``make_tree``): node i's parent is node i-1 with probability 1/2,
+else uniform over {-1, 0, .., i-2} (-1: a child of the last committed token),
+so trees mix deep chains and side branches the way dynamic drafters build
+them.  ``make_tree_logits`` plants each row's maximum as for chains and gives
+node i the planted token of its parent's row (row 0 for the root) with the
+workload's agreement probability, else a different token.
 
 Every workload uses 16-token pages laid out as [P, Hkv, 16, d] with a random
 page permutation; unused block-table entries are -1.  The pool holds exactly
@@ -68,7 +79,11 @@ WORKLOADS = {
     "gqa70b_int8": Workload("gqa70b_int8", 16, 64, 8, 128, 8192, 4, "int8", "bf16", 0.5, ident=4),
     "ragged": Workload("ragged", 64, 32, 8, 128, (256, 16384), (1, 8), "bf16", "bf16",
                        1.0, 128256, 0.8, ident=5),
+    "tree8b": Workload("tree8b", 32, 32, 8, 128, 4096, 8, "bf16", "bf16", 1.0, 128256, 0.8,
+                       append=True, ident=6),
 }
+
+TREE_WORKLOADS = ("tree8b",)
 
 TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}
 
@@ -202,6 +217,47 @@ def make_logits(w: Workload, k_h, device="cpu", seed_offset=0):
     seq_of = torch.repeat_interleave(torch.arange(B, device=device),
                                      torch.as_tensor(k_h, dtype=torch.int64, device=device))
     draft = planted[torch.arange(T, device=device) + seq_of]
+    if T:
+        miss = torch.rand(T, generator=g, device=device) >= w.match_p
+        shift = 1 + torch.randint(0, V - 1, (T,), generator=g, device=device, dtype=torch.int64)
+        draft = torch.where(miss, (draft + shift) % V, draft)
+    return dict(logits=logits, draft_ids=draft.to(torch.int32), planted=planted)
+
+
+def make_tree(k_h, device="cpu", seed=0, p_chain=0.5):
+    """Parent arrays of one token tree per sequence, concatenated: int32 [T]."""
+    g = _gen("cpu", 4000 + seed)
+    out = []
+    for k in k_h:
+        for i in range(k):
+            u = float(torch.rand((), generator=g))
+            if i > 0 and u < p_chain:
+                out.append(i - 1)
+            else:
+                out.append(int(torch.randint(-1, max(i - 1, 0), (), generator=g)) if i > 1 else -1)
+    return torch.tensor(out, dtype=torch.int32, device=device)
+
+
+def make_tree_logits(w: Workload, k_h, parents, device="cpu", seed_offset=0):
+    """Tree acceptance inputs: logits [sum(k_b+1), V] with planted row maxima
+    and node tokens that copy the planted token of their parent's row with
+    probability ``w.match_p`` (else a different token)."""
+    g = _gen(device, 5000 + w.ident + 97 * seed_offset)
+    B = len(k_h)
+    rows = sum(k_h) + B
+    V = w.vocab
+    planted = torch.randint(0, V, (rows,), generator=g, device=device, dtype=torch.int64)
+    logits = planted_rows(rows, V, planted, g, device)
+    T = sum(k_h)
+    seq_of = torch.repeat_interleave(torch.arange(B, device=device),
+                                     torch.as_tensor(k_h, dtype=torch.int64, device=device))
+    starts = torch.zeros(B, dtype=torch.int64, device=device)
+    if B:
+        starts[1:] = torch.cumsum(torch.as_tensor(k_h, dtype=torch.int64, device=device), 0)[:-1]
+    par = parents.to(device=device, dtype=torch.int64)
+    # row of the parent: sequence row base (start + b) + 1 + parent
+    parent_row = starts[seq_of] + seq_of + 1 + par if T else par
+    draft = planted[parent_row] if T else planted[:0]
     if T:
         miss = torch.rand(T, generator=g, device=device) >= w.match_p
         shift = 1 + torch.randint(0, V - 1, (T,), generator=g, device=device, dtype=torch.int64)
