@@ -31,6 +31,10 @@ What each function follows (pages cited by title and section):
   "Tree based verification": tree attention over each draft's lineage, the
   longest branch the target agrees with, and the surviving branch made
   contiguous in the cache.
+* ``accept_stochastic`` -- the same page, section "How does this drafter
+  maintain the same distribution of the target?": accept with probability
+  min(1, p/q), otherwise sample the residual max(p - q, 0); random numbers
+  are inputs.
 
 Pins (tests marked ``not gpu``): a torch float64 SDPA with an explicit mask and
 a pure-Python triple loop for attention; closed forms (constant V rows,
@@ -39,7 +43,9 @@ permutation, GQA = MHA on repeated KV); a brute-force exact-rational INT8
 quantiser, hand-derived tie cases and the round-trip bound; numpy.argmax and
 constructed tie / NaN / signed-zero rows for acceptance; for trees, a boolean
 transitive closure for the masks, torch SDPA with the tree mask, brute-force
-path enumeration and chain trees reducing to the causal case.  No function here is
+path enumeration and chain trees reducing to the causal case; for stochastic
+acceptance, the page's worked example, the output-distribution identity
+located from the oracle's own decision boundaries, and the greedy limit.  No function here is
 "parity unpinned".
 """
 from .attention import spec_verify_attn
@@ -47,6 +53,7 @@ from .kv_quant import kv_quant_int8, dequant_int8, round_to_bf16
 from .kv_append import kv_append
 from .accept import argmax_rows, accept_prefix
 from .tree import ancestor_masks, accept_tree, commit_path
+from .stochastic import accept_stochastic
 
 __all__ = [
     "spec_verify_attn",
@@ -59,4 +66,5 @@ __all__ = [
     "ancestor_masks",
     "accept_tree",
     "commit_path",
+    "accept_stochastic",
 ]
