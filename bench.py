@@ -4,7 +4,9 @@ One step = one pass of the whole hot path over one synthetic batch:
   kv_append (the k new K/V rows of every sequence; INT8 caches quantise on
   write) -> spec_verify_attn -> accept_prefix (argmax over the vocabulary and
   the longest accepted prefix).  Token-tree workloads (--workload tree8b) run
-  kv_append -> tree_masks -> tree attention -> accept_tree -> kv_commit_path.
+  kv_append -> tree_masks -> tree attention -> accept_tree -> kv_commit_path;
+  --workload ragged_sampled replaces greedy acceptance by stochastic acceptance
+  (rejection sampling over target and drafter logits).
 Default workload: 7B-MHA shape, B=8, Hq=Hkv=32, d=128, S=2048, k=4, bf16 paged
 KV (16-token pages, random page permutation).  That shape names no vocabulary;
 acceptance runs over fp32 logits [B*(k+1), 128256] with drafts agreeing with
@@ -140,8 +142,18 @@ class Inputs:
             self.step_attn = step_attn
         else:
             self.attn = tva.prepare_spec_verify_attn(self.batch, case["q"], self.kv, self.out)
-            self.accept = tva.prepare_accept_prefix(self.batch, case["logits"], case["draft_ids"],
-                                                    self.ids, self.alen, self.nxt)
+            if w.name in wl.SAMPLED_WORKLOADS:
+                case["draft_logits"] = wl.make_draft_logits(case["logits"], case["k_host"],
+                                                            device=dev, seed=w.ident + seed_offset)
+                case["u_accept"], case["u_sample"] = wl.make_uniforms(
+                    case["T"], B, device=dev, seed=w.ident + seed_offset)
+                self.accept = tva.prepare_accept_stochastic(
+                    self.batch, case["logits"], case["draft_logits"], case["draft_ids"],
+                    case["u_accept"], case["u_sample"], self.alen, self.nxt)
+            else:
+                self.accept = tva.prepare_accept_prefix(self.batch, case["logits"],
+                                                        case["draft_ids"], self.ids, self.alen,
+                                                        self.nxt)
             self.step_attn = self.attn
 
 
@@ -176,6 +188,10 @@ def cpu_baseline(wl, w, dev, budget_s):
         case["parents"] = wl.make_tree(case["k_host"], device=dev, seed=w.ident)
         case.update(wl.make_tree_logits(w, case["k_host"], case["parents"], device=dev))
         parents = np_(case["parents"])
+    sampled = w.name in wl.SAMPLED_WORKLOADS
+    if sampled:
+        dlog = np_(wl.make_draft_logits(case["logits"], case["k_host"], device=dev, seed=w.ident))
+        ua, us = (np_(t) for t in wl.make_uniforms(case["T"], case["B"], device=dev, seed=w.ident))
     kp, vp = np_(case["k_pool"]), np_(case["v_pool"])
     bt, ctx, cu = np_(case["block_table"]), np_(case["ctx_lens"]), np_(case["cu_q"])
     qn = np_(case["q"])
@@ -221,6 +237,10 @@ def cpu_baseline(wl, w, dev, budget_s):
                                                    parents[int(cu[b]):int(cu[b + 1])], one)
                 for pool in (kp, vp):
                     oracle.commit_path(pool, bt[b:b + 1], ctx[b:b + 1], one, n, path)
+            elif sampled:
+                q0, q1 = int(cu[b]), int(cu[b + 1])
+                oracle.accept_stochastic(logits[r0:r1], dlog[q0:q1], drafts[q0:q1], one, 1.0,
+                                         ua[q0:q1], us[b:b + 1])
             else:
                 oracle.accept_prefix(logits[r0:r1], drafts[int(cu[b]):int(cu[b + 1])], one)
         t_acc = time.perf_counter() - t0
@@ -340,8 +360,8 @@ def main():
                          f"S={w.ctx}, k={w.k}"
                          f"{' token-tree nodes' if w.name in wl.TREE_WORKLOADS else ''}, "
                          f"{w.kv_dtype} paged KV (16-token pages, random "
-                         f"page permutation); acceptance over fp32 logits "
-                         f"[sum(k_b+1), {w.vocab}]"),
+                         f"page permutation); "
+                         f"{'stochastic acceptance (rejection sampling, temperature 1) over fp32 target logits [sum(k_b+1), %d] and drafter logits [sum(k_b), %d]' % (w.vocab, w.vocab) if w.name in wl.SAMPLED_WORKLOADS else 'acceptance over fp32 logits [sum(k_b+1), %d]' % w.vocab}"),
             "global_batch": w.B, "seq_len": w.ctx if isinstance(w.ctx, int) else list(w.ctx),
             "drafts_per_seq": w.k if isinstance(w.k, int) else list(w.k),
             "parallelism": "single GPU", "input_sets_rotated": nsets,

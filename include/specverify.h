@@ -244,6 +244,41 @@ sva_status sva_accept_tree(const sva_batch *batch, const float *logits, int32_t 
 sva_status sva_kv_commit_path(const sva_batch *batch, const int32_t *accept_len,
                               const int32_t *accept_path, const sva_paged_kv *kv, void *stream);
 
+/* ---- Stochastic acceptance -------------------------------------------------
+ * "Decoding Speculative Decoding from First Principles", section "How does
+ * this drafter maintain the same distribution of the target?": with p the
+ * target's and q the drafter's distribution at a draft position and x the
+ * drafted token, the draft is accepted with probability min(1, p(x)/q(x));
+ * at the first rejection the emitted token is sampled from the residual
+ * max(p - q, 0), renormalised, and the pass stops; the emitted tokens are then
+ * distributed exactly as the target's.  If every draft is accepted the +1
+ * token is sampled from p after the last draft.  p = softmax(target_logits /
+ * temperature), q = softmax(draft_logits / temperature).  The random numbers
+ * are inputs, so the call is deterministic:
+ *   target_logits  device [T + B, V] fp32, rows as for sva_accept_prefix
+ *   draft_logits   device [T, V] fp32: the drafter's logits at each draft
+ *   draft_ids      device [T] int32: the drafted tokens
+ *   u_accept       device [T] fp32 in [0, 1): draft j is accepted iff
+ *                  u_accept[j] < p(x)/q(x) (q(x) = 0 accepts, p(x) = 0 rejects)
+ *   u_sample       device [B] fp32 in [0, 1): the emitted token is the first
+ *                  index whose running sum of weights exceeds u * their total
+ *                  (residual weights after a rejection -- p if the residual is
+ *                  zero everywhere -- else p of the row after the last draft)
+ *   accept_len     device [B] int32 (written): accepted drafts n_b
+ *   next_token     device [B] int32 (written): the sampled token
+ *   workspace      >= sva_accept_stochastic_workspace_bytes(batch, V) bytes,
+ *                  16-byte aligned, no initialisation needed
+ * Logits must not be NaN (-inf marks a token of probability zero).  Decisions
+ * use fp32 arithmetic: where u lies within rounding of p/q, or u_sample * total
+ * within rounding of a running-sum boundary, either neighbouring outcome may
+ * be returned. */
+size_t sva_accept_stochastic_workspace_bytes(const sva_batch *batch, int32_t V);
+sva_status sva_accept_stochastic(const sva_batch *batch, const float *target_logits,
+                                 const float *draft_logits, int32_t V, float temperature,
+                                 const int32_t *draft_ids, const float *u_accept,
+                                 const float *u_sample, int32_t *accept_len, int32_t *next_token,
+                                 void *workspace, size_t workspace_bytes, void *stream);
+
 const char *sva_status_string(sva_status status);
 const char *sva_last_error(void);
 

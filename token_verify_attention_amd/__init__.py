@@ -22,7 +22,8 @@ import torch
 __all__ = [
     "load", "SvaError", "Batch", "PagedKV", "kv_quant_int8", "kv_append", "spec_verify_attn",
     "verify_workspace_bytes", "accept_prefix", "accept_workspace_bytes", "LIB_PATH",
-    "tree_masks", "accept_tree", "kv_commit_path",
+    "tree_masks", "accept_tree", "kv_commit_path", "accept_stochastic",
+    "accept_stochastic_workspace_bytes",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "_lib", "libspecverify.so")
@@ -96,6 +97,11 @@ def load():
         lib.sva_accept_tree.argtypes = [vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         lib.sva_kv_commit_path.restype = ctypes.c_int
         lib.sva_kv_commit_path.argtypes = [vp, vp, vp, vp, vp]
+        lib.sva_accept_stochastic_workspace_bytes.restype = sz
+        lib.sva_accept_stochastic_workspace_bytes.argtypes = [vp, i32]
+        lib.sva_accept_stochastic.restype = ctypes.c_int
+        lib.sva_accept_stochastic.argtypes = [vp, vp, vp, i32, ctypes.c_float, vp, vp, vp, vp, vp,
+                                              vp, sz, vp]
         _lib = lib
     return _lib
 
@@ -465,6 +471,63 @@ def kv_commit_path(batch, accept_len, accept_path, kv, stream=None):
         _stream(stream, kv.k.device)))
 
 
+def accept_stochastic_workspace_bytes(batch, V):
+    lib = load()
+    cb = batch._c()
+    return int(lib.sva_accept_stochastic_workspace_bytes(ctypes.byref(cb), int(V)))
+
+
+def _check_stochastic(batch, target_logits, draft_logits, draft_ids, u_accept, u_sample,
+                      accept_len, next_token):
+    for t, n, rows in ((target_logits, "target_logits", batch.total_q + batch.B),
+                       (draft_logits, "draft_logits", batch.total_q)):
+        _need(t, n, 2)
+        if t.dtype != torch.float32:
+            raise TypeError(f"{n} must be float32")
+        if int(t.shape[0]) != rows:
+            raise ValueError(f"{n} has {t.shape[0]} rows, expected {rows}")
+    if target_logits.shape[1] != draft_logits.shape[1]:
+        raise ValueError("target and draft logits must have the same vocabulary")
+    _int32_vec(draft_ids, batch.total_q, "draft_ids")
+    for t, n, want in ((u_accept, "u_accept", batch.total_q), (u_sample, "u_sample", batch.B)):
+        _need(t, n, 1)
+        if t.dtype != torch.float32:
+            raise TypeError(f"{n} must be float32")
+        _shape(t, (want,), n)
+    _int32_vec(accept_len, batch.B, "accept_len")
+    _int32_vec(next_token, batch.B, "next_token")
+    _same_device(target_logits, draft_logits, draft_ids, u_accept, u_sample, accept_len,
+                 next_token, batch.cu_q)
+
+
+def accept_stochastic(batch, target_logits, draft_logits, draft_ids, u_accept, u_sample,
+                      temperature=1.0, accept_len=None, next_token=None, workspace=None,
+                      stream=None):
+    """Lossless stochastic acceptance.  target_logits [T+B, V] and draft_logits
+    [T, V] float32 (p, q = softmax(logits / temperature)), draft_ids [T] int32,
+    uniforms u_accept [T] and u_sample [B] float32 in [0, 1).
+    Returns (accept_len [B], next_token [B])."""
+    lib = load()
+    _need(target_logits, "target_logits", 2)
+    dev = target_logits.device
+    V = int(target_logits.shape[1])
+    if accept_len is None:
+        accept_len = torch.empty(batch.B, dtype=torch.int32, device=dev)
+    if next_token is None:
+        next_token = torch.empty(batch.B, dtype=torch.int32, device=dev)
+    _check_stochastic(batch, target_logits, draft_logits, draft_ids, u_accept, u_sample,
+                      accept_len, next_token)
+    if workspace is None:
+        workspace = torch.empty(max(accept_stochastic_workspace_bytes(batch, V), 256),
+                                dtype=torch.uint8, device=dev)
+    cb = batch._c()
+    _check("sva_accept_stochastic", lib.sva_accept_stochastic(
+        ctypes.byref(cb), _ptr(target_logits), _ptr(draft_logits), V, float(temperature),
+        _ptr(draft_ids), _ptr(u_accept), _ptr(u_sample), _ptr(accept_len), _ptr(next_token),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream, dev)))
+    return accept_len, next_token
+
+
 class _Prepared:
     """A call with every argument marshalled once; calling it only enqueues
     the C entry point on the stream (current stream of the device by default)."""
@@ -568,5 +631,24 @@ def prepare_kv_commit_path(batch, accept_len, accept_path, kv):
                      (cb, ckv, batch, accept_len, accept_path, kv))
 
 
+def prepare_accept_stochastic(batch, target_logits, draft_logits, draft_ids, u_accept, u_sample,
+                              accept_len, next_token, temperature=1.0, workspace=None):
+    lib = load()
+    _check_stochastic(batch, target_logits, draft_logits, draft_ids, u_accept, u_sample,
+                      accept_len, next_token)
+    V = int(target_logits.shape[1])
+    if workspace is None:
+        workspace = torch.empty(max(accept_stochastic_workspace_bytes(batch, V), 256),
+                                dtype=torch.uint8, device=target_logits.device)
+    cb = batch._c()
+    args = (ctypes.byref(cb), _ptr(target_logits), _ptr(draft_logits), V, float(temperature),
+            _ptr(draft_ids), _ptr(u_accept), _ptr(u_sample), _ptr(accept_len), _ptr(next_token),
+            _ptr(workspace), workspace.numel() * workspace.element_size())
+    return _Prepared("sva_accept_stochastic", lib.sva_accept_stochastic, args,
+                     target_logits.device, (cb, batch, target_logits, draft_logits, draft_ids,
+                                            u_accept, u_sample, accept_len, next_token, workspace))
+
+
 __all__ += ["prepare_kv_append", "prepare_spec_verify_attn", "prepare_accept_prefix",
+            "prepare_accept_stochastic",
             "prepare_tree_masks", "prepare_accept_tree", "prepare_kv_commit_path"]

@@ -299,6 +299,39 @@ sva_status sva_accept_tree(const sva_batch* batch, const float* logits, int32_t 
   return e == hipSuccess ? SVA_OK : hip_fail(e, "accept_tree launch");
 }
 
+size_t sva_accept_stochastic_workspace_bytes(const sva_batch* batch, int32_t V) {
+  g_last_error.clear();
+  if (check_batch(batch) != SVA_OK || V < 1) return 0;
+  return sva::plan_sample(batch, V).total_bytes;
+}
+
+sva_status sva_accept_stochastic(const sva_batch* batch, const float* target_logits,
+                                 const float* draft_logits, int32_t V, float temperature,
+                                 const int32_t* draft_ids, const float* u_accept,
+                                 const float* u_sample, int32_t* accept_len, int32_t* next_token,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  if (sva_status s = check_batch(batch)) return s;
+  if (V < 1) return fail(SVA_ERR_INVALID_ARG, "V = %d < 1", V);
+  if (!(temperature > 0.f) || !std::isfinite(temperature))
+    return fail(SVA_ERR_INVALID_ARG, "temperature must be finite and > 0");
+  if (batch->B == 0) return SVA_OK;
+  if (!target_logits || !u_sample || !accept_len || !next_token ||
+      (batch->total_q > 0 && (!draft_logits || !draft_ids || !u_accept)))
+    return fail(SVA_ERR_INVALID_ARG, "NULL pointer");
+  const sva::SamplePlan plan = sva::plan_sample(batch, V);
+  if (!workspace || workspace_bytes < plan.total_bytes)
+    return fail(SVA_ERR_INVALID_ARG, "workspace of %zu bytes < %zu needed", workspace_bytes,
+                plan.total_bytes);
+  if (!aligned16(workspace)) return fail(SVA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  const DeviceInfo* dev;
+  if (sva_status s = current_device(&dev)) return s;
+  hipError_t e = sva::launch_accept_stochastic(batch, target_logits, draft_logits, V, temperature,
+                                               draft_ids, u_accept, u_sample, accept_len,
+                                               next_token, plan, workspace, as_stream(stream));
+  return e == hipSuccess ? SVA_OK : hip_fail(e, "accept_stochastic launch");
+}
+
 sva_status sva_kv_commit_path(const sva_batch* batch, const int32_t* accept_len,
                               const int32_t* accept_path, const sva_paged_kv* kv, void* stream) {
   g_last_error.clear();

@@ -64,4 +64,24 @@ hipError_t launch_kv_commit_path(const sva_batch* batch, const int32_t* accept_l
                                  const int32_t* accept_path, const sva_paged_kv* kv,
                                  hipStream_t st);
 
+// Stochastic acceptance: row statistics over chunks, per-sequence decisions,
+// then inverse-CDF sampling of one row per sequence.  Workspace: chunk
+// statistics of every target and draft row, one record per sequence, and the
+// per-chunk weight sums of the sampled rows.
+struct SamplePlan {
+  int stat_rows;
+  int chunks;
+  int chunk_len;
+  int per;                                  // elements per thread range of a chunk
+  size_t stats_off, rec_off, sums_off, parts_off;
+  size_t total_bytes;
+};
+SamplePlan plan_sample(const sva_batch* batch, int V);
+hipError_t launch_accept_stochastic(const sva_batch* batch, const float* target_logits,
+                                    const float* draft_logits, int V, float temperature,
+                                    const int32_t* draft_ids, const float* u_accept,
+                                    const float* u_sample, int32_t* accept_len,
+                                    int32_t* next_token, const SamplePlan& plan, void* workspace,
+                                    hipStream_t st);
+
 }  // namespace sva

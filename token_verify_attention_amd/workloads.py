@@ -28,6 +28,11 @@ for are not available, and none of their items are reproduced):
                   acceptance logits [sum(k_b+1), 128256], node tokens agree
                   with the target argmax at their parent with probability 0.8.
 
+* ``ragged_sampled`` the ragged serving batch with stochastic acceptance:
+                  drafter logits [T, 128256] = the target row's logits plus
+                  N(0, 0.5^2) noise, temperature 1, uniforms u_accept [T] and
+                  u_sample [B] from U[0, 1).
+
 Token trees (``make_tree``): node i's parent is node i-1 with probability 1/2,
 else uniform over {-1, 0, .., i-2} (-1: a child of the last committed token),
 so trees mix deep chains and side branches the way dynamic drafters build
@@ -81,7 +86,11 @@ WORKLOADS = {
                        1.0, 128256, 0.8, ident=5),
     "tree8b": Workload("tree8b", 32, 32, 8, 128, 4096, 8, "bf16", "bf16", 1.0, 128256, 0.8,
                        append=True, ident=6),
+    "ragged_sampled": Workload("ragged_sampled", 64, 32, 8, 128, (256, 16384), (1, 8), "bf16",
+                               "bf16", 1.0, 128256, 0.8, ident=7),
 }
+
+SAMPLED_WORKLOADS = ("ragged_sampled",)
 
 TREE_WORKLOADS = ("tree8b",)
 
@@ -263,3 +272,26 @@ def make_tree_logits(w: Workload, k_h, parents, device="cpu", seed_offset=0):
         shift = 1 + torch.randint(0, V - 1, (T,), generator=g, device=device, dtype=torch.int64)
         draft = torch.where(miss, (draft + shift) % V, draft)
     return dict(logits=logits, draft_ids=draft.to(torch.int32), planted=planted)
+
+
+def make_draft_logits(logits, k_h, device="cpu", seed=0, noise=0.5):
+    """Drafter logits [T, V]: row j of sequence b is the target's row j
+    (cu_q[b] + b + j) plus N(0, noise^2) noise."""
+    g = _gen(device, 6000 + seed)
+    B = len(k_h)
+    rows = []
+    base = 0
+    for b, k in enumerate(k_h):
+        rows.append(torch.arange(base + b, base + b + k, device=device))
+        base += k
+    idx = torch.cat(rows) if rows else torch.zeros(0, dtype=torch.int64, device=device)
+    out = logits[idx].clone()
+    out.add_(torch.randn(out.shape, generator=g, device=device, dtype=torch.float32), alpha=noise)
+    return out
+
+
+def make_uniforms(T, B, device="cpu", seed=0):
+    """u_accept [T] and u_sample [B] from U[0, 1) (float32)."""
+    g = _gen(device, 7000 + seed)
+    return (torch.rand(T, generator=g, device=device, dtype=torch.float32),
+            torch.rand(B, generator=g, device=device, dtype=torch.float32))
