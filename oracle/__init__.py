@@ -35,6 +35,9 @@ What each function follows (pages cited by title and section):
   maintain the same distribution of the target?": accept with probability
   min(1, p/q), otherwise sample the residual max(p - q, 0); random numbers
   are inputs.
+* ``kvmu_apply`` -- "HeteroReason", KV Cache Management Unit (Fig. 7): the
+  valid / current / step-ahead pointer triplet and its Initialization,
+  Speculation, Accept and Rollback modes, plus a token-level prefix commit.
 
 Pins (tests marked ``not gpu``): a torch float64 SDPA with an explicit mask and
 a pure-Python triple loop for attention; closed forms (constant V rows,
@@ -45,7 +48,8 @@ constructed tie / NaN / signed-zero rows for acceptance; for trees, a boolean
 transitive closure for the masks, torch SDPA with the tree mask, brute-force
 path enumeration and chain trees reducing to the causal case; for stochastic
 acceptance, the page's worked example, the output-distribution identity
-located from the oracle's own decision boundaries, and the greedy limit.  No function here is
+located from the oracle's own decision boundaries, and the greedy limit; for
+the KVMU, the page's mode table and invariants of the state machine.  No function here is
 "parity unpinned".
 """
 from .attention import spec_verify_attn
@@ -54,6 +58,7 @@ from .kv_append import kv_append
 from .accept import argmax_rows, accept_prefix
 from .tree import ancestor_masks, accept_tree, commit_path
 from .stochastic import accept_stochastic
+from .kvmu import kvmu_apply
 
 __all__ = [
     "spec_verify_attn",
@@ -67,4 +72,5 @@ __all__ = [
     "accept_tree",
     "commit_path",
     "accept_stochastic",
+    "kvmu_apply",
 ]
