@@ -279,6 +279,35 @@ sva_status sva_accept_stochastic(const sva_batch *batch, const float *target_log
                                  const float *u_sample, int32_t *accept_len, int32_t *next_token,
                                  void *workspace, size_t workspace_bytes, void *stream);
 
+/* ---- KV-cache pointer management --------------------------------------------
+ * "HeteroReason", KV Cache Management Unit (Fig. 7): each sequence's cache is
+ * tracked by a pointer triplet -- valid (the last verified context boundary),
+ * curr (the step under verification) and ahead (the step-ahead speculation
+ * frontier) -- moved by the controller's modes.  Rejected speculative history
+ * is discarded by moving pointers only.  The Prefix mode is the token-level
+ * form used with the accept calls: the first n_b drafts are kept, the rest
+ * rolled back.  Keeping the triplets on the device lets a verification loop
+ * commit from accept_len without a host round trip. */
+typedef enum {
+  SVA_KVMU_INIT = 0,       /* valid, curr, ahead <- arg                          */
+  SVA_KVMU_SPECULATE = 1,  /* ahead <- ahead + max(arg, 0)                       */
+  SVA_KVMU_ACCEPT = 2,     /* valid <- curr, curr <- ahead                       */
+  SVA_KVMU_ROLLBACK = 3,   /* curr, ahead <- valid                               */
+  SVA_KVMU_PREFIX = 4      /* valid <- min(valid + max(arg, 0), ahead);
+                              curr, ahead <- valid                               */
+} sva_kvmu_mode;
+
+/* Apply one mode to every sequence's triplet.
+ *   mode          device [B] int32 per-sequence modes, or NULL to apply
+ *                 uniform_mode to all (an unknown per-sequence mode leaves that
+ *                 sequence unchanged)
+ *   arg           device [B] int32 (position or count), or NULL for 0
+ *   state         device [B, 3] int32 (valid, curr, ahead), updated in place
+ *   ctx_lens      device [B] int32 or NULL: receives the new valid pointers
+ *                 (the S_b of the next verification step) */
+sva_status sva_kvmu_apply(int32_t B, const int32_t *mode, int32_t uniform_mode,
+                          const int32_t *arg, int32_t *state, int32_t *ctx_lens, void *stream);
+
 const char *sva_status_string(sva_status status);
 const char *sva_last_error(void);
 

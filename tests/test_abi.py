@@ -68,6 +68,9 @@ def test_host_checked_errors_need_no_gpu():
     assert lib.sva_kv_commit_path(None, None, None, None, None) == 1
     assert lib.sva_accept_stochastic(None, None, None, 10, ctypes.c_float(1.0), None, None, None,
                                      None, None, None, 0, None) == 1
+    assert lib.sva_kvmu_apply(-1, None, 0, None, None, None, None) == 1
+    assert lib.sva_kvmu_apply(4, None, 9, None, None, None, None) == 1
+    assert lib.sva_kvmu_apply(0, None, 1, None, None, None, None) == 0
 
 
 def test_batch_and_cache_shape_checks():

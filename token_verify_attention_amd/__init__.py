@@ -23,8 +23,11 @@ __all__ = [
     "load", "SvaError", "Batch", "PagedKV", "kv_quant_int8", "kv_append", "spec_verify_attn",
     "verify_workspace_bytes", "accept_prefix", "accept_workspace_bytes", "LIB_PATH",
     "tree_masks", "accept_tree", "kv_commit_path", "accept_stochastic",
-    "accept_stochastic_workspace_bytes",
+    "accept_stochastic_workspace_bytes", "kvmu_apply", "KVMU_INIT", "KVMU_SPECULATE",
+    "KVMU_ACCEPT", "KVMU_ROLLBACK", "KVMU_PREFIX",
 ]
+
+KVMU_INIT, KVMU_SPECULATE, KVMU_ACCEPT, KVMU_ROLLBACK, KVMU_PREFIX = 0, 1, 2, 3, 4
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "_lib", "libspecverify.so")
 
@@ -97,6 +100,8 @@ def load():
         lib.sva_accept_tree.argtypes = [vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         lib.sva_kv_commit_path.restype = ctypes.c_int
         lib.sva_kv_commit_path.argtypes = [vp, vp, vp, vp, vp]
+        lib.sva_kvmu_apply.restype = ctypes.c_int
+        lib.sva_kvmu_apply.argtypes = [i32, vp, i32, vp, vp, vp, vp]
         lib.sva_accept_stochastic_workspace_bytes.restype = sz
         lib.sva_accept_stochastic_workspace_bytes.argtypes = [vp, i32]
         lib.sva_accept_stochastic.restype = ctypes.c_int
@@ -526,6 +531,31 @@ def accept_stochastic(batch, target_logits, draft_logits, draft_ids, u_accept, u
         _ptr(draft_ids), _ptr(u_accept), _ptr(u_sample), _ptr(accept_len), _ptr(next_token),
         _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream, dev)))
     return accept_len, next_token
+
+
+def kvmu_apply(state, mode, arg=None, ctx_lens=None, stream=None):
+    """Apply KVMU modes to the pointer triplets state [B, 3] int32 (valid,
+    curr, ahead) in place.  mode: one KVMU_* value for every sequence, or a
+    device [B] int32 tensor of per-sequence modes; arg: device [B] int32 or
+    None; ctx_lens: optional device [B] int32 receiving the new valid
+    pointers.  Returns state."""
+    lib = load()
+    _need(state, "state", 2)
+    if state.dtype != torch.int32 or int(state.shape[1]) != 3:
+        raise ValueError("state must be int32 [B, 3]")
+    B = int(state.shape[0])
+    per_seq = isinstance(mode, torch.Tensor)
+    if per_seq:
+        _int32_vec(mode, B, "mode")
+    if arg is not None:
+        _int32_vec(arg, B, "arg")
+    if ctx_lens is not None:
+        _int32_vec(ctx_lens, B, "ctx_lens")
+    _same_device(state, mode if per_seq else None, arg, ctx_lens)
+    _check("sva_kvmu_apply", lib.sva_kvmu_apply(
+        B, _ptr(mode) if per_seq else None, 0 if per_seq else int(mode), _ptr(arg), _ptr(state),
+        _ptr(ctx_lens), _stream(stream, state.device)))
+    return state
 
 
 class _Prepared:

@@ -332,6 +332,20 @@ sva_status sva_accept_stochastic(const sva_batch* batch, const float* target_log
   return e == hipSuccess ? SVA_OK : hip_fail(e, "accept_stochastic launch");
 }
 
+sva_status sva_kvmu_apply(int32_t B, const int32_t* mode, int32_t uniform_mode,
+                          const int32_t* arg, int32_t* state, int32_t* ctx_lens, void* stream) {
+  g_last_error.clear();
+  if (B < 0) return fail(SVA_ERR_INVALID_ARG, "B = %d < 0", B);
+  if (!mode && (uniform_mode < SVA_KVMU_INIT || uniform_mode > SVA_KVMU_PREFIX))
+    return fail(SVA_ERR_INVALID_ARG, "uniform_mode = %d", uniform_mode);
+  if (B == 0) return SVA_OK;
+  if (!state) return fail(SVA_ERR_INVALID_ARG, "state is NULL");
+  const DeviceInfo* dev;
+  if (sva_status s = current_device(&dev)) return s;
+  hipError_t e = sva::launch_kvmu(B, mode, uniform_mode, arg, state, ctx_lens, as_stream(stream));
+  return e == hipSuccess ? SVA_OK : hip_fail(e, "kvmu_apply launch");
+}
+
 sva_status sva_kv_commit_path(const sva_batch* batch, const int32_t* accept_len,
                               const int32_t* accept_path, const sva_paged_kv* kv, void* stream) {
   g_last_error.clear();

@@ -84,4 +84,8 @@ hipError_t launch_accept_stochastic(const sva_batch* batch, const float* target_
                                     int32_t* next_token, const SamplePlan& plan, void* workspace,
                                     hipStream_t st);
 
+// KVMU pointer triplets: one thread per sequence applies its mode.
+hipError_t launch_kvmu(int B, const int32_t* mode, int uniform_mode, const int32_t* arg,
+                       int32_t* state, int32_t* ctx_lens, hipStream_t st);
+
 }  // namespace sva
