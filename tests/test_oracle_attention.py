@@ -52,6 +52,8 @@ SHAPES = [
     (3, 8, 2, 16, [40, 0, 16], [5, 2, 4]),
     (2, 6, 3, 32, [31, 33], [2, 6]),
     (3, 4, 1, 8, [15, 16, 1], [1, 0, 7]),
+    # long speculated steps (step-level verification: tens to hundreds of drafts)
+    (2, 7, 1, 16, [64, 3], [96, 40]),
 ]
 
 
