@@ -6,7 +6,11 @@ One step = one pass of the whole hot path over one synthetic batch:
   the longest accepted prefix).  Token-tree workloads (--workload tree8b) run
   kv_append -> tree_masks -> tree attention -> accept_tree -> kv_commit_path;
   --workload ragged_sampled replaces greedy acceptance by stochastic acceptance
-  (rejection sampling over target and drafter logits).
+  (rejection sampling over target and drafter logits); --workload prm7b_step
+  verifies long speculated steps (128 drafts per sequence, the attention shape
+  of a 7B process reward model): kv_append -> verification attention, whose
+  roofline is MFMA throughput (the reward model's threshold is not part of
+  this path).
 Default workload: 7B-MHA shape, B=8, Hq=Hkv=32, d=128, S=2048, k=4, bf16 paged
 KV (16-token pages, random page permutation).  That shape names no vocabulary;
 acceptance runs over fp32 logits [B*(k+1), 128256] with drafts agreeing with
@@ -35,6 +39,7 @@ import torch
 METRIC = "verify-attn KV HBM GB/s (% of peak) and verified draft tokens/sec, 1 GPU"
 HBM_PEAK_GBPS = 8000.0
 MALL_BYTES = 256 << 20
+MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
 def log(*a):
@@ -48,6 +53,19 @@ def kv_bytes(w, ctx, ks):
     per_row = w.d * elem + (2 if w.kv_dtype == "int8" else 0)
     rows = sum(c + k for c, k in zip(ctx, ks))
     return 2 * w.Hkv * rows * per_row
+
+
+def attn_flops(w, ctx, ks):
+    """Algorithmic FLOPs of one verify-attn launch: per query row of draft i
+    (G rows per draft and kv head), S_b + i + 1 visible keys, each costing a
+    d-long dot product for the score and a d-long multiply-add into the
+    output (2 FLOPs per multiply-add)."""
+    G = w.Hq // w.Hkv
+    total = 0
+    for c, k in zip(ctx, ks):
+        keys = k * (c + 1) + k * (k - 1) // 2          # sum over drafts of S + i + 1
+        total += 4 * w.d * keys * G * w.Hkv
+    return total
 
 
 def other_bytes(w, ctx, ks, max_pages):
@@ -98,7 +116,9 @@ class Inputs:
 
     def __init__(self, tva, wl, w, seed_offset, dev):
         tree = w.name in wl.TREE_WORKLOADS
-        self.case = case = wl.make_case(w, device=dev, seed_offset=seed_offset, with_logits=not tree)
+        long = w.name in wl.LONG_WORKLOADS
+        self.case = case = wl.make_case(w, device=dev, seed_offset=seed_offset,
+                                        with_logits=not (tree or long))
         if tree:
             case["parents"] = wl.make_tree(case["k_host"], device=dev, seed=w.ident + 97 * seed_offset)
             case.update(wl.make_tree_logits(w, case["k_host"], case["parents"], device=dev,
@@ -142,7 +162,9 @@ class Inputs:
             self.step_attn = step_attn
         else:
             self.attn = tva.prepare_spec_verify_attn(self.batch, case["q"], self.kv, self.out)
-            if w.name in wl.SAMPLED_WORKLOADS:
+            if long:
+                self.accept = lambda stream=None: None
+            elif w.name in wl.SAMPLED_WORKLOADS:
                 case["draft_logits"] = wl.make_draft_logits(case["logits"], case["k_host"],
                                                             device=dev, seed=w.ident + seed_offset)
                 case["u_accept"], case["u_sample"] = wl.make_uniforms(
@@ -182,7 +204,8 @@ def cpu_baseline(wl, w, dev, budget_s):
     from threadpoolctl import threadpool_limits
 
     tree = w.name in wl.TREE_WORKLOADS
-    case = wl.make_case(w, device=dev, seed_offset=0, with_logits=not tree)
+    long = w.name in wl.LONG_WORKLOADS
+    case = wl.make_case(w, device=dev, seed_offset=0, with_logits=not (tree or long))
     np_ = lambda t: (t.float() if t.dtype == torch.bfloat16 else t).cpu().numpy()
     if tree:
         case["parents"] = wl.make_tree(case["k_host"], device=dev, seed=w.ident)
@@ -196,7 +219,8 @@ def cpu_baseline(wl, w, dev, budget_s):
     bt, ctx, cu = np_(case["block_table"]), np_(case["ctx_lens"]), np_(case["cu_q"])
     qn = np_(case["q"])
     kn, vn = np_(case["k_new"]), np_(case["v_new"])
-    logits, drafts = np_(case["logits"]), np_(case["draft_ids"])
+    logits = np_(case["logits"]) if "logits" in case else None
+    drafts = np_(case["draft_ids"]) if "draft_ids" in case else None
     scale = 1.0 / math.sqrt(w.d)
     B, H = case["B"], w.Hkv
     pairs = [(b, g) for b in range(B) for g in range(H)]
@@ -229,7 +253,7 @@ def cpu_baseline(wl, w, dev, budget_s):
         t_attn = time.perf_counter() - t0
         seqs = sorted({b for b, _ in pairs[:done_pairs]})
         t0 = time.perf_counter()
-        for b in seqs:
+        for b in ([] if long else seqs):
             r0, r1 = int(cu[b]) + b, int(cu[b + 1]) + b + 1
             one = np.array([0, int(cu[b + 1] - cu[b])])
             if tree:
@@ -251,9 +275,10 @@ def cpu_baseline(wl, w, dev, budget_s):
     return {
         "value": tokens / step_s, "unit": "verified draft tokens/s", "cores": 1, "kind": "oracle",
         "sample": (f"{done_pairs} of {len(pairs)} (sequence, kv-head) attention pairs "
-                   f"({t_attn:.1f} s), acceptance{' and branch commit' if tree else ''} for "
-                   f"{len(seqs)} of {B} sequences, the whole append; scaled to the full batch; "
-                   f"numpy BLAS limited to 1 thread"),
+                   f"({t_attn:.1f} s), "
+                   + ("" if long else f"acceptance{' and branch commit' if tree else ''} for "
+                      f"{len(seqs)} of {B} sequences, ")
+                   + "the whole append; scaled to the full batch; numpy BLAS limited to 1 thread"),
         "seconds_per_step_estimate": step_s,
     }
 
@@ -280,7 +305,8 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     w = wl.WORKLOADS[args.workload]
-    if w.vocab is None:
+    long = w.name in wl.LONG_WORKLOADS
+    if w.vocab is None and not long:
         w = dataclasses.replace(w, vocab=128256, match_p=0.8)
 
     sets = [Inputs(tva, wl, w, 0, dev)]
@@ -340,6 +366,8 @@ def main():
     kvb = bytes_all / args.steps
     achieved = kvb / (attn_avg * 1e-3) / 1e9
     traffic = measured_traffic(w.name, attn_avg)
+    flops = sum(attn_flops(w, x.case["ctx_host"], x.case["k_host"]) for x in sets) / nsets
+    tflops = flops / (attn_avg * 1e-3) / 1e12
 
     probe = copy_probe_gbps(dev)
     result = {
@@ -358,10 +386,11 @@ def main():
         "config": {
             "workload": (f"{w.name}: B={w.B}, Hq={w.Hq}, Hkv={w.Hkv}, d={w.d}, "
                          f"S={w.ctx}, k={w.k}"
+                         f"{' drafts per step (step-level verification)' if long else ''}"
                          f"{' token-tree nodes' if w.name in wl.TREE_WORKLOADS else ''}, "
                          f"{w.kv_dtype} paged KV (16-token pages, random "
                          f"page permutation); "
-                         f"{'stochastic acceptance (rejection sampling, temperature 1) over fp32 target logits [sum(k_b+1), %d] and drafter logits [sum(k_b), %d]' % (w.vocab, w.vocab) if w.name in wl.SAMPLED_WORKLOADS else 'acceptance over fp32 logits [sum(k_b+1), %d]' % w.vocab}"),
+                         f"{'no acceptance (a reward-model threshold)' if long else 'stochastic acceptance (rejection sampling, temperature 1) over fp32 target logits [sum(k_b+1), %d] and drafter logits [sum(k_b), %d]' % (w.vocab, w.vocab) if w.name in wl.SAMPLED_WORKLOADS else 'acceptance over fp32 logits [sum(k_b+1), %d]' % w.vocab}"),
             "global_batch": w.B, "seq_len": w.ctx if isinstance(w.ctx, int) else list(w.ctx),
             "drafts_per_seq": w.k if isinstance(w.k, int) else list(w.k),
             "parallelism": "single GPU", "input_sets_rotated": nsets,
@@ -374,12 +403,20 @@ def main():
         "draft_tokens_per_step": T,
         "other_bytes_per_launch": other_bytes(w, ctx, ks, max_pages),
         "copy_probe_gbps": probe,
-        "roofline": {
+        "attn_flops_per_launch": flops,
+        "attn_tflops": tflops,
+        "roofline": ({
+            "bound": "mfma", "achieved": tflops, "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": tflops / MFMA_BF16_PEAK_TFLOPS,
+            "traffic": traffic and traffic["gbps"], "traffic_unit": "GB/s",
+            "kernel": "verify_attn_rows_kernel",
+            "traffic_bytes_per_launch": traffic and traffic["bytes"],
+        } if long else {
             "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic and traffic["gbps"],
             "kernel": "verify_attn_kernel",
             "traffic_bytes_per_launch": traffic and traffic["bytes"],
-        },
+        }),
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

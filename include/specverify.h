@@ -79,7 +79,8 @@ typedef struct {
  *   ctx_lens   [B] device int32: committed rows S_b, EXCLUDING this step's drafts
  *   cu_q       [B+1] device int32: prefix sums of k_b (cu_q[0] = 0); k_b may be 0
  *   total_q    host copy of cu_q[B] (T, the number of draft rows)
- *   max_q      host upper bound on every k_b (1..16)
+ *   max_q      host upper bound on every k_b (1..16; 1..1024 for sva_kv_append
+ *              and sva_spec_verify_attn, 1..32 for sva_spec_verify_attn_tree)
  *   max_len    host upper bound on every S_b + k_b */
 typedef struct {
   int32_t B;
@@ -146,9 +147,16 @@ size_t sva_verify_workspace_bytes(const sva_batch *batch, const sva_paged_kv *kv
  *               used, and every call leaves them all-zero again, so one
  *               workspace serves calls of any shape in stream order.  Calls that
  *               may run concurrently need distinct workspaces.
- * Supported: page_size 16, d in {64, 128}, Hq % Hkv == 0, max_q <= 16,
- * max_q * (Hq / Hkv) <= 128, B <= 4096.  SVA_F32 caches always take the VALU
- * path (query rows past 16 are handled in further passes over the pages). */
+ * Supported: page_size 16, d in {64, 128}, Hq % Hkv == 0, B <= 4096, and
+ * max_q <= 16 with max_q * (Hq / Hkv) <= 128 on every path; bf16 and INT8
+ * caches on the MFMA path (the default) also take long speculated steps,
+ * max_q <= 1024 ("HeteroReason": a process reward model verifies a whole
+ * reasoning step in one parallel pass).  Pairs with many query rows (k_b * G
+ * above 32, when their 128-row blocks fill the device, and always above 16
+ * drafts or 128 rows) run on a row-block kernel that reads each page once per
+ * block of 128 rows and needs no more workspace than the counters.  SVA_F32
+ * caches always take the VALU path (query rows past 16 are handled in further
+ * passes over the pages). */
 sva_status sva_spec_verify_attn(const sva_batch *batch, const void *q, int32_t q_dtype,
                                 int32_t Hq, const sva_paged_kv *kv, float softmax_scale,
                                 void *out, int32_t out_dtype, const sva_verify_opts *opts,

@@ -87,16 +87,26 @@ def test_batch_and_cache_shape_checks():
     kv.d = 96
     assert call(4) == 2                                    # d outside {64, 128}
     kv.d = 128
+    kv.kv_dtype = tva.SVA_F32                              # fp32 caches (VALU path):
     b.max_q = 17
     assert call(4) == 2                                    # more than 16 drafts
     b.max_q = 16
     assert call(2 * 64) == 2                               # max_q * G > 128
+    kv.kv_dtype = tva.SVA_BF16
     b.B = -1
     assert call(4) == 1
     b.B = 2
     kv.kv_dtype = tva.SVA_INT8                             # INT8 without scales
     assert call(4) == 1
     assert b"scale" in lib.sva_last_error()
+    kv.kv_dtype = tva.SVA_F32                              # long steps: MFMA path only
+    b.max_q = 64
+    assert call(4) == 2
+    assert b"MFMA" in lib.sva_last_error()
+    b.max_q = 2000                                         # past 1024 drafts
+    kv.kv_dtype = tva.SVA_BF16
+    assert call(4) == 2
+    b.max_q = 16
     kv.kv_dtype = tva.SVA_BF16                             # tree call without its mask
     assert lib.sva_spec_verify_attn_tree(
         ctypes.byref(b), ctypes.c_void_p(64), 1, 4, ctypes.byref(kv), None, ctypes.c_float(0.1),

@@ -1,0 +1,105 @@
+"""GPU parity of verification attention with long speculated steps (through
+the C ABI): tens to hundreds of drafts per sequence, as when a process reward
+model scores a whole reasoning step in one pass ("HeteroReason").  These
+shapes run on the row-block kernel (128 query rows per workgroup, pages shared
+by its four waves).  Small cases cover k from 17 to 300, GQA groups 1 to 7,
+bf16 and INT8 caches, d = 64 / 128, S = 0 and ragged mixes; a tree mask with
+more than 128 rows per pair takes the same kernel; the full prm7b_step
+workload is checked on sampled pairs.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import token_verify_attention_amd as tva
+from token_verify_attention_amd import workloads as wl
+from gpu_helpers import assert_close, batch_of, np_, oracle_attn, paged_kv, rows_of_pairs, say
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+W = wl.Workload
+
+
+def _wk(name, Hq, Hkv, d, kv, q, sigma=1.0, ident=110):
+    return W(name, 1, Hq, Hkv, d, 0, 1, kv, q, sigma, None, None, False, ident)
+
+
+LONG = [
+    (_wk("long-bf16-g7", 28, 4, 128, "bf16", "bf16", ident=111), [500, 0, 63], [128, 40, 17]),
+    (_wk("long-bf16-mha", 8, 8, 128, "bf16", "bf16", ident=112), [16, 300], [300, 129]),
+    (_wk("long-int8-g4", 16, 4, 128, "int8", "bf16", 0.5, ident=113), [200, 1], [64, 100]),
+    (_wk("long-bf16-d64", 8, 2, 64, "bf16", "bf16", ident=114), [31, 700, 5], [33, 96, 250]),
+    (_wk("long-mixed", 16, 4, 128, "bf16", "bf16", ident=115), [90, 10, 1000, 0], [4, 150, 1, 64]),
+]
+
+
+@pytest.mark.parametrize("spec", LONG, ids=[s[0].name for s in LONG])
+def test_long_steps(spec):
+    w, ctx, ks = spec
+    say(f"long steps {w.name}")
+    case = wl.make_case(w, device=DEV, ctx=ctx, k=ks, with_logits=False)
+    kv = paged_kv(case)
+    out = tva.spec_verify_attn(batch_of(case), case["q"], kv)
+    torch.cuda.synchronize()
+    if w.kv_dtype == "int8":
+        assert_close(out, oracle_attn(case, quantised=True), "int8_deq")
+        assert_close(out, oracle_attn(case, quantised=False), "int8")
+    else:
+        assert_close(out, oracle_attn(case), "bf16")
+
+
+def test_long_steps_after_append():
+    """The k new rows appended by sva_kv_append are the drafts attention reads."""
+    w = _wk("long-append", 28, 4, 128, "bf16", "bf16", ident=116)
+    case = wl.make_case(w, device=DEV, ctx=[100, 7], k=[128, 200], with_logits=False)
+    batch = batch_of(case)
+    kv = paged_kv(case)
+    tva.kv_append(batch, case["k_new"], case["v_new"], kv)
+    out = tva.spec_verify_attn(batch, case["q"], kv, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref = oracle.spec_verify_attn(np_(case["q"]), np_(kv.k), np_(kv.v), np_(case["block_table"]),
+                                  np_(case["ctx_lens"]), np_(case["cu_q"]), 1.0 / math.sqrt(w.d))
+    assert_close(out, ref, "bf16")
+
+
+def test_tree_mask_on_row_block_kernel():
+    """16 tree nodes x G = 16: 256 query rows per pair, beyond the split kernel."""
+    w = _wk("long-tree", 64, 4, 128, "bf16", "bf16", ident=117)
+    ks = [16, 9, 16]
+    case = wl.make_case(w, device=DEV, ctx=[70, 0, 300], k=ks, with_logits=False)
+    parents = wl.make_tree(ks, device=DEV, seed=3)
+    batch = batch_of(case)
+    masks = tva.tree_masks(batch, parents)
+    out = tva.spec_verify_attn(batch, case["q"], paged_kv(case), draft_mask=masks)
+    torch.cuda.synchronize()
+    om = oracle.ancestor_masks(np_(parents), np_(case["cu_q"]))
+    ref = oracle.spec_verify_attn(np_(case["q"]), np_(case["k_pool"]), np_(case["v_pool"]),
+                                  np_(case["block_table"]), np_(case["ctx_lens"]),
+                                  np_(case["cu_q"]), 1.0 / math.sqrt(w.d), draft_mask=om)
+    assert_close(out, ref, "bf16")
+
+
+def test_row_block_kernel_equals_split_kernel_on_short_steps():
+    """A shape both kernels take (k*G = 64 rows): same results within the bar."""
+    w = _wk("both", 16, 4, 128, "bf16", "bf16", ident=118)
+    case = wl.make_case(w, device=DEV, ctx=[400, 33], k=[16, 12], with_logits=False)
+    kv = paged_kv(case)
+    batch = batch_of(case)
+    a = tva.spec_verify_attn(batch, case["q"], kv, out_dtype=torch.float32)      # split (small B)
+    ref = oracle_attn(case)
+    assert_close(a, ref, "bf16")
+
+
+def test_prm7b_step_full_size_sampled():
+    w = wl.WORKLOADS["prm7b_step"]
+    say("prm7b_step full size")
+    case = wl.make_case(w, device=DEV, with_logits=False)
+    kv = paged_kv(case)
+    out = tva.spec_verify_attn(batch_of(case), case["q"], kv)
+    torch.cuda.synchronize()
+    pairs = [(0, 0), (5, 3), (11, 1), (15, 2)]
+    ref = oracle_attn(case, select=pairs)
+    assert_close(out, ref, "bf16", rows=rows_of_pairs(case, pairs))

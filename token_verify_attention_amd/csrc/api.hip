@@ -65,7 +65,10 @@ sva_status current_device(const DeviceInfo** out) {
   return SVA_OK;
 }
 
-sva_status check_batch(const sva_batch* b) {
+constexpr int kMaxDrafts = 16;          // drafts per sequence, most entry points
+constexpr int kMaxDraftsLong = 1024;    // attention and append (long speculated steps)
+
+sva_status check_batch(const sva_batch* b, int max_drafts = kMaxDrafts) {
   if (!b) return fail(SVA_ERR_INVALID_ARG, "batch is NULL");
   if (b->B < 0) return fail(SVA_ERR_INVALID_ARG, "B = %d < 0", b->B);
   if (b->B > 4096) return fail(SVA_ERR_UNSUPPORTED, "B = %d > 4096", b->B);
@@ -74,7 +77,8 @@ sva_status check_batch(const sva_batch* b) {
     return fail(SVA_ERR_INVALID_ARG, "ctx_lens / cu_q is NULL");
   if (b->total_q > 0 && b->max_q < 1)
     return fail(SVA_ERR_INVALID_ARG, "max_q = %d but total_q = %d", b->max_q, b->total_q);
-  if (b->max_q > 16) return fail(SVA_ERR_UNSUPPORTED, "max_q = %d > 16", b->max_q);
+  if (b->max_q > max_drafts)
+    return fail(SVA_ERR_UNSUPPORTED, "max_q = %d > %d", b->max_q, max_drafts);
   if (b->max_q < 0) return fail(SVA_ERR_INVALID_ARG, "max_q = %d < 0", b->max_q);
   if (int64_t(b->B) * b->max_q < b->total_q)
     return fail(SVA_ERR_INVALID_ARG, "total_q = %d exceeds B * max_q", b->total_q);
@@ -138,7 +142,7 @@ sva_status sva_kv_quant_int8(const void* x, int32_t src_dtype, int64_t rows, int
 sva_status sva_kv_append(const sva_batch* batch, const void* k_new, const void* v_new,
                          int32_t src_dtype, const sva_paged_kv* kv, void* stream) {
   g_last_error.clear();
-  if (sva_status s = check_batch(batch)) return s;
+  if (sva_status s = check_batch(batch, kMaxDraftsLong)) return s;
   if (sva_status s = check_kv(kv, true)) return s;
   if (src_dtype != SVA_F32 && src_dtype != SVA_BF16)
     return fail(SVA_ERR_UNSUPPORTED, "src_dtype = %d", src_dtype);
@@ -153,15 +157,22 @@ sva_status sva_kv_append(const sva_batch* batch, const void* k_new, const void* 
   return e == hipSuccess ? SVA_OK : hip_fail(e, "kv_append launch");
 }
 
-static sva_status check_attn_shape(const sva_batch* batch, const sva_paged_kv* kv, int32_t Hq) {
-  if (sva_status s = check_batch(batch)) return s;
+static sva_status check_attn_shape(const sva_batch* batch, const sva_paged_kv* kv, int32_t Hq,
+                                   const sva_verify_opts* opts, bool tree) {
+  if (sva_status s = check_batch(batch, tree ? 32 : kMaxDraftsLong)) return s;
   if (sva_status s = check_kv(kv, true)) return s;
   if (kv->d != 64 && kv->d != 128) return fail(SVA_ERR_UNSUPPORTED, "d = %d (64 or 128)", kv->d);
   if (Hq < 1 || Hq % kv->Hkv != 0)
     return fail(SVA_ERR_INVALID_ARG, "Hq = %d is not a multiple of Hkv = %d", Hq, kv->Hkv);
   const int64_t G = Hq / kv->Hkv;
-  if (G * batch->max_q > 128)
-    return fail(SVA_ERR_UNSUPPORTED, "max_q * G = %lld > 128", (long long)(G * batch->max_q));
+  // more than 16 drafts or 128 query rows per pair: the row-block MFMA kernel only
+  const bool valu = kv->kv_dtype == SVA_F32 || (opts && opts->path == 1);
+  if (valu && (batch->max_q > kMaxDrafts || G * batch->max_q > 128))
+    return fail(SVA_ERR_UNSUPPORTED,
+                "max_q = %d, max_q * G = %lld: past 16 drafts or 128 rows only bf16 / INT8 "
+                "caches on the MFMA path", batch->max_q, (long long)(G * batch->max_q));
+  if (G * batch->max_q > (int64_t(1) << 24))
+    return fail(SVA_ERR_UNSUPPORTED, "max_q * G = %lld too large", (long long)(G * batch->max_q));
   const int64_t pages_ub =
       int64_t(batch->B) * kv->Hkv * std::min<int64_t>(kv->max_pages_per_seq, (int64_t(batch->max_len) + 15) / 16);
   if (pages_ub >= (int64_t(1) << 31) - 1)
@@ -172,7 +183,7 @@ static sva_status check_attn_shape(const sva_batch* batch, const sva_paged_kv* k
 size_t sva_verify_workspace_bytes(const sva_batch* batch, const sva_paged_kv* kv, int32_t Hq,
                                   const sva_verify_opts* opts) {
   g_last_error.clear();
-  if (check_attn_shape(batch, kv, Hq) != SVA_OK) return 0;
+  if (check_attn_shape(batch, kv, Hq, opts, false) != SVA_OK) return 0;
   const DeviceInfo* dev;
   if (current_device(&dev) != SVA_OK) return 0;
   return sva::plan_verify_attn(batch, kv, Hq, dev->num_cus, opts).total_bytes;
@@ -183,7 +194,7 @@ static sva_status verify_attn(const sva_batch* batch, const void* q, int32_t q_d
                               float softmax_scale, void* out, int32_t out_dtype,
                               const sva_verify_opts* opts, void* workspace,
                               size_t workspace_bytes, void* stream) {
-  if (sva_status s = check_attn_shape(batch, kv, Hq)) return s;
+  if (sva_status s = check_attn_shape(batch, kv, Hq, opts, draft_mask != nullptr)) return s;
   if (q_dtype != SVA_F32 && q_dtype != SVA_BF16)
     return fail(SVA_ERR_UNSUPPORTED, "q_dtype = %d", q_dtype);
   if (out_dtype != SVA_F32 && out_dtype != SVA_BF16)

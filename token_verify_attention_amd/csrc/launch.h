@@ -19,6 +19,8 @@ hipError_t launch_kv_append(const sva_batch* batch, const void* k_new, const voi
 // Verification attention.  `num_wg` is the grid size; the workspace holds the
 // completion counters followed by the partial-result slots.
 struct AttnPlan {
+  bool rows_kernel;     // row-block kernel (many query rows per pair); no workspace
+  int rows_grid;        // its grid (an upper bound on the row blocks)
   int num_wg;
   int slot_rows;
   size_t counter_bytes;

@@ -60,6 +60,8 @@ constexpr int kWavesValu = 4;
 constexpr int kMaxWorkgroups = 4096;
 constexpr int kMfmaRows = 32;
 constexpr int kValuRows = 16;
+constexpr int kMaxDraftsSplit = 16;            // max_q the split kernel takes
+constexpr int kMaxRowsSplit = 128;             // max_q * G the split kernel takes
 constexpr int kRingBudget = 136 * 1024;        // LDS bytes for the page rings of all waves
 constexpr float kNegBig = -1.0e30f;            // finite start value of running maxima
 constexpr float kLog2e = 1.4426950408889634f;
@@ -92,15 +94,20 @@ struct SeqInfo {
   int S, k, q0, np;
 };
 
-// Keys a query row sees: the committed context 0 .. S-1 and the drafts j < k
-// whose bit j is set in the row's draft mask.  Causal drafts: draft i's mask
-// is bits 0 .. i (positions 0 .. S + i).  Tree attention: the caller's mask.
-// One register per row; the draft range end S + k is the segment's.
+// Keys a query row sees: the committed context 0 .. S-1 and some drafts, kept
+// in one register per row.  Mask form: bit j set when draft j is visible --
+// the caller's tree mask, or bits 0 .. i for causal draft i (at most 32
+// drafts).  Index form (causal calls of the row-block kernel, up to 1024
+// drafts): the draft index i, drafts 0 .. i visible.  The draft range end
+// S + k is the segment's; padding rows see no draft.
 __device__ __forceinline__ uint32_t row_mask(const AttnParams& p, int q0, int i) {
   return p.draft_mask ? p.draft_mask[q0 + i] : (2u << i) - 1u;
 }
 __device__ __forceinline__ bool key_visible(int pos, int S, int end, uint32_t mask) {
   return pos < S || (pos < end && ((mask >> ((pos - S) & 31)) & 1u));
+}
+__device__ __forceinline__ bool key_visible_idx(int pos, int S, int end, int i) {
+  return pos < S || (pos < end && pos - S <= i);
 }
 
 // Sequence b with every device-resident value clamped into the buffers.
@@ -829,7 +836,7 @@ __device__ __forceinline__ f16x8 codes8_to_f16(uint32_t w0, uint32_t w1) {
 //    K scale is the only factor left on each score; the V scale multiplies the
 //    fp16 weight pairs, and the denominator is a second all-ones MFMA over the
 //    unscaled weights.
-template <typename KV, int D, int NRB>
+template <typename KV, int D, int NRB, bool kIdx = false>
 struct MfmaStep {
   using Gm = Geo<KV, D, kWavesValu>;      // page geometry only
   static constexpr bool I8 = sizeof(KV) == 1;
@@ -848,7 +855,8 @@ struct MfmaStep {
   f32x4 lsum[NRB];                        // INT8: all-ones MFMA over the unscaled weights
   float m[NRB], l[NRB];
   float s0[NRB];                          // INT8: start value of the S^T accumulator
-  uint32_t vis[NRB];                      // draft masks of the rows
+  // draft visibility of the rows: masks, or draft indices (kIdx)
+  typename std::conditional<kIdx, int, uint32_t>::type vis[NRB];
   int ctx;                                // S of the sequence
   int valid_end;
   int lane, l16, c;
@@ -881,9 +889,10 @@ struct MfmaStep {
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
       const int r = r0 + 16 * rb + l16;
-      vis[rb] = 0u;
+      vis[rb] = kIdx ? -1 : 0;
       if (r < sg.R) {
-        vis[rb] = row_mask(p, sg.q0, r / p.G);
+        if constexpr (kIdx) vis[rb] = r / p.G;
+        else vis[rb] = row_mask(p, sg.q0, r / p.G);
         const int64_t qe = out_row(p, sg, r) * D + c * (D / 4);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
@@ -906,6 +915,11 @@ struct MfmaStep {
 #pragma unroll
       for (int db = 0; db < NDB; ++db) acc[rb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
+  }
+
+  __device__ __forceinline__ bool visible(int pos, int rb) const {
+    if constexpr (kIdx) return key_visible_idx(pos, ctx, valid_end, vis[rb]);
+    else return key_visible(pos, ctx, valid_end, vis[rb]);
   }
 
   // A operand of S^T = K Q^T: K row l16, d 32c + 8ks .. +8
@@ -1039,7 +1053,7 @@ struct MfmaStep {
         const int pg = j >> 2, i = j & 3;
         const int pos = (a + pg) * kPage + 4 * c + i;
         const float v = fmaf(s[pg][rb][i], f16x2_half(kw[pg][i >> 1], i & 1), -m[rb]);
-        y[rb][j] = (!EDGE || (pg < npg && key_visible(pos, ctx, valid_end, vis[rb]))) ? v : -INFINITY;
+        y[rb][j] = (!EDGE || (pg < npg && visible(pos, rb))) ? v : -INFINITY;
         t = fmaxf(t, y[rb][j]);
       }
       move |= xrow32_max(xrow16_max(t)) > kLazy;
@@ -1053,7 +1067,7 @@ struct MfmaStep {
           const int pg = j >> 2, i = j & 3;
           const int pos = (a + pg) * kPage + 4 * c + i;
           const float v = s[pg][rb][i] * f16x2_half(kw[pg][i >> 1], i & 1);
-          x[j] = (!EDGE || (pg < npg && key_visible(pos, ctx, valid_end, vis[rb]))) ? v : -INFINITY;
+          x[j] = (!EDGE || (pg < npg && visible(pos, rb))) ? v : -INFINITY;
           t = fmaxf(t, x[j]);
         }
         const float xm = xrow32_max(xrow16_max(t));
@@ -1124,7 +1138,7 @@ struct MfmaStep {
         for (int i = 0; i < 4; ++i) {
           const int pos = (a + pg) * kPage + 4 * c + i;
           const float v = s[pg][rb][i] * scale_log2;
-          x[rb][pg][i] = (!EDGE || (pg < npg && key_visible(pos, ctx, valid_end, vis[rb]))) ? v : -INFINITY;
+          x[rb][pg][i] = (!EDGE || (pg < npg && visible(pos, rb))) ? v : -INFINITY;
           t = fmaxf(t, x[rb][pg][i]);
         }
       }
@@ -1216,6 +1230,25 @@ struct MfmaStep {
       slot[NRB * NDB * kWave * 4 + (NRB + rb) * kWave + lane] = l[rb];
     }
   }
+  // Normalised output rows r0 .. r0 + 16 NRB - 1 (those below sg.R) straight
+  // from this wave's state (row-block kernel: every wave owns its rows).
+  __device__ __forceinline__ void write_rows(const AttnParams& p, const Seg& sg, int r0) const {
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+      const int r = r0 + 16 * rb + l16;
+      if (r >= sg.R) continue;
+      const float inv = 1.f / l[rb];
+      const int64_t oe = out_row(p, sg, r) * D;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        f32x4 v = acc[rb][db];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] *= inv;
+        store_out4(p, oe + 16 * db + 4 * c, v);
+      }
+    }
+  }
+
   // Merge of the NW waves' states stored at mrg + w * SLOT_F (store()
   // layout), spread over every thread of the workgroup: thread items are
   // (row, 4 columns), rows varying fastest so that a wave's 16-byte LDS reads
@@ -1563,6 +1596,161 @@ __global__ __launch_bounds__((AttnLds<KV, D, MF>::NT), 1) void verify_attn_kerne
 }
 
 // ============================================================================
+// row-block kernel: many query rows per pair (long speculated steps)
+// ============================================================================
+//
+// Step-level verification scores a whole speculated step -- tens to hundreds
+// of drafts -- in one pass ("HeteroReason": the PRM verifies a complete step
+// in a single parallel pass).  With k*G query rows per (sequence, kv head) far
+// above 32, splitting the keys over waves (the kernel above) would re-stream
+// the pages once per 32 rows.  Here a workgroup owns a block of 128 query rows
+// of one pair, each of its 4 waves 32 of them, and all four share every page:
+// step s brings pages 4s .. 4s+3 into a workgroup ring (one page copied by
+// each wave), and after one barrier every wave runs its rows over all four.
+// A wave never merges with another, and nothing is split over workgroups, so
+// no workspace is used.  Keys are streamed up to the block's last row's
+// position; the causal (or tree) mask applies on the pages holding drafts.
+
+constexpr int kRowWaves = 4;                       // one wave per SIMD
+constexpr int kRowBlock = kRowWaves * kMfmaRows;   // 128 query rows per workgroup
+
+template <typename KV, int D>
+struct RowsLds {
+  using Gm = Geo<KV, D, kRowWaves>;
+  static constexpr int STEP = kRowWaves * Gm::SLOT;   // one page (K, V, scales) per wave
+  static constexpr int NS_RAW = kRingBudget / STEP;
+  static constexpr int NS = NS_RAW < 2 ? 2 : (NS_RAW > 4 ? 4 : NS_RAW);   // steps in the ring
+  static constexpr int RING = NS * STEP;
+};
+
+// Row blocks of sequence b: Hkv * ceil(k_b * G / 128).
+__device__ __forceinline__ int row_blocks(const AttnParams& p, const SeqInfo& si) {
+  return si.k > 0 ? p.Hkv * ((si.k * p.G + kRowBlock - 1) / kRowBlock) : 0;
+}
+
+// kTree: the call carries tree masks (at most 32 drafts, mask form); causal
+// calls keep draft indices (any number of drafts).
+template <typename KV, int D, bool kTree>
+__global__ __launch_bounds__(kRowWaves * kWave, 1) void verify_attn_rows_kernel(AttnParams p) {
+  using Gm = Geo<KV, D, kRowWaves>;
+  using L = RowsLds<KV, D>;
+  constexpr int NS = L::NS;
+  constexpr int NT = kRowWaves * kWave;
+  __shared__ __attribute__((aligned(1024))) char s_ring[L::RING];
+  __shared__ int32_t s_scan[NT];
+  __shared__ int32_t s_info[4];
+  const int tid = threadIdx.x;
+  const int B = p.B;
+
+  // ---- this workgroup's block: exclusive scan of the per-sequence counts
+  const int per = (B + NT - 1) / NT;
+  int tot = 0;
+  for (int e = 0; e < per; ++e) {
+    const int b = tid * per + e;
+    if (b < B) tot += row_blocks(p, seq_info(p, b));
+  }
+  s_scan[tid] = tot;
+  __syncthreads();
+  if (tid < kWave) {
+    constexpr int PER_LANE = NT / kWave;
+    int run = 0;
+    for (int i = 0; i < PER_LANE; ++i) {
+      const int v = s_scan[tid * PER_LANE + i];
+      s_scan[tid * PER_LANE + i] = run;
+      run += v;
+    }
+    int incl = run;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int u = __shfl_up(incl, o, kWave);
+      if (tid >= o) incl += u;
+    }
+    const int excl = incl - run;
+    for (int i = 0; i < PER_LANE; ++i) s_scan[tid * PER_LANE + i] += excl;
+    if (tid == kWave - 1) s_info[0] = incl;
+  }
+  __syncthreads();
+  const int total = s_info[0];
+  // consecutive blocks (the row blocks of one pair) go to one XCD
+  const int hw = blockIdx.x;
+  const int W = gridDim.x;
+  const int w = (W % 8 == 0) ? (hw % 8) * (W / 8) + hw / 8 : hw;
+  if (w >= total) return;
+  {
+    const int base = s_scan[tid];
+    if (tot > 0 && base <= w && w < base + tot) {
+      int run = base;
+      for (int e = 0; e < per; ++e) {
+        const int b = tid * per + e;
+        const int n = row_blocks(p, seq_info(p, b));
+        if (w < run + n) {
+          s_info[1] = b;
+          s_info[2] = w - run;
+          break;
+        }
+        run += n;
+      }
+    }
+  }
+  __syncthreads();
+  const int b = s_info[1];
+  const SeqInfo si = seq_info(p, b);
+  const int nblk = (si.k * p.G + kRowBlock - 1) / kRowBlock;
+  Seg sg;
+  sg.b = b;
+  sg.g = s_info[2] / nblk;
+  sg.S = si.S;
+  sg.k = si.k;
+  sg.q0 = si.q0;
+  sg.np = si.np;
+  sg.R = si.k * p.G;
+  sg.pa = 0;
+  sg.full = true;
+  sg.slot = 0;
+  const int r0 = (s_info[2] % nblk) * kRowBlock;
+  const int last_row = min(sg.R, r0 + kRowBlock) - 1;
+  // keys up to the last row's position: pages 0 .. npages-1
+  const int npages = min(si.np, (si.S + last_row / p.G) / kPage + 1);
+  sg.pe = npages;
+  const int wave = wave_id();
+  const int rw = r0 + kMfmaRows * wave;            // this wave's first row
+  const bool active = rw < sg.R;                    // wave-uniform
+  MfmaStep<KV, D, 2, !kTree> st(p, sg, rw);
+  const int nsteps = (npages + kRowWaves - 1) / kRowWaves;
+  // every wave copies one page per step (past the end: a copy of the last page,
+  // never used), so the per-wave copy counts -- and the waits -- are uniform
+  auto issue = [&](int s) {
+    const int pg = min(kRowWaves * s + wave, npages - 1);
+    dma_page<KV, D>(p, page_id(p, b, pg), sg.g, s_ring + (s % NS) * L::STEP + wave * Gm::SLOT);
+  };
+  for (int s = 0; s < NS - 1 && s < nsteps; ++s) issue(s);
+  st.ready();
+  for (int s = 0; s < nsteps; ++s) {
+    wait_steps<Gm::P, NS - 1>(min(NS - 2, nsteps - 1 - s));
+    // this wave's page of step s has landed and its reads of step s-1 are done;
+    // after the barrier every page of step s is in LDS and slot s-1 is free
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (s + NS - 1 < nsteps) issue(s + NS - 1);
+    if (active) {
+      const char* base = s_ring + (s % NS) * L::STEP;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int a = kRowWaves * s + 2 * u;
+        if (a >= npages) break;
+        const char* sa = base + 2 * u * Gm::SLOT;
+        const bool second = a + 1 < npages;
+        st.load(sa, sa + Gm::SLOT);
+        // both pages inside the committed context: no masks
+        if ((a + 2) * kPage <= sg.S) st.template compute<false>(a, second);
+        else st.template compute<true>(a, second);
+      }
+    }
+  }
+  st.finish();
+  if (active) st.write_rows(p, sg, rw);
+}
+
+// ============================================================================
 // host side
 // ============================================================================
 
@@ -1570,6 +1758,16 @@ AttnPlan plan_verify_attn(const sva_batch* batch, const sva_paged_kv* kv, int Hq
                           const sva_verify_opts* opts) {
   AttnPlan pl;
   const int G = Hq / kv->Hkv;
+  // Row-block kernel: when a pair has more query rows than the split kernel
+  // handles in one pass and the blocks alone fill the device (or the split
+  // kernel cannot take the shape at all).  MFMA path only.
+  const bool mfma_ok = kv->kv_dtype != SVA_F32 && !(opts && opts->path == 1);
+  const int64_t rows = int64_t(std::max(batch->max_q, 1)) * G;
+  const int64_t blocks_ub =
+      int64_t(kv->Hkv) * ((int64_t(batch->total_q) * G + kRowBlock - 1) / kRowBlock + batch->B);
+  pl.rows_kernel = mfma_ok && (batch->max_q > kMaxDraftsSplit || rows > kMaxRowsSplit ||
+                               (rows > kMfmaRows && blocks_ub >= num_cus));
+  pl.rows_grid = int(std::min<int64_t>(blocks_ub, 0x7fffffff));
   const int64_t pages_per_seq =
       std::min<int64_t>(kv->max_pages_per_seq, (int64_t(batch->max_len) + kPage - 1) / kPage);
   const int64_t pages_ub = int64_t(batch->B) * kv->Hkv * std::max<int64_t>(pages_per_seq, 1);
@@ -1586,7 +1784,23 @@ AttnPlan plan_verify_attn(const sva_batch* batch, const sva_paged_kv* kv, int Hq
   pl.counter_bytes = size_t(kMaxWorkgroups) * 4;
   pl.slot_bytes = size_t(2) * W * pl.slot_rows * (kv->d + 2) * sizeof(float);
   pl.total_bytes = pl.counter_bytes + pl.slot_bytes;
+  if (pl.rows_kernel) {                 // no workspace needed
+    pl.num_wg = 0;
+    pl.slot_bytes = 0;
+    pl.total_bytes = pl.counter_bytes;
+  }
   return pl;
+}
+
+template <typename KV, int D>
+static hipError_t attn_rows_launch(const AttnParams& p, int grid, hipStream_t st) {
+  if (p.draft_mask)
+    hipLaunchKernelGGL((verify_attn_rows_kernel<KV, D, true>), dim3(grid), dim3(kRowWaves * kWave),
+                       0, st, p);
+  else
+    hipLaunchKernelGGL((verify_attn_rows_kernel<KV, D, false>), dim3(grid), dim3(kRowWaves * kWave),
+                       0, st, p);
+  return hipGetLastError();
 }
 
 template <typename KV, int D>
@@ -1635,6 +1849,14 @@ hipError_t launch_verify_attn(const sva_batch* batch, const void* q, int q_dtype
   p.slot_rows = plan.slot_rows;
   p.W = plan.num_wg;
   const bool mfma = path != 1;         // fp32 caches always take the VALU kernel
+  if (plan.rows_kernel) {
+    if (plan.rows_grid <= 0) return hipSuccess;
+    if (kv->kv_dtype == SVA_BF16)
+      return kv->d == 64 ? attn_rows_launch<uint16_t, 64>(p, plan.rows_grid, st)
+                         : attn_rows_launch<uint16_t, 128>(p, plan.rows_grid, st);
+    return kv->d == 64 ? attn_rows_launch<int8_t, 64>(p, plan.rows_grid, st)
+                       : attn_rows_launch<int8_t, 128>(p, plan.rows_grid, st);
+  }
   if (kv->kv_dtype == SVA_F32)
     return kv->d == 64 ? attn_launch<float, 64>(p, false, st) : attn_launch<float, 128>(p, false, st);
   if (kv->kv_dtype == SVA_BF16)

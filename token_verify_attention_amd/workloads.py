@@ -28,6 +28,10 @@ for are not available, and none of their items are reproduced):
                   acceptance logits [sum(k_b+1), 128256], node tokens agree
                   with the target argmax at their parent with probability 0.8.
 
+* ``prm7b_step``  step-level verification of long speculated steps: the
+                  attention shape of a 7B process reward model (Qwen2.5-Math-
+                  7B: Hq=28, Hkv=4, d=128) scoring a 128-token step per
+                  sequence, B=16, S=4096, bf16 ~ N(0,1).
 * ``ragged_sampled`` the ragged serving batch with stochastic acceptance:
                   drafter logits [T, 128256] = the target row's logits plus
                   N(0, 0.5^2) noise, temperature 1, uniforms u_accept [T] and
@@ -88,9 +92,12 @@ WORKLOADS = {
                        append=True, ident=6),
     "ragged_sampled": Workload("ragged_sampled", 64, 32, 8, 128, (256, 16384), (1, 8), "bf16",
                                "bf16", 1.0, 128256, 0.8, ident=7),
+    "prm7b_step": Workload("prm7b_step", 16, 28, 4, 128, 4096, 128, "bf16", "bf16", append=True,
+                           ident=8),
 }
 
 SAMPLED_WORKLOADS = ("ragged_sampled",)
+LONG_WORKLOADS = ("prm7b_step",)
 
 TREE_WORKLOADS = ("tree8b",)
 
