@@ -1610,15 +1610,24 @@ __global__ __launch_bounds__((AttnLds<KV, D, MF>::NT), 1) void verify_attn_kerne
 // A wave never merges with another, and nothing is split over workgroups, so
 // no workspace is used.  Keys are streamed up to the block's last row's
 // position; the causal (or tree) mask applies on the pages holding drafts.
+// The steps that need no mask run in a loop of their own: with both step
+// kinds in one loop body the compiler keeps two copies of the accumulators
+// at the join and spills the query operands.
 
-constexpr int kRowWaves = 4;                       // one wave per SIMD
+constexpr int kRowWaves = 4;                       // one wave per SIMD per workgroup
 constexpr int kRowBlock = kRowWaves * kMfmaRows;   // 128 query rows per workgroup
+constexpr int kRowPages = 4;                       // pages per step, one per copying wave
 
+// Two workgroups per CU (two waves per SIMD: one wave's LDS reads and softmax
+// run while the other's MFMAs do) wherever the step fits in 256 VGPRs; the
+// INT8 d=128 step needs more and runs one workgroup per CU.
 template <typename KV, int D>
 struct RowsLds {
   using Gm = Geo<KV, D, kRowWaves>;
-  static constexpr int STEP = kRowWaves * Gm::SLOT;   // one page (K, V, scales) per wave
-  static constexpr int NS_RAW = kRingBudget / STEP;
+  static constexpr int OCC = (sizeof(KV) == 1 && D == 128) ? 1 : 2;
+  static constexpr int BUDGET = OCC > 1 ? 72 * 1024 : kRingBudget;
+  static constexpr int STEP = kRowPages * Gm::SLOT;   // the pages (K, V, scales) of one step
+  static constexpr int NS_RAW = BUDGET / STEP;
   static constexpr int NS = NS_RAW < 2 ? 2 : (NS_RAW > 4 ? 4 : NS_RAW);   // steps in the ring
   static constexpr int RING = NS * STEP;
 };
@@ -1631,7 +1640,8 @@ __device__ __forceinline__ int row_blocks(const AttnParams& p, const SeqInfo& si
 // kTree: the call carries tree masks (at most 32 drafts, mask form); causal
 // calls keep draft indices (any number of drafts).
 template <typename KV, int D, bool kTree>
-__global__ __launch_bounds__(kRowWaves * kWave, 1) void verify_attn_rows_kernel(AttnParams p) {
+__global__ __launch_bounds__(kRowWaves * kWave, (RowsLds<KV, D>::OCC))
+void verify_attn_rows_kernel(AttnParams p) {
   using Gm = Geo<KV, D, kRowWaves>;
   using L = RowsLds<KV, D>;
   constexpr int NS = L::NS;
@@ -1716,36 +1726,44 @@ __global__ __launch_bounds__(kRowWaves * kWave, 1) void verify_attn_rows_kernel(
   const int rw = r0 + kMfmaRows * wave;            // this wave's first row
   const bool active = rw < sg.R;                    // wave-uniform
   MfmaStep<KV, D, 2, !kTree> st(p, sg, rw);
-  const int nsteps = (npages + kRowWaves - 1) / kRowWaves;
-  // every wave copies one page per step (past the end: a copy of the last page,
-  // never used), so the per-wave copy counts -- and the waits -- are uniform
+  const int nsteps = (npages + kRowPages - 1) / kRowPages;
+  // waves 0 .. kRowPages-1 copy one page each per step (past the end: a copy of
+  // the last page, never used), so their copy counts -- and waits -- are
+  // uniform; any other wave only meets them at the step barrier
+  static_assert(kRowPages <= kRowWaves && kRowPages % 2 == 0, "page copies per step");
+  const bool copier = wave < kRowPages;
   auto issue = [&](int s) {
-    const int pg = min(kRowWaves * s + wave, npages - 1);
+    if (!copier) return;
+    const int pg = min(kRowPages * s + wave, npages - 1);
     dma_page<KV, D>(p, page_id(p, b, pg), sg.g, s_ring + (s % NS) * L::STEP + wave * Gm::SLOT);
   };
   for (int s = 0; s < NS - 1 && s < nsteps; ++s) issue(s);
   st.ready();
-  for (int s = 0; s < nsteps; ++s) {
-    wait_steps<Gm::P, NS - 1>(min(NS - 2, nsteps - 1 - s));
-    // this wave's page of step s has landed and its reads of step s-1 are done;
-    // after the barrier every page of step s is in LDS and slot s-1 is free
+  // One step: wait for this wave's copies of step s; after the barrier every
+  // page of step s is in LDS and slot s-1 (read by every wave) is free.
+  auto step = [&](int s, auto edge) {
+    constexpr bool EDGE = decltype(edge)::value;
+    if (copier) wait_steps<Gm::P, NS - 1>(min(NS - 2, nsteps - 1 - s));
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     if (s + NS - 1 < nsteps) issue(s + NS - 1);
-    if (active) {
-      const char* base = s_ring + (s % NS) * L::STEP;
+    if (!active) return;
+    const char* base = s_ring + (s % NS) * L::STEP;
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int a = kRowWaves * s + 2 * u;
-        if (a >= npages) break;
-        const char* sa = base + 2 * u * Gm::SLOT;
-        const bool second = a + 1 < npages;
-        st.load(sa, sa + Gm::SLOT);
-        // both pages inside the committed context: no masks
-        if ((a + 2) * kPage <= sg.S) st.template compute<false>(a, second);
-        else st.template compute<true>(a, second);
-      }
+    for (int u = 0; u < kRowPages / 2; ++u) {
+      const int a = kRowPages * s + 2 * u;
+      if (EDGE && a >= npages) break;
+      const char* sa = base + 2 * u * Gm::SLOT;
+      st.load(sa, sa + Gm::SLOT);
+      st.template compute<EDGE>(a, !EDGE || a + 1 < npages);
     }
-  }
+  };
+  // Steps whose pages all lie inside the committed context need no masks;
+  // two separate loops keep each one's body straight-line code, so the
+  // accumulators stay in place across iterations.
+  const int s_plain = min(nsteps, (sg.S / kPage) / kRowPages);
+  int s = 0;
+  for (; s < s_plain; ++s) step(s, std::false_type{});
+  for (; s < nsteps; ++s) step(s, std::true_type{});
   st.finish();
   if (active) st.write_rows(p, sg, rw);
 }
