@@ -142,7 +142,7 @@ size_t sva_verify_workspace_bytes(const sva_batch *batch, const sva_paged_kv *kv
  *   q           device [T, Hq, d] of q_dtype (SVA_F32 or SVA_BF16)
  *   out         device [T, Hq, d] of out_dtype (SVA_F32 or SVA_BF16), written
  *   workspace   device, >= sva_verify_workspace_bytes(...) bytes.  Its first
- *               16 KB hold completion counters (one per workgroup, for any grid
+ *               32 KB hold completion counters (two per workgroup, for any grid
  *               size): they must be all-zero before the workspace is first
  *               used, and every call leaves them all-zero again, so one
  *               workspace serves calls of any shape in stream order.  Calls that

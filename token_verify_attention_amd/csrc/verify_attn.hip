@@ -54,9 +54,9 @@ namespace sva {
 // allows one wave per SIMD only).
 constexpr int kWavesInt8 = 8;
 constexpr int kWavesValu = 4;
-// The workspace starts with one completion counter per possible workgroup, at a
-// fixed size, so partial slots of one call never overlap the counters of a
-// later call with a different grid.
+// The workspace starts with two completion counters per possible workgroup
+// (arrivals, publications), at a fixed size, so partial slots of one call never
+// overlap the counters of a later call with a different grid.
 constexpr int kMaxWorkgroups = 4096;
 constexpr int kMfmaRows = 32;
 constexpr int kValuRows = 16;
@@ -133,12 +133,35 @@ struct Seg {
   int R;          // query rows of the pair: k * G
   bool full;      // the segment is the whole pair
   int slot;       // partial slot when !full
+  bool fuse;      // split pair merged with the last workgroup's wave merge
 };
 
 __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// The thread index for the merges after the page loop.  Pinned (through a
+// volatile move), the merge's index math is not hoisted out of the segment
+// loop, where it would hold registers through the page loop: the INT8 kernel
+// (256 VGPRs for 8 waves) would spill, and in the bf16 kernel the hoisted
+// cross-workgroup merge measurably slows the page loop.  The wave merge of
+// the bf16 kernel keeps the hoisted (precomputed) form, which takes its index
+// math off the path after the last page.
+// Row factors of the wave merge: kMergeTab floats per query row (up to 32
+// rows): the weights of up to 8 waves, then the maximum and the denominator.
+constexpr int kMergeTab = 12;
+__device__ __forceinline__ float* merge_table() {
+  __shared__ __attribute__((aligned(16))) float s_tab[32 * kMergeTab];
+  return s_tab;
+}
+
+template <bool kPin>
+__device__ __forceinline__ int merge_tid() {
+  int tid = int(threadIdx.x);
+  if constexpr (kPin) asm volatile("v_mov_b32 %0, %1" : "=v"(tid) : "v"(tid));
+  return tid;
 }
 
 // This thread's wave within the workgroup, as a wave-uniform (scalar) value.
@@ -1220,6 +1243,7 @@ struct MfmaStep {
   }
 
   static constexpr int SLOT_F = NRB * NDB * kWave * 4 + 2 * NRB * kWave;
+  static constexpr int SLOT_ROWS = 16 * NRB;
   __device__ __forceinline__ void store(float* slot) const {
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
@@ -1249,34 +1273,103 @@ struct MfmaStep {
     }
   }
 
-  // Merge of the NW waves' states stored at mrg + w * SLOT_F (store()
-  // layout), spread over every thread of the workgroup: thread items are
-  // (row, 4 columns), rows varying fastest so that a wave's 16-byte LDS reads
-  // spread over all banks; each combines the NW partials in a fixed order and
-  // writes the normalised output rows, or the unnormalised partial (O, m, l)
-  // of a segment that is not the whole pair.
-  static __device__ __forceinline__ void merge_write(const AttnParams& p, const Seg& sg, int r0,
-                                                     const float* mrg, int nw) {
-    constexpr int D4 = D / 4;
-    constexpr int ITEMS = 16 * NRB * D4;
+  // One (row, 4-column) item of the merge of the nw waves' states stored at
+  // mrg + w * stride (store() layout), combined in wave order: the running
+  // maximum M, the denominator L and the unnormalised output columns O.
+  static __device__ __forceinline__ void merge_item(const float* mrg, int nw, int stride, int r,
+                                                    int d4, float& M, float& L, f32x4& O) {
     constexpr int MOFF = NRB * NDB * kWave * 4;
-    for (int it = threadIdx.x; it < ITEMS; it += nw * kWave) {
-      const int r = it % (16 * NRB), d4 = it / (16 * NRB);
-      const int rb = r >> 4, l16 = r & 15;
-      const int oidx = ((rb * NDB + (d4 >> 2)) * kWave + l16 + 16 * (d4 & 3)) * 4;
-      const int midx = MOFF + rb * kWave + l16;
-      float M = kNegBig;
-      for (int w = 0; w < nw; ++w) M = fmaxf(M, mrg[w * SLOT_F + midx]);
-      float L = 0.f;
-      f32x4 O = {0.f, 0.f, 0.f, 0.f};
-      for (int w = 0; w < nw; ++w) {
-        const float* sl = mrg + w * SLOT_F;
-        const float f = exp2f(sl[midx] - M);
-        L += f * sl[midx + NRB * kWave];
-        const f32x4 o = *reinterpret_cast<const f32x4*>(sl + oidx);
+    const int oidx = (((r >> 4) * NDB + (d4 >> 2)) * kWave + (r & 15) + 16 * (d4 & 3)) * 4;
+    const int midx = MOFF + (r >> 4) * kWave + (r & 15);
+    M = kNegBig;
+    for (int w = 0; w < nw; ++w) M = fmaxf(M, mrg[w * stride + midx]);
+    L = 0.f;
+    O = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int w = 0; w < nw; ++w) {
+      const float* sl = mrg + w * stride;
+      const float f = exp2f(sl[midx] - M);
+      L += f * sl[midx + NRB * kWave];
+      const f32x4 o = *reinterpret_cast<const f32x4*>(sl + oidx);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) O[i] += f * o[i];
-      }
+      for (int i = 0; i < 4; ++i) O[i] += f * o[i];
+    }
+  }
+  // The same merge in two phases, for the 8-wave INT8 kernel, where reading
+  // every wave's (m, l) once per item makes the merge LDS-bound.  Rows: threads 0 .. 16 NRB - 1 each take one query row and
+  // write to tab (kMergeTab floats per row) the wave weights f_w = 2^(m_w - M)
+  // in entries 0 .. nw-1, the running maximum M (entry 8) and the denominator
+  // L = sum_w f_w l_w (entry 9), in wave order.  Columns (after a barrier):
+  // each (row, 4-column) item sums f_w O_w in wave order.
+  static __device__ __forceinline__ void merge_rows(const float* mrg, int nw, int stride,
+                                                    float* tab, int tid) {
+    constexpr int MOFF = NRB * NDB * kWave * 4;
+    if (tid >= 16 * NRB) return;
+    const int midx = MOFF + (tid >> 4) * kWave + (tid & 15);
+    float M = kNegBig;
+    for (int w = 0; w < nw; ++w) M = fmaxf(M, mrg[w * stride + midx]);
+    float L = 0.f;
+    for (int w = 0; w < nw; ++w) {
+      const float f = exp2f(mrg[w * stride + midx] - M);
+      L += f * mrg[w * stride + midx + NRB * kWave];
+      tab[tid * kMergeTab + w] = f;
+    }
+    tab[tid * kMergeTab + 8] = M;
+    tab[tid * kMergeTab + 9] = L;
+  }
+  static __device__ __forceinline__ void merge_cols(const float* mrg, int nw, int stride,
+                                                    const float* tab, int r, int d4, float& M,
+                                                    float& L, f32x4& O) {
+    const int oidx = (((r >> 4) * NDB + (d4 >> 2)) * kWave + (r & 15) + 16 * (d4 & 3)) * 4;
+    O = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int w = 0; w < nw; ++w) {
+      const float f = tab[r * kMergeTab + w];
+      const f32x4 o = *reinterpret_cast<const f32x4*>(mrg + w * stride + oidx);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) O[i] += f * o[i];
+    }
+    M = tab[r * kMergeTab + 8];
+    L = tab[r * kMergeTab + 9];
+  }
+  // Unnormalised partial (O, m, l) of row `row` of a segment that is not the
+  // whole pair, into the segment's slot (device-coherent stores).
+  static __device__ __forceinline__ void write_partial(const AttnParams& p, const Seg& sg, int row,
+                                                       int d4, float M, float L, const f32x4& O) {
+    float* sb = slot_base<D>(p, sg.slot);
+    st_dev4(slot_rsrc(sb, p.slot_rows * D * 4), (row * D + 4 * d4) * 4, O);
+    if (d4 == 0) {
+      st_dev(sb + int64_t(p.slot_rows) * D + row, M);
+      st_dev(sb + int64_t(p.slot_rows) * (D + 1) + row, L);
+    }
+  }
+
+  // Every item of the wave merge (two phases in the INT8 kernel: the
+  // barrier between them is called by every thread).
+  static __device__ __forceinline__ void merge_any(const float* mrg, int nw, int stride, int r,
+                                                   int d4, float& M, float& L, f32x4& O) {
+    if constexpr (I8) merge_cols(mrg, nw, stride, merge_table(), r, d4, M, L, O);
+    else merge_item(mrg, nw, stride, r, d4, M, L, O);
+  }
+  static __device__ __forceinline__ void merge_prepare(const float* mrg, int nw, int stride,
+                                                       int tid) {
+    if constexpr (I8) {
+      merge_rows(mrg, nw, stride, merge_table(), tid);
+      __syncthreads();
+    }
+  }
+
+  // Merge of the nw waves' states spread over every thread of the workgroup:
+  // thread items are (row, 4 columns), rows varying fastest so that a wave's
+  // 16-byte LDS reads spread over all banks; writes the normalised output
+  // rows, or the partial of a segment that is not the whole pair.
+  static __device__ __forceinline__ void merge_write(const AttnParams& p, const Seg& sg, int r0,
+                                                     const float* mrg, int nw, int stride) {
+    constexpr int ITEMS = 16 * NRB * (D / 4);
+    merge_prepare(mrg, nw, stride, merge_tid<I8>());
+    for (int it = merge_tid<I8>(); it < ITEMS; it += nw * kWave) {
+      const int r = it % (16 * NRB), d4 = it / (16 * NRB);
+      float M, L;
+      f32x4 O;
+      merge_any(mrg, nw, stride, r, d4, M, L, O);
       const int row = r0 + r;
       if (row >= sg.R) continue;                    // padding rows of the last block
       if (sg.full) {
@@ -1285,48 +1378,12 @@ struct MfmaStep {
         for (int i = 0; i < 4; ++i) O[i] *= inv;
         store_out4(p, out_row(p, sg, row) * D + 4 * d4, O);
       } else {
-        float* sb = slot_base<D>(p, sg.slot);
-        st_dev4(slot_rsrc(sb, p.slot_rows * D * 4), (row * D + 4 * d4) * 4, O);
-        if (d4 == 0) {
-          st_dev(sb + int64_t(p.slot_rows) * D + row, M);
-          st_dev(sb + int64_t(p.slot_rows) * (D + 1) + row, L);
-        }
+        write_partial(p, sg, row, d4, M, L, O);
       }
     }
   }
 };
 
-// One pass over the segment's pages for rows r0.. of the pair: stream, then
-// merge the NW waves through LDS (the ring is idle by then).  MFMA steps store
-// every wave's state at once and merge in one round spread over all threads;
-// VALU steps merge pairwise and wave 0 writes the output rows or the partial
-// slot.
-template <typename KV, int D, int NW, class St>
-__device__ __forceinline__ void pass(const AttnParams& p, const Seg& sg, int r0, St& st,
-                                     char* ring_all) {
-  const int wave = wave_id();
-  run_pages<KV, D, NW>(p, sg, ring_all + wave * Geo<KV, D, NW>::RING, st);
-  st.finish();
-  __syncthreads();                                    // every wave is off the ring
-  float* mrg = reinterpret_cast<float*>(ring_all);
-  constexpr int SLOT = St::SLOT_F;
-  if constexpr (St::kSplit) {                         // MFMA steps: one merge round
-    st.store(mrg + wave * SLOT);
-    __syncthreads();
-    St::merge_write(p, sg, r0, mrg, NW);
-    __syncthreads();
-  } else {
-#pragma unroll
-    for (int half = NW / 2; half >= 1; half /= 2) {
-      if (wave >= half && wave < 2 * half) st.store(mrg + (wave - half) * SLOT);
-      __syncthreads();
-      if (wave < half) st.combine(mrg + wave * SLOT);
-      __syncthreads();
-    }
-    if (wave == 0) st.write(p, sg, r0);
-    __syncthreads();
-  }
-}
 
 // ============================================================================
 // cross-workgroup merge of a pair split over several workgroups
@@ -1342,6 +1399,26 @@ __device__ __forceinline__ int wg_of(int64_t x, int64_t N, int W) {
 __device__ __forceinline__ int slot_of(int w, int64_t pair_begin, int64_t N, int W) {
   const int64_t s = range_start(w, N, W);
   return (max(s, pair_begin) == s) ? 2 * w : 2 * w + 1;
+}
+
+// Folds one partial state (m, l, o) into a running one (M, L, O).  Every merge
+// of partials goes through this one sequence of operations (fixed fma forms),
+// in segment order, so the result does not depend on which workgroup merges.
+__device__ __forceinline__ void combine_partial(float& M, float& L, f32x4& O, float m, float l,
+                                                const f32x4& o) {
+  const float Mn = fmaxf(M, m);
+  const float fa = exp2f(M - Mn), fb = exp2f(m - Mn);
+  L = fmaf(fa, L, fb * l);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) O[i] = fmaf(fa, O[i], fb * o[i]);
+  M = Mn;
+}
+
+// Non-empty page ranges (segments) of the pair spanning workgroups wf .. wl.
+__device__ __forceinline__ int pair_segments(int wf, int wl, int64_t N, int W) {
+  int n = 0;
+  for (int x = wf; x <= wl; ++x) n += range_start(x + 1, N, W) > range_start(x, N, W);
+  return n;
 }
 
 template <int D, int NT>
@@ -1388,14 +1465,7 @@ __device__ __forceinline__ void merge_pair(const AttnParams& p, const Seg& sg, i
       for (int h = 0; h < 2; ++h) {
         if (!use[h]) continue;
 #pragma unroll
-        for (int u = 0; u < kItems; ++u) {
-          const float Mn = fmaxf(M[u], ms[h][u]);
-          const float fa = exp2f(M[u] - Mn), fb = exp2f(ms[h][u] - Mn);
-          L[u] = fa * L[u] + fb * ls[h][u];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) O[u][i] = fa * O[u][i] + fb * os[h][u][i];
-          M[u] = Mn;
-        }
+        for (int u = 0; u < kItems; ++u) combine_partial(M[u], L[u], O[u], ms[h][u], ls[h][u], os[h][u]);
       }
     }
 #pragma unroll
@@ -1412,6 +1482,191 @@ __device__ __forceinline__ void merge_pair(const AttnParams& p, const Seg& sg, i
   }
 }
 
+// Merge of a pair split over several workgroups, fused with the last one's
+// wave merge.  Each workgroup of the pair, once its waves' states are in LDS,
+// counts its arrival (device-scope counter) and merges its waves' states into
+// registers; every workgroup but the last to arrive writes its partial and
+// then counts it as published (second counter).  The last to arrive waits for
+// the others' publications -- they have all arrived, so they are running and
+// publish without waiting on anything -- and folds every segment of the pair
+// in segment order, its own from registers and the others from their slots,
+// through combine_partial: the same operations whichever workgroup is last.
+// Saves the last workgroup a write, a fence and a reload of its own partial.
+// Split pairs of at most 32 query rows (one pass over the pages) take this
+// path; the last workgroup resets both counters.
+constexpr int kSpinLimit = 1 << 22;
+
+// The current segment's pair: global page range [pb, pend) and total pages N,
+// kept in LDS (not in registers through the page loop).
+__device__ __forceinline__ int64_t* pair_info() {
+  __shared__ int64_t s_pair[3];
+  return s_pair;
+}
+// This workgroup's logical index: consecutive ranges go to one XCD.
+__device__ __forceinline__ int logical_wg(int W) {
+  const int hw = blockIdx.x;
+  return (W % 8 == 0) ? (hw % 8) * (W / 8) + hw / 8 : hw;
+}
+// Whether this workgroup is the last of the current pair to arrive.
+__device__ __forceinline__ int& pair_last() {
+  __shared__ int s_last;
+  return s_last;
+}
+// The current pair's arrival counter and its number of segments.
+__device__ __forceinline__ int32_t* pair_arrivals(const AttnParams& p) {
+  return p.counters + wg_of(pair_info()[0], pair_info()[2], p.W);
+}
+__device__ __forceinline__ int pair_nseg(const AttnParams& p) {
+  const int64_t pb = pair_info()[0], pend = pair_info()[1], N = pair_info()[2];
+  return pair_segments(wg_of(pb, N, p.W), wg_of(pend - 1, N, p.W), N, p.W);
+}
+
+template <class St, int D, int NT>
+__device__ __forceinline__ void merge_fused(const AttnParams& p, const Seg& sg, const float* mrg,
+                                            int stride) {
+  constexpr int RW = St::SLOT_ROWS;
+  constexpr int ITEMS = RW * (D / 4);
+  constexpr int J = (ITEMS + NT - 1) / NT;
+  const int tid = merge_tid<true>();
+  const int64_t pb = pair_info()[0], pend = pair_info()[1], N = pair_info()[2];
+  const int wf = wg_of(pb, N, p.W), wl = wg_of(pend - 1, N, p.W);
+  int32_t* published = p.counters + kMaxWorkgroups + wf;
+  float M[J], L[J];
+  f32x4 O[J];
+  St::merge_prepare(mrg, NT / kWave, stride, tid);
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int it = tid + j * NT;
+    if (it < ITEMS) St::merge_any(mrg, NT / kWave, stride, it % RW, it / RW, M[j], L[j], O[j]);
+  }
+  if (!pair_last()) {                  // set before the barrier that ended the stream
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int it = tid + j * NT;
+      if (it < ITEMS && it % RW < sg.R) St::write_partial(p, sg, it % RW, it / RW, M[j], L[j], O[j]);
+    }
+    // the partial's stores are complete at device scope before the count
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (tid == 0) __hip_atomic_fetch_add(published, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return;
+  }
+  if (tid == 0) {
+    const int others = pair_segments(wf, wl, N, p.W) - 1;
+    for (int n = 0; n < kSpinLimit; ++n) {
+      if (__hip_atomic_load(published, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= others) break;
+      __builtin_amdgcn_s_sleep(2);
+    }
+  }
+  __syncthreads();
+  float Mc[J], Lc[J];
+  f32x4 Oc[J];
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    Mc[j] = kNegBig;
+    Lc[j] = 0.f;
+    Oc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  // segments in order, up to kBatch at a time: every load of a batch is
+  // issued before its partials are folded in, so a batch costs one latency
+  constexpr int kBatch = 3;
+  const int self = logical_wg(p.W);
+  int w = wf;
+  while (w <= wl) {
+    int ws[kBatch];
+    int n = 0;
+    for (; w <= wl && n < kBatch; ++w)
+      if (range_start(w + 1, N, p.W) > range_start(w, N, p.W)) ws[n++] = w;   // non-empty
+    float ms[kBatch][J], ls[kBatch][J];
+    f32x4 os[kBatch][J];
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      if (k >= n || ws[k] == self) continue;
+      float* sb = slot_base<D>(p, slot_of(ws[k], pb, N, p.W));
+      const auto rs = slot_rsrc(sb, p.slot_rows * D * 4);
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        const int it = min(tid + j * NT, ITEMS - 1);
+        const int r = min(it % RW, sg.R - 1), d4 = it / RW;
+        ms[k][j] = ld_dev(sb + int64_t(p.slot_rows) * D + r);
+        ls[k][j] = ld_dev(sb + int64_t(p.slot_rows) * (D + 1) + r);
+        os[k][j] = ld_dev4(rs, (r * D + 4 * d4) * 4);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      if (k >= n) continue;
+      const bool own = ws[k] == self;
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        if (own) combine_partial(Mc[j], Lc[j], Oc[j], M[j], L[j], O[j]);
+        else combine_partial(Mc[j], Lc[j], Oc[j], ms[k][j], ls[k][j], os[k][j]);
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int it = tid + j * NT;
+    if (it >= ITEMS || it % RW >= sg.R) continue;
+    const float inv = 1.f / Lc[j];
+    f32x4 o = Oc[j];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] *= inv;
+    store_out4(p, out_row(p, sg, it % RW) * D + 4 * (it / RW), o);
+  }
+  if (tid == 0) {
+    __hip_atomic_store(p.counters + wf, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(published, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// One pass over the segment's pages for rows r0.. of the pair: stream, then
+// merge the NW waves through LDS.  MFMA steps: each wave's ring region is
+// large enough for its state, so a wave stores its state there as soon as its
+// own pages are done, and one round spread over all threads merges them;
+// VALU steps merge pairwise through the idle ring and wave 0 writes the output
+// rows or the partial slot.
+template <typename KV, int D, int NW, class St>
+__device__ __forceinline__ void pass(const AttnParams& p, const Seg& sg, int r0, St& st,
+                                     char* ring_all) {
+  const int wave = wave_id();
+  constexpr int GR = Geo<KV, D, NW>::RING;
+  if constexpr (St::kSplit) {
+    constexpr int SB = St::SLOT_F * 4;
+    constexpr int WR = GR > SB ? GR : SB;             // this wave's ring, then its state
+    char* mine = ring_all + wave * WR;
+    run_pages<KV, D, NW>(p, sg, mine, st);
+    // a split pair's arrival is counted as soon as wave 0's pages are done, so
+    // the counter's round trip overlaps the other waves' last pages
+    int old = 0;
+    if (sg.fuse && threadIdx.x == 0)
+      old = __hip_atomic_fetch_add(pair_arrivals(p), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    st.finish();
+    st.store(reinterpret_cast<float*>(mine));        // no other wave touches this region
+    if (sg.fuse && threadIdx.x == 0) pair_last() = (old == pair_nseg(p) - 1);
+    __syncthreads();
+    const float* mrg = reinterpret_cast<const float*>(ring_all);
+    if (sg.fuse) merge_fused<St, D, NW * kWave>(p, sg, mrg, WR / 4);
+    else St::merge_write(p, sg, r0, mrg, NW, WR / 4);
+    __syncthreads();
+  } else {
+    run_pages<KV, D, NW>(p, sg, ring_all + wave * GR, st);
+    st.finish();
+    __syncthreads();                                  // every wave is off the ring
+    float* mrg = reinterpret_cast<float*>(ring_all);
+    constexpr int SLOT = St::SLOT_F;
+#pragma unroll
+    for (int half = NW / 2; half >= 1; half /= 2) {
+      if (wave >= half && wave < 2 * half) st.store(mrg + (wave - half) * SLOT);
+      __syncthreads();
+      if (wave < half) st.combine(mrg + wave * SLOT);
+      __syncthreads();
+    }
+    if (wave == 0) st.write(p, sg, r0);
+    __syncthreads();
+  }
+}
+
 // ============================================================================
 // kernel
 // ============================================================================
@@ -1420,11 +1675,12 @@ template <typename KV, int D, bool MF>
 struct AttnLds {
   static constexpr int NW = (MF && sizeof(KV) == 1) ? kWavesInt8 : kWavesValu;
   static constexpr int NT = NW * kWave;
-  static constexpr int RING = NW * Geo<KV, D, NW>::RING;
-  // the wave merge reuses the ring: NW slots (MFMA) or NW/2 slots (VALU) of the
-  // largest step state
-  static constexpr int MERGE = MF ? NW * 4 * (2 * (D / 16) * kWave * 4 + 4 * kWave)
-                                  : (NW / 2) * 4 * (kValuRows * D * 2 + 64);
+  // MFMA: each wave's region holds its ring, then its state (two row blocks
+  // at most); VALU: the wave merge reuses the ring (NW/2 slots of the state)
+  static constexpr int GR = Geo<KV, D, NW>::RING;
+  static constexpr int SB = MF ? 4 * (2 * (D / 16) * kWave * 4 + 4 * kWave) : 0;
+  static constexpr int RING = NW * (GR > SB ? GR : SB);
+  static constexpr int MERGE = MF ? 0 : (NW / 2) * 4 * (kValuRows * D * 2 + 64);
   static constexpr int RING_ALLOC = RING > MERGE ? RING : MERGE;
   // VALU passes stage their query rows and per-wave probabilities in LDS
   static constexpr int QS = MF ? 4 : kValuRows * 2 * (D / 2 + 4);   // dwords (fp32 layout, the larger)
@@ -1515,8 +1771,7 @@ __global__ __launch_bounds__((AttnLds<KV, D, MF>::NT), 1) void verify_attn_kerne
   if (N == 0) return;
 
   // ---- this workgroup's page range; consecutive ranges go to one XCD
-  const int hw = blockIdx.x;
-  const int w = (p.W % 8 == 0) ? (hw % 8) * (p.W / 8) + hw / 8 : hw;
+  const int w = logical_wg(p.W);
   const int64_t g0 = range_start(w, N, p.W), g1 = range_start(w + 1, N, p.W);
   if (g0 >= g1) return;
 
@@ -1565,10 +1820,16 @@ __global__ __launch_bounds__((AttnLds<KV, D, MF>::NT), 1) void verify_attn_kerne
     sg.pe = int(se - pb);
     sg.full = (cur == pb) && (se == pend);
     sg.slot = (cur == g0) ? 2 * w : 2 * w + 1;
+    sg.fuse = MF && !sg.full && sg.R <= kMfmaRows;
+    if (sg.fuse && tid == 0) {          // read after the barriers of the pass
+      pair_info()[0] = pb;
+      pair_info()[1] = pend;
+      pair_info()[2] = N;
+    }
 
     process_segment<KV, D, MF>(p, sg, s_ring, s_q, s_ps);
 
-    if (!sg.full) {
+    if (!sg.full && !sg.fuse) {
       // every thread's partial stores are complete at device scope before the
       // barrier, so the increment below is ordered after all of them
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -1799,7 +2060,7 @@ AttnPlan plan_verify_attn(const sva_batch* batch, const sva_paged_kv* kv, int Hq
   }
   pl.num_wg = W;
   pl.slot_rows = std::max(batch->max_q, 1) * G;
-  pl.counter_bytes = size_t(kMaxWorkgroups) * 4;
+  pl.counter_bytes = size_t(2 * kMaxWorkgroups) * 4;   // arrival and publication counters
   pl.slot_bytes = size_t(2) * W * pl.slot_rows * (kv->d + 2) * sizeof(float);
   pl.total_bytes = pl.counter_bytes + pl.slot_bytes;
   if (pl.rows_kernel) {                 // no workspace needed
