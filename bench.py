@@ -362,6 +362,17 @@ def main():
     a_end.record(stream)
     torch.cuda.synchronize()
     attn_avg = a_start.elapsed_time(a_end) / args.steps
+    # Per-launch distribution: each launch between its own pair of events
+    # (the events add a little idle time between launches; the roofline
+    # figures use the back-to-back average above).
+    marks = [ev() for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
+    marks[0].record(stream)
+    for s in range(args.steps):
+        sets[s % nsets].attn()
+        marks[s + 1].record(stream)
+    torch.cuda.synchronize()
+    per_launch = np.array([marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps)]) * 1e3
     bytes_all = sum(set_bytes[s % nsets] for s in range(args.steps))
     kvb = bytes_all / args.steps
     achieved = kvb / (attn_avg * 1e-3) / 1e9
@@ -399,6 +410,9 @@ def main():
         "kv_hbm_gbps": achieved,
         "kv_frac_of_peak": achieved / HBM_PEAK_GBPS,
         "attn_ms_avg": attn_avg,
+        "attn_us_per_launch": {"p10": float(np.percentile(per_launch, 10)),
+                               "p50": float(np.median(per_launch)),
+                               "p90": float(np.percentile(per_launch, 90))},
         "attn_draft_tokens_per_s": T / (attn_avg * 1e-3),
         "draft_tokens_per_step": T,
         "other_bytes_per_launch": other_bytes(w, ctx, ks, max_pages),

@@ -172,7 +172,8 @@ def _sample_pairs(case, n, seed):
     return sorted(pairs)
 
 
-@pytest.mark.parametrize("name", ["tiny", "mha7b", "gqa8b", "gqa70b_int8", "ragged"])
+@pytest.mark.parametrize("name", ["tiny", "mha7b", "gqa8b", "gqa70b_int8", "gqa70b_int8_tp8",
+                                  "ragged"])
 def test_full_size_workloads_sampled(name):
     w = wl.WORKLOADS[name]
     say(f"attn full-size {name}: generating")

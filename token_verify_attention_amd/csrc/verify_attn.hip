@@ -43,6 +43,7 @@
 #include "launch.h"
 
 #include <algorithm>
+#include <cmath>
 #include <type_traits>
 
 namespace sva {
@@ -2055,8 +2056,16 @@ AttnPlan plan_verify_attn(const sva_batch* batch, const sva_paged_kv* kv, int Hq
     W = std::min(opts->num_workgroups, kMaxWorkgroups);
   } else {
     const int64_t want = (pages_ub + 15) / 16;     // at least 4 pages per wave
-    W = int(std::min<int64_t>(std::min(std::max(num_cus, 1), kMaxWorkgroups),
-                              std::max<int64_t>(want, 1)));
+    // Splitting a pair over one more workgroup shortens its stream by a share
+    // of its pages but adds a partial to its merge, which one workgroup reads
+    // after the others finish; a partial costs about as much as streaming 8
+    // pages, so the time is lowest near sqrt(pages per pair / 8) segments.
+    const int64_t pairs = int64_t(batch->B) * kv->Hkv;
+    const int64_t seg_cap =
+        std::max<int64_t>(2, int64_t(std::sqrt(double(std::max<int64_t>(pages_per_seq, 1)) / 8.0) + 0.5));
+    W = int(std::min<int64_t>(std::min<int64_t>(std::min(std::max(num_cus, 1), kMaxWorkgroups),
+                                                std::max<int64_t>(want, 1)),
+                              pairs * seg_cap));
   }
   pl.num_wg = W;
   pl.slot_rows = std::max(batch->max_q, 1) * G;

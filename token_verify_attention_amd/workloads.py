@@ -20,6 +20,10 @@ for are not available, and none of their items are reproduced):
                   k new K/V rows per sequence to append.
 * ``gqa70b_int8`` B=16, Hq=64, Hkv=8, d=128, S=8192, k=4, K/V ~ N(0, 0.5) in
                   fp32 (quantised to INT8 by the code under test), Q bf16.
+* ``gqa70b_int8_tp8`` one GPU's share of ``gqa70b_int8`` under 8-way tensor
+                  parallelism over kv heads: B=16, Hq=8, Hkv=1, otherwise the
+                  same (16 (sequence, kv head) pairs, each split over many
+                  workgroups).
 * ``ragged``      B=64, S_b ~ U[256, 16384], k_b ~ U{1..8}, Hq=32, Hkv=8,
                   d=128, bf16; acceptance logits [sum(k_b+1), 128256] ~ N(0,1),
                   drafts agree with the target argmax with probability 0.8.
@@ -86,6 +90,8 @@ WORKLOADS = {
     "mha7b": Workload("mha7b", 8, 32, 32, 128, 2048, 4, "bf16", "bf16", ident=2),
     "gqa8b": Workload("gqa8b", 32, 32, 8, 128, 4096, 8, "bf16", "bf16", append=True, ident=3),
     "gqa70b_int8": Workload("gqa70b_int8", 16, 64, 8, 128, 8192, 4, "int8", "bf16", 0.5, ident=4),
+    "gqa70b_int8_tp8": Workload("gqa70b_int8_tp8", 16, 8, 1, 128, 8192, 4, "int8", "bf16", 0.5,
+                                ident=9),
     "ragged": Workload("ragged", 64, 32, 8, 128, (256, 16384), (1, 8), "bf16", "bf16",
                        1.0, 128256, 0.8, ident=5),
     "tree8b": Workload("tree8b", 32, 32, 8, 128, 4096, 8, "bf16", "bf16", 1.0, 128256, 0.8,
