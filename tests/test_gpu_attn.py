@@ -228,3 +228,20 @@ def test_one_workspace_serves_calls_of_any_grid_size():
         torch.cuda.synchronize()
         assert_close(out, ref, "bf16")
         assert int(ws[:32768].count_nonzero()) == 0, n
+
+
+@pytest.mark.parametrize("name,nwg", [("gqa70b_int8", 0), ("gqa70b_int8_tp8", 0), ("gqa8b", 600)])
+def test_split_pairs_are_bit_reproducible(name, nwg):
+    """Pairs split over several workgroups are merged in segment order by
+    whichever workgroup arrives last; which one that is varies from run to
+    run, the result must not: repeated calls give identical bits."""
+    w = wl.WORKLOADS[name]
+    case = wl.make_case(w, device=DEV, with_logits=False)
+    batch = batch_of(case)
+    kv = paged_kv(case)
+    say(f"attn reproducibility {name} nwg={nwg}")
+    outs = [tva.spec_verify_attn(batch, case["q"], kv, num_workgroups=nwg) for _ in range(6)]
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
+    assert torch.isfinite(outs[0].float()).all()
