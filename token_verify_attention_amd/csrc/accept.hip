@@ -11,8 +11,9 @@
 //   key = (order-preserving float bits << 32) | (0xffffffff - index)
 // so that the maximum key is the maximum value with the lowest index among
 // ties.  NaN maps to the top key (first NaN wins) and -0.0 to +0.0.
-// Kernel 2 runs one wave per sequence: lane j reduces the chunk keys of row j,
-// then a ballot finds the first draft that disagrees.
+// Kernel 2 runs one wave per sequence: the lanes reduce the chunk keys of the
+// sequence's rows (eight rows per pass, lane c reading chunk c of each), lane
+// j keeps row j's token, and a ballot finds the first draft that disagrees.
 #include "common.h"
 #include "launch.h"
 
@@ -31,11 +32,6 @@ __device__ __forceinline__ uint64_t make_key(float f, uint32_t idx) {
   return (uint64_t(order_key(f)) << 32) | uint64_t(0xffffffffu - idx);
 }
 
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int o) {
-  const uint32_t lo = __shfl_xor(uint32_t(v), o, kWave);
-  const uint32_t hi = __shfl_xor(uint32_t(v >> 32), o, kWave);
-  return (uint64_t(hi) << 32) | lo;
-}
 
 template <bool kVec4>
 __global__ __launch_bounds__(kArgThreads) void argmax_chunks_kernel(
@@ -48,13 +44,25 @@ __global__ __launch_bounds__(kArgThreads) void argmax_chunks_kernel(
   const float* rp = logits + int64_t(row) * V;
   uint64_t best = 0;                        // below every real key
   if constexpr (kVec4) {
-    // begin and chunk_len are multiples of 4 and rows are 16-byte aligned
-    for (int i = begin + 4 * threadIdx.x; i < end; i += 4 * kArgThreads) {
-      const f32x4 v = *reinterpret_cast<const f32x4*>(rp + i);
+    // begin, chunk_len and V are multiples of 4 and rows are 16-byte aligned;
+    // eight 16-byte loads in flight per thread
+    constexpr int kBatch = 8;
+    for (int i0 = begin + 4 * threadIdx.x; i0 < end; i0 += 4 * kArgThreads * kBatch) {
+      f32x4 v[kBatch];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint64_t k = make_key(v[e], uint32_t(i + e));
-        best = k > best ? k : best;
+      for (int u = 0; u < kBatch; ++u) {
+        const int i = i0 + 4 * kArgThreads * u;
+        if (i < end) v[u] = *reinterpret_cast<const f32x4*>(rp + i);
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int i = i0 + 4 * kArgThreads * u;
+        if (i >= end) continue;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint64_t k = make_key(v[u][e], uint32_t(i + e));
+          best = k > best ? k : best;
+        }
       }
     }
   } else {
@@ -90,15 +98,10 @@ __global__ __launch_bounds__(kWave) void accept_scan_kernel(
   q1 = min(max(q1, q0), T);
   const int k = min(q1 - q0, max_q);        // k <= 16 < 64 lanes
   const int row0 = q0 + b;
-  int tok = 0;
-  if (lane <= k) {
-    const uint64_t* kp = keys + int64_t(row0 + lane) * chunks;
-    uint64_t best = kp[0];
-    for (int c = 1; c < chunks; ++c) best = kp[c] > best ? kp[c] : best;
-    tok = int(0xffffffffu - uint32_t(best));
-    argmax_ids[row0 + lane] = tok;
-  }
-  const bool mismatch = lane < k && draft_ids[q0 + lane] != tok;
+  const int draft = lane < k ? draft_ids[q0 + lane] : 0;
+  const int tok = row_tokens_from_keys(keys, chunks, row0, k + 1);   // lane j: row j
+  if (lane <= k) argmax_ids[row0 + lane] = tok;
+  const bool mismatch = lane < k && draft != tok;
   const uint64_t bal = __ballot(mismatch);
   const int n = bal ? __builtin_ctzll(bal) : k;
   const int nxt = __shfl(tok, n, kWave);

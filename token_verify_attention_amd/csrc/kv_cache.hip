@@ -156,12 +156,26 @@ template <typename Src, typename Dst, int D>
 __global__ __launch_bounds__(kQuantThreads) void kv_append_kernel(AppendParams p) {
   constexpr int N = D / kRowLanes;
   __shared__ int32_t s_cu[kMaxLdsSeqs + 1];
-  for (int i = threadIdx.x; i <= p.B; i += blockDim.x) s_cu[i] = p.cu_q[i];
-  __syncthreads();
+  __shared__ int32_t s_ctx[kMaxLdsSeqs];
   const int sub = threadIdx.x % kRowLanes;
   const int64_t n_rows = int64_t(p.T) * p.Hkv * 2;
-  for (int64_t r = int64_t(blockIdx.x) * kRowsPerBlock + threadIdx.x / kRowLanes; r < n_rows;
-       r += int64_t(gridDim.x) * kRowsPerBlock) {
+  const int64_t stride = int64_t(gridDim.x) * kRowsPerBlock;
+  const int64_t r_first = int64_t(blockIdx.x) * kRowsPerBlock + threadIdx.x / kRowLanes;
+  auto src_of = [&](int64_t r) {
+    return static_cast<const Src*>((r & 1) ? p.v_new : p.k_new) + (r >> 1) * D + sub * N;
+  };
+  // The first row's source values depend on nothing else: their load is in
+  // flight while cu_q and ctx_lens are staged, so the row costs two memory
+  // round trips (lengths, then the block-table entry) before its store.
+  float v[N];
+  if (r_first < n_rows) Chunk<Src, N>::load(src_of(r_first), v);
+  for (int i = threadIdx.x; i <= p.B; i += blockDim.x) {
+    s_cu[i] = p.cu_q[i];
+    if (i < p.B) s_ctx[i] = p.ctx_lens[i];
+  }
+  __syncthreads();
+  for (int64_t r = r_first; r < n_rows; r += stride) {
+    if (r != r_first) Chunk<Src, N>::load(src_of(r), v);
     const int which = int(r & 1);                 // 0: K, 1: V
     const int64_t tg = r >> 1;
     const int t = int(tg / p.Hkv);
@@ -173,15 +187,12 @@ __global__ __launch_bounds__(kQuantThreads) void kv_append_kernel(AppendParams p
       if (s_cu[mid] <= t) lo = mid; else hi = mid - 1;
     }
     const int b = lo;
-    const int pos = p.ctx_lens[b] + (t - s_cu[b]);
+    const int pos = s_ctx[b] + (t - s_cu[b]);
     const int lp = pos / kPage;
     if (pos < 0 || lp >= p.max_pages) continue;   // out of contract: skip
     const int page = p.block_table[int64_t(b) * p.max_pages + lp];
     if (page < 0 || page >= p.num_pages) continue;
     const int64_t dst_row = (int64_t(page) * p.Hkv + g) * kPage + (pos % kPage);
-    const Src* src = static_cast<const Src*>(which ? p.v_new : p.k_new) + tg * D + sub * N;
-    float v[N];
-    Chunk<Src, N>::load(src, v);
     if constexpr (sizeof(Dst) == 1) {
       int8_t c[N];
       const uint16_t s16 = quant_row<N>(v, c);

@@ -76,14 +76,9 @@ __global__ __launch_bounds__(kWave) void accept_tree_scan_kernel(
   int q0, k;
   tree_range(cu_q, T, max_q, b, q0, k);
   const int row0 = q0 + b;
-  int tok = 0;
-  if (lane <= k) {                          // row 0: the root; row 1 + i: after node i
-    const uint64_t* kp = keys + int64_t(row0 + lane) * chunks;
-    uint64_t best = kp[0];
-    for (int c = 1; c < chunks; ++c) best = kp[c] > best ? kp[c] : best;
-    tok = int(0xffffffffu - uint32_t(best));
-    argmax_ids[row0 + lane] = tok;
-  }
+  // row 0: the root; row 1 + i: after node i
+  const int tok = row_tokens_from_keys(keys, chunks, row0, k + 1);
+  if (lane <= k) argmax_ids[row0 + lane] = tok;
   const int par = lane < k ? tree_parent(parents, q0, lane) : -2;
   const int draft = lane < k ? draft_ids[q0 + lane] : 0;
   int cur = -1, n = 0, mine = -1;           // lane j keeps path node j
