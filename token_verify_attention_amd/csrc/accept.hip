@@ -16,6 +16,7 @@
 // j keeps row j's token, and a ballot finds the first draft that disagrees.
 #include "common.h"
 #include "launch.h"
+#include "accept_keys.h"
 
 namespace sva {
 

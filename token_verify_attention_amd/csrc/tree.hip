@@ -24,6 +24,7 @@
 //    row is staged in LDS before any row is written.
 #include "common.h"
 #include "launch.h"
+#include "accept_keys.h"
 
 namespace sva {
 

@@ -1877,9 +1877,7 @@ __global__ __launch_bounds__((AttnLds<KV, D, MF>::NT), 1) void verify_attn_kerne
 // at the join and spills the query operands.
 
 constexpr int kRowWaves = 4;                       // one wave per SIMD per workgroup
-constexpr int kRowNRB = 2;                         // 16-row blocks per wave
-constexpr int kRowWaveRows = 16 * kRowNRB;         // query rows per wave
-constexpr int kRowBlock = kRowWaves * kRowWaveRows;   // query rows per workgroup
+constexpr int kRowBlock = kRowWaves * kMfmaRows;   // 128 query rows per workgroup
 constexpr int kRowPages = 4;                       // pages per step, one per copying wave
 
 // Two workgroups per CU (two waves per SIMD: one wave's LDS reads and softmax
@@ -1888,7 +1886,7 @@ constexpr int kRowPages = 4;                       // pages per step, one per co
 template <typename KV, int D>
 struct RowsLds {
   using Gm = Geo<KV, D, kRowWaves>;
-  static constexpr int OCC = (kRowNRB > 2 || (sizeof(KV) == 1 && D == 128)) ? 1 : 2;
+  static constexpr int OCC = (sizeof(KV) == 1 && D == 128) ? 1 : 2;
   static constexpr int BUDGET = OCC > 1 ? 72 * 1024 : kRingBudget;
   static constexpr int STEP = kRowPages * Gm::SLOT;   // the pages (K, V, scales) of one step
   static constexpr int NS_RAW = BUDGET / STEP;
@@ -1987,9 +1985,9 @@ void verify_attn_rows_kernel(AttnParams p) {
   const int npages = min(si.np, (si.S + last_row / p.G) / kPage + 1);
   sg.pe = npages;
   const int wave = wave_id();
-  const int rw = r0 + kRowWaveRows * wave;         // this wave's first row
+  const int rw = r0 + kMfmaRows * wave;            // this wave's first row
   const bool active = rw < sg.R;                    // wave-uniform
-  MfmaStep<KV, D, kRowNRB, !kTree> st(p, sg, rw);
+  MfmaStep<KV, D, 2, !kTree> st(p, sg, rw);
   const int nsteps = (npages + kRowPages - 1) / kRowPages;
   // waves 0 .. kRowPages-1 copy one page each per step (past the end: a copy of
   // the last page, never used), so their copy counts -- and waits -- are
