@@ -256,9 +256,16 @@ struct Geo {
   static __device__ __forceinline__ int swz_k(int rho) { return (rho / RPW) & (CPR - 1); }
   // V: bf16 -- 4 rows x 32 contiguous bytes (transposing 16-bit reads);
   // INT8 -- 4 rows x 16 bytes of each of 2 pages (transposing 8-bit reads);
-  // fp32 -- 4-row quads (VALU path).
+  // fp32 -- 4-row quads (VALU path).  The 16-lane groups of rows 4c .. 4c+3
+  // and 4c+4 .. 4c+7 read together, so bit 2 of the row also moves the
+  // chunks (bf16: by half a bank window; INT8: into the slots the other
+  // group leaves free); without it the two groups hit the same banks
+  // (measured: bank-conflict cycles 2.3-2.7x the LDS-active cycles, halved
+  // by this term).
   static __device__ __forceinline__ int swz_v(int rho) {
-    return ES == 4 ? ((rho >> 2) & 3) * 2 : (ES == 2 ? 2 * (rho & 3) : (rho & 3));
+    return ES == 4 ? ((rho >> 2) & 3) * 2
+                   : (ES == 2 ? (2 * (rho & 3)) ^ ((RB >= 256 ? 8 : 2) * ((rho >> 2) & 1))
+                              : ((rho & 3) ^ (RB >= 128 ? (rho >> 2) & 1 : 0)));
   }
 };
 
