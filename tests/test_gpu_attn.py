@@ -245,3 +245,20 @@ def test_split_pairs_are_bit_reproducible(name, nwg):
     for o in outs[1:]:
         assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
     assert torch.isfinite(outs[0].float()).all()
+
+
+@pytest.mark.parametrize("kvd,nwg", [("bf16", 0), ("bf16", 600), ("int8", 300)])
+def test_long_context_few_pairs_many_segments(kvd, nwg):
+    """One long sequence over two kv heads: each pair is split over tens to
+    hundreds of workgroups, so the last one folds many partials (more than
+    one table's worth at 600 workgroups)."""
+    w = _wk(f"long-ctx-{kvd}", 8, 2, 128, kvd, "bf16", 0.5 if kvd == "int8" else 1.0, ident=70)
+    case = _case(w, [60000], [4])
+    batch = batch_of(case)
+    kv = paged_kv(case)
+    say(f"attn long context {kvd} nwg={nwg}")
+    outs = [tva.spec_verify_attn(batch, case["q"], kv, num_workgroups=nwg) for _ in range(3)]
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
+    _check(case, outs[0])

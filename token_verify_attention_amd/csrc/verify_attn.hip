@@ -201,9 +201,6 @@ __device__ __forceinline__ float* slot_base(const AttnParams& p, int slot) {
 __device__ __forceinline__ void st_dev(float* a, float v) {
   __hip_atomic_store(a, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ float ld_dev(const float* a) {
-  return __hip_atomic_load(const_cast<float*>(a), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 // 16-byte variants through a buffer resource over one partial slot: the same
 // sc1 (device-coherent) policy in one instruction instead of four.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t slot_rsrc(float* base, int bytes) {
@@ -215,6 +212,11 @@ __device__ __forceinline__ void st_dev4(__amdgpu_buffer_rsrc_t r, int byte_off, 
 }
 __device__ __forceinline__ f32x4 ld_dev4(__amdgpu_buffer_rsrc_t r, int byte_off) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, kCpolSc1);
+}
+// 4-byte device-coherent load that is not an atomic: the compiler keeps many
+// in flight (it waits after every atomic load).
+__device__ __forceinline__ float ld_dev1(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, kCpolSc1));
 }
 
 __device__ __forceinline__ void store_out4(const AttnParams& p, int64_t elem, f32x4 v) {
@@ -1423,7 +1425,14 @@ __device__ __forceinline__ void combine_partial(float& M, float& L, f32x4& O, fl
 }
 
 // Non-empty page ranges (segments) of the pair spanning workgroups wf .. wl.
+__device__ __forceinline__ bool range_nonempty(int w, int64_t N, int W) {
+  return N >= W || range_start(w + 1, N, W) > range_start(w, N, W);
+}
+__device__ __forceinline__ int pair_slot(int w, int wf, int first_slot) {
+  return w == wf ? first_slot : 2 * w;
+}
 __device__ __forceinline__ int pair_segments(int wf, int wl, int64_t N, int W) {
+  if (N >= W) return wl - wf + 1;
   int n = 0;
   for (int x = wf; x <= wl; ++x) n += range_start(x + 1, N, W) > range_start(x, N, W);
   return n;
@@ -1457,14 +1466,14 @@ __device__ __forceinline__ void merge_pair(const AttnParams& p, const Seg& sg, i
         const int w = w0 + h;
         use[h] = w <= wl && range_start(w + 1, N, p.W) > range_start(w, N, p.W);   // non-empty
         float* sb = slot_base<D>(p, slot_of(use[h] ? w : w0, pb, N, p.W));
-        const auto rs = slot_rsrc(sb, p.slot_rows * D * 4);
+        const auto rs = slot_rsrc(sb, p.slot_rows * (D + 2) * 4);
 #pragma unroll
         for (int u = 0; u < kItems; ++u) {
           const int it = base + u * NT + threadIdx.x;
           const int r = min(it, items - 1) / (D / 4), d4 = min(it, items - 1) % (D / 4);
           if (use[h]) {
-            ms[h][u] = ld_dev(sb + int64_t(p.slot_rows) * D + r);
-            ls[h][u] = ld_dev(sb + int64_t(p.slot_rows) * (D + 1) + r);
+            ms[h][u] = ld_dev1(rs, (p.slot_rows * D + r) * 4);
+            ls[h][u] = ld_dev1(rs, (p.slot_rows * (D + 1) + r) * 4);
             os[h][u] = ld_dev4(rs, (r * D + 4 * d4) * 4);
           }
         }
@@ -1579,25 +1588,26 @@ __device__ __forceinline__ void merge_fused(const AttnParams& p, const Seg& sg, 
   // issued before its partials are folded in, so a batch costs one latency
   constexpr int kBatch = 3;
   const int self = logical_wg(p.W);
+  const int first_slot = slot_of(wf, pb, N, p.W);
   int w = wf;
   while (w <= wl) {
     int ws[kBatch];
     int n = 0;
     for (; w <= wl && n < kBatch; ++w)
-      if (range_start(w + 1, N, p.W) > range_start(w, N, p.W)) ws[n++] = w;   // non-empty
+      if (range_nonempty(w, N, p.W)) ws[n++] = w;   // non-empty
     float ms[kBatch][J], ls[kBatch][J];
     f32x4 os[kBatch][J];
 #pragma unroll
     for (int k = 0; k < kBatch; ++k) {
       if (k >= n || ws[k] == self) continue;
-      float* sb = slot_base<D>(p, slot_of(ws[k], pb, N, p.W));
-      const auto rs = slot_rsrc(sb, p.slot_rows * D * 4);
+      float* sb = slot_base<D>(p, pair_slot(ws[k], wf, first_slot));
+      const auto rs = slot_rsrc(sb, p.slot_rows * (D + 2) * 4);
 #pragma unroll
       for (int j = 0; j < J; ++j) {
         const int it = min(tid + j * NT, ITEMS - 1);
         const int r = min(it % RW, sg.R - 1), d4 = it / RW;
-        ms[k][j] = ld_dev(sb + int64_t(p.slot_rows) * D + r);
-        ls[k][j] = ld_dev(sb + int64_t(p.slot_rows) * (D + 1) + r);
+        ms[k][j] = ld_dev1(rs, (p.slot_rows * D + r) * 4);
+        ls[k][j] = ld_dev1(rs, (p.slot_rows * (D + 1) + r) * 4);
         os[k][j] = ld_dev4(rs, (r * D + 4 * d4) * 4);
       }
     }
