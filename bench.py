@@ -1,16 +1,17 @@
 """Benchmark of the speculative-verification hot path on one MI355X.
 
 One step = one pass of the whole hot path over one synthetic batch:
-  kv_append (the k new K/V rows of every sequence; INT8 caches quantise on
-  write) -> spec_verify_attn -> accept_prefix (argmax over the vocabulary and
-  the longest accepted prefix).  Token-tree workloads (--workload tree8b) run
-  kv_append -> tree_masks -> tree attention -> accept_tree -> kv_commit_path;
-  --workload ragged_sampled replaces greedy acceptance by stochastic acceptance
-  (rejection sampling over target and drafter logits); --workload prm7b_step
-  verifies long speculated steps (128 drafts per sequence, the attention shape
-  of a 7B process reward model): kv_append -> verification attention, whose
-  roofline is MFMA throughput (the reward model's threshold is not part of
-  this path).
+  spec_verify_attn_append (the k new K/V rows of every sequence written into
+  the cache -- INT8 caches quantise on write -- and the drafts verified, one
+  launch) -> accept_prefix (argmax over the vocabulary and the longest
+  accepted prefix).  Token-tree workloads (--workload tree8b) run
+  tree_masks -> the same call with the tree masks -> accept_tree ->
+  kv_commit_path; --workload ragged_sampled replaces greedy acceptance by
+  stochastic acceptance (rejection sampling over target and drafter logits);
+  --workload prm7b_step verifies long speculated steps (128 drafts per
+  sequence, the attention shape of a 7B process reward model): kv_append ->
+  verification attention, whose roofline is MFMA throughput (the reward
+  model's threshold is not part of this path).
 Default workload: 7B-MHA shape, B=8, Hq=Hkv=32, d=128, S=2048, k=4, bf16 paged
 KV (16-token pages, random page permutation).  That shape names no vocabulary;
 acceptance runs over fp32 logits [B*(k+1), 128256] with drafts agreeing with
@@ -20,9 +21,10 @@ and agreement rate).
 Prints ONE JSON line.  `value` is verified draft tokens per second for whole
 steps (inputs resident in HBM); `roofline` is the attention kernel's KV bytes
 over its own average launch time against 8 TB/s; `cpu_baseline` is the fp64
-oracle on the host.  The attention kernel's average launch time comes from the same number of
-back-to-back launches after the timed steps, between one pair of HIP events
-on its stream; `roofline.traffic` is HBM traffic from committed rocprofv3
+oracle on the host.  The attention kernel's average launch time comes from
+the same number of back-to-back launches of the attention call alone
+(sva_spec_verify_attn, no append) after the timed steps, between one pair of
+HIP events on its stream; `roofline.traffic` is HBM traffic from committed rocprofv3
 counter readings (null when they no longer match the kernel's sources).
 """
 import argparse
@@ -144,6 +146,11 @@ class Inputs:
             self.tree_masks()
             self.attn = tva.prepare_spec_verify_attn(self.batch, case["q"], self.kv, self.out,
                                                      draft_mask=self.masks)
+            # the step appends and verifies in one call (one launch)
+            fused = tva.prepare_spec_verify_attn_append(self.batch, case["q"], self.kv,
+                                                        case["k_new"], case["v_new"], self.out,
+                                                        draft_mask=self.masks)
+            self.append = lambda stream=None: None
             acc = tva.prepare_accept_tree(self.batch, case["logits"], case["draft_ids"],
                                           case["parents"], self.ids, self.alen, self.nxt,
                                           self.path)
@@ -153,12 +160,11 @@ class Inputs:
                 acc(stream)
                 commit(stream)
             self.accept = accept
-            attn = self.attn
             masks_call = self.tree_masks
 
             def step_attn(stream=None):
                 masks_call(stream)
-                attn(stream)
+                fused(stream)
             self.step_attn = step_attn
         else:
             self.attn = tva.prepare_spec_verify_attn(self.batch, case["q"], self.kv, self.out)
@@ -176,7 +182,14 @@ class Inputs:
                 self.accept = tva.prepare_accept_prefix(self.batch, case["logits"],
                                                         case["draft_ids"], self.ids, self.alen,
                                                         self.nxt)
-            self.step_attn = self.attn
+            if long:
+                # the row-block kernel appends in a launch of its own anyway
+                self.step_attn = self.attn
+            else:
+                # the step appends and verifies in one call (one launch)
+                self.step_attn = tva.prepare_spec_verify_attn_append(
+                    self.batch, case["q"], self.kv, case["k_new"], case["v_new"], self.out)
+                self.append = lambda stream=None: None
 
 
 def copy_probe_gbps(dev, nbytes=1 << 30, reps=10):

@@ -220,6 +220,26 @@ sva_status sva_spec_verify_attn_tree(const sva_batch *batch, const void *q, int3
                                      int32_t out_dtype, const sva_verify_opts *opts,
                                      void *workspace, size_t workspace_bytes, void *stream);
 
+/* Append, then verify, in one call: the same results as sva_kv_append(batch,
+ * k_new, v_new, src_dtype, kv) followed by sva_spec_verify_attn (draft_mask
+ * NULL) or sva_spec_verify_attn_tree (draft_mask given) on the same stream,
+ * cache bytes included ("HeteroReason", workflow Phase 3: the speculated rows
+ * enter the cache and are verified in the same pass).  On the split-KV
+ * kernels the appended rows are written by the workgroup that streams their
+ * page, before it starts streaming, so the step needs one launch fewer; for
+ * long speculated steps (the row-block kernel) the append is its own launch.
+ *   k_new, v_new  device [T, Hkv, d] of src_dtype (SVA_F32 or SVA_BF16), as for
+ *                 sva_kv_append
+ * Every other argument, and every limit, is as for sva_spec_verify_attn (or
+ * the tree variant when draft_mask is given). */
+sva_status sva_spec_verify_attn_append(const sva_batch *batch, const void *q, int32_t q_dtype,
+                                       int32_t Hq, const sva_paged_kv *kv, const void *k_new,
+                                       const void *v_new, int32_t src_dtype,
+                                       const uint32_t *draft_mask, float softmax_scale,
+                                       void *out, int32_t out_dtype,
+                                       const sva_verify_opts *opts, void *workspace,
+                                       size_t workspace_bytes, void *stream);
+
 /* Greedy tree acceptance.  Logit rows as for sva_accept_prefix: sequence b
  * owns k_b + 1 rows from cu_q[b] + b; row 0 scores the token after the
  * committed context, row 1 + i the token after node i.  From the root, the

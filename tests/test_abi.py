@@ -68,6 +68,9 @@ def test_host_checked_errors_need_no_gpu():
     assert lib.sva_kv_commit_path(None, None, None, None, None) == 1
     assert lib.sva_accept_stochastic(None, None, None, 10, ctypes.c_float(1.0), None, None, None,
                                      None, None, None, 0, None) == 1
+    # append-and-verify: NULL batch, then NULL new rows and a bad source dtype
+    assert lib.sva_spec_verify_attn_append(None, None, 0, 8, None, None, None, 0, None,
+                                           ctypes.c_float(1.0), None, 0, None, None, 0, None) == 1
     assert lib.sva_kvmu_apply(-1, None, 0, None, None, None, None) == 1
     assert lib.sva_kvmu_apply(4, None, 9, None, None, None, None) == 1
     assert lib.sva_kvmu_apply(0, None, 1, None, None, None, None) == 0
@@ -112,6 +115,13 @@ def test_batch_and_cache_shape_checks():
         ctypes.byref(b), ctypes.c_void_p(64), 1, 4, ctypes.byref(kv), None, ctypes.c_float(0.1),
         ctypes.c_void_p(64), 1, None, ctypes.c_void_p(64), 1 << 30, None) == 1
     assert b"draft_mask" in lib.sva_last_error()
+    app = lambda kn, vn, sd: lib.sva_spec_verify_attn_append(    # append and verify
+        ctypes.byref(b), ctypes.c_void_p(64), 1, 4, ctypes.byref(kv), kn, vn, sd, None,
+        ctypes.c_float(0.1), ctypes.c_void_p(64), 1, None, ctypes.c_void_p(64), 1 << 30, None)
+    assert app(None, None, tva.SVA_BF16) == 1
+    assert b"k_new" in lib.sva_last_error()
+    assert app(ctypes.c_void_p(64), ctypes.c_void_p(64), 3) == 2
+    assert app(ctypes.c_void_p(72), ctypes.c_void_p(64), tva.SVA_BF16) == 1   # misaligned
 
 
 def test_build_flags_keep_ieee_division_and_no_packed_fp32():

@@ -96,6 +96,9 @@ def load():
         lib.sva_spec_verify_attn_tree.restype = ctypes.c_int
         lib.sva_spec_verify_attn_tree.argtypes = [vp, vp, i32, i32, vp, vp, ctypes.c_float, vp,
                                                   i32, vp, vp, sz, vp]
+        lib.sva_spec_verify_attn_append.restype = ctypes.c_int
+        lib.sva_spec_verify_attn_append.argtypes = [vp, vp, i32, i32, vp, vp, vp, i32, vp,
+                                                    ctypes.c_float, vp, i32, vp, vp, sz, vp]
         lib.sva_accept_tree.restype = ctypes.c_int
         lib.sva_accept_tree.argtypes = [vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         lib.sva_kv_commit_path.restype = ctypes.c_int
@@ -372,6 +375,36 @@ def spec_verify_attn(batch, q, kv, softmax_scale=None, out=None, out_dtype=None,
     return out
 
 
+def spec_verify_attn_append(batch, q, kv, k_new, v_new, softmax_scale=None, out=None,
+                            out_dtype=None, workspace=None, path=PATH_AUTO, num_workgroups=0,
+                            stream=None, draft_mask=None):
+    """kv_append(batch, k_new, v_new, kv) then spec_verify_attn(...) in one
+    call (one launch on the split-KV kernels): the new rows enter the cache
+    and the drafts are verified.  Same results as the two calls."""
+    lib = load()
+    _need(q, "q", 3)
+    Hq, d = int(q.shape[1]), int(q.shape[2])
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
+    _check_append(batch, k_new, v_new, kv)
+    _check_attn(batch, q, kv, out)
+    _check_mask(batch, draft_mask, q)
+    nbytes = verify_workspace_bytes(batch, kv, Hq, path, num_workgroups)
+    if workspace is None:
+        workspace = _zeroed_workspace(q.device, nbytes)
+    _need(workspace, "workspace")
+    cb, ckv, co = batch._c(), kv._c(), _opts(path, num_workgroups)
+    _check("sva_spec_verify_attn_append", lib.sva_spec_verify_attn_append(
+        ctypes.byref(cb), _ptr(q), _dtype_code(q, "q"), Hq, ctypes.byref(ckv), _ptr(k_new),
+        _ptr(v_new), _dtype_code(k_new, "k_new"),
+        _ptr(draft_mask) if draft_mask is not None else None, float(softmax_scale), _ptr(out),
+        _dtype_code(out, "out"), ctypes.byref(co), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream, q.device)))
+    return out
+
+
 def accept_workspace_bytes(batch, V):
     lib = load()
     cb = batch._c()
@@ -603,6 +636,30 @@ def prepare_spec_verify_attn(batch, q, kv, out, softmax_scale=None, workspace=No
             _ptr(workspace), workspace.numel() * workspace.element_size())
     return _Prepared("sva_spec_verify_attn", lib.sva_spec_verify_attn, args, q.device,
                      (cb, ckv, co, batch, q, kv, out, workspace))
+
+
+def prepare_spec_verify_attn_append(batch, q, kv, k_new, v_new, out, softmax_scale=None,
+                                    workspace=None, path=PATH_AUTO, num_workgroups=0,
+                                    draft_mask=None):
+    lib = load()
+    _check_append(batch, k_new, v_new, kv)
+    _check_attn(batch, q, kv, out)
+    _check_mask(batch, draft_mask, q)
+    Hq, d = int(q.shape[1]), int(q.shape[2])
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d)
+    nbytes = verify_workspace_bytes(batch, kv, Hq, path, num_workgroups)
+    if workspace is None:
+        workspace = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=q.device)
+    cb, ckv, co = batch._c(), kv._c(), _opts(path, num_workgroups)
+    args = (ctypes.byref(cb), _ptr(q), _dtype_code(q, "q"), Hq, ctypes.byref(ckv), _ptr(k_new),
+            _ptr(v_new), _dtype_code(k_new, "k_new"),
+            _ptr(draft_mask) if draft_mask is not None else None, float(softmax_scale),
+            _ptr(out), _dtype_code(out, "out"), ctypes.byref(co), _ptr(workspace),
+            workspace.numel() * workspace.element_size())
+    return _Prepared("sva_spec_verify_attn_append", lib.sva_spec_verify_attn_append, args,
+                     q.device, (cb, ckv, co, batch, q, kv, out, workspace, k_new, v_new,
+                                draft_mask))
 
 
 def prepare_accept_prefix(batch, logits, draft_ids, argmax_ids, accept_len, next_token,

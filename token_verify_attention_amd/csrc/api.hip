@@ -193,7 +193,9 @@ static sva_status verify_attn(const sva_batch* batch, const void* q, int32_t q_d
                               const sva_paged_kv* kv, const uint32_t* draft_mask,
                               float softmax_scale, void* out, int32_t out_dtype,
                               const sva_verify_opts* opts, void* workspace,
-                              size_t workspace_bytes, void* stream) {
+                              size_t workspace_bytes, void* stream,
+                              const void* k_new = nullptr, const void* v_new = nullptr,
+                              int32_t src_dtype = SVA_BF16) {
   if (sva_status s = check_attn_shape(batch, kv, Hq, opts, draft_mask != nullptr)) return s;
   if (q_dtype != SVA_F32 && q_dtype != SVA_BF16)
     return fail(SVA_ERR_UNSUPPORTED, "q_dtype = %d", q_dtype);
@@ -219,7 +221,8 @@ static sva_status verify_attn(const sva_batch* batch, const void* q, int32_t q_d
                 plan.total_bytes);
   if (!aligned16(workspace)) return fail(SVA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
   hipError_t e = sva::launch_verify_attn(batch, q, q_dtype, Hq, kv, draft_mask, softmax_scale, out,
-                                         out_dtype, path, plan, workspace, as_stream(stream));
+                                         out_dtype, path, plan, workspace, as_stream(stream),
+                                         k_new, v_new, src_dtype);
   return e == hipSuccess ? SVA_OK : hip_fail(e, "spec_verify_attn launch");
 }
 
@@ -230,6 +233,26 @@ sva_status sva_spec_verify_attn(const sva_batch* batch, const void* q, int32_t q
   g_last_error.clear();
   return verify_attn(batch, q, q_dtype, Hq, kv, nullptr, softmax_scale, out, out_dtype, opts,
                      workspace, workspace_bytes, stream);
+}
+
+sva_status sva_spec_verify_attn_append(const sva_batch* batch, const void* q, int32_t q_dtype,
+                                       int32_t Hq, const sva_paged_kv* kv, const void* k_new,
+                                       const void* v_new, int32_t src_dtype,
+                                       const uint32_t* draft_mask, float softmax_scale,
+                                       void* out, int32_t out_dtype, const sva_verify_opts* opts,
+                                       void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  if (sva_status s = check_batch(batch, kMaxDraftsLong)) return s;
+  if (sva_status s = check_kv(kv, true)) return s;
+  if (src_dtype != SVA_F32 && src_dtype != SVA_BF16)
+    return fail(SVA_ERR_UNSUPPORTED, "src_dtype = %d", src_dtype);
+  if (batch->total_q > 0 && batch->B > 0) {
+    if (!k_new || !v_new) return fail(SVA_ERR_INVALID_ARG, "k_new / v_new is NULL");
+    if (!aligned16(k_new) || !aligned16(v_new))
+      return fail(SVA_ERR_INVALID_ARG, "k_new / v_new must be 16-byte aligned");
+  }
+  return verify_attn(batch, q, q_dtype, Hq, kv, draft_mask, softmax_scale, out, out_dtype, opts,
+                     workspace, workspace_bytes, stream, k_new, v_new, src_dtype);
 }
 
 sva_status sva_spec_verify_attn_tree(const sva_batch* batch, const void* q, int32_t q_dtype,

@@ -31,10 +31,14 @@ AttnPlan plan_verify_attn(const sva_batch* batch, const sva_paged_kv* kv, int Hq
                           const sva_verify_opts* opts);
 // draft_mask: [T] tree attention masks (bit j: draft j of the sequence is
 // visible), or NULL for causal drafts.
+// k_new / v_new (may be NULL): [T, Hkv, d] rows of src_dtype appended to the
+// cache at positions S_b .. S_b+k_b-1 before the attention reads them.
 hipError_t launch_verify_attn(const sva_batch* batch, const void* q, int q_dtype, int Hq,
                               const sva_paged_kv* kv, const uint32_t* draft_mask,
                               float softmax_scale, void* out, int out_dtype, int path,
-                              const AttnPlan& plan, void* workspace, hipStream_t st);
+                              const AttnPlan& plan, void* workspace, hipStream_t st,
+                              const void* k_new = nullptr, const void* v_new = nullptr,
+                              int src_dtype = 0);
 
 // Acceptance: chunked argmax then a per-sequence scan.
 struct AcceptPlan {

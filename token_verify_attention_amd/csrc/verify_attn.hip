@@ -41,6 +41,7 @@
 // in the scores and zeroed in V, so NaN garbage never reaches an output.
 #include "common.h"
 #include "launch.h"
+#include "kv_rows.h"
 
 #include <algorithm>
 #include <cmath>
@@ -81,6 +82,9 @@ struct AttnParams {
   const int32_t* ctx_lens;
   const int32_t* cu_q;
   const uint32_t* draft_mask;   // [T] tree attention masks, or NULL (causal drafts)
+  const void* k_new;            // [T, Hkv, d] new rows to append first, or NULL
+  const void* v_new;
+  int src_f32;                  // element type of k_new / v_new: fp32, else bf16
   void* out;
   float* partials;
   int32_t* counters;
@@ -1743,6 +1747,82 @@ __device__ __forceinline__ void process_segment(const AttnParams& p, const Seg& 
   }
 }
 
+// ============================================================================
+// append of the new rows, fused into the verification pass
+// ============================================================================
+//
+// HeteroReason, workflow Phase 3: the target appends the speculated rows to
+// the cache and verifies them in the same pass.  A new row is written by the
+// wave that will copy its page (wave w copies units -- pairs of pages --
+// w, w + NW, ... of each segment), before that wave issues any page copy, with
+// the same conversion (and INT8 rule) as sva_kv_append; no other wave and no
+// other workgroup reads that row of that kv head in this call.  A wave's
+// memory operations complete in issue order and every step waits for its own
+// copies, so the stores are complete before any copy issued after the
+// wave's first wait -- every copy but the first S steps of the first
+// segment.  A wave that holds new rows in those steps waits for its stores
+// before issuing them; the others start streaming at once.  16 lanes per
+// row; out-of-contract positions (past the block table, invalid page ids)
+// are skipped as the append does.  Returns whether the wave must wait.
+template <typename KV, typename Src, int D, int NW>
+__device__ __forceinline__ bool append_wave_rows(const AttnParams& p, int64_t g0, int64_t g1,
+                                                 int b, int64_t sb) {
+  constexpr int N = D / kRowLanes;
+  constexpr int S_RING = Geo<KV, D, NW>::S;          // steps issued before the first wait
+  const int wave = wave_id();
+  const int group = lane_id() / kRowLanes, sub = lane_id() % kRowLanes;
+  bool early = false;
+  bool first = true;
+  SeqInfo si = seq_info(p, b);
+  int64_t cur = g0;
+  while (cur < g1) {
+    while (cur >= sb + int64_t(p.Hkv) * si.np) {      // next sequence with pages
+      sb += int64_t(p.Hkv) * si.np;
+      ++b;
+      si = seq_info(p, b);
+    }
+    const int o = int(cur - sb);
+    const int g = o / si.np;
+    const int pa = o - g * si.np;
+    const int64_t pend = sb + int64_t(g + 1) * si.np;
+    const int64_t se = min(g1, pend);
+    const int pe = pa + int(se - cur);
+    // positions S .. S+k-1 whose page lies in [pa, pe), 4 per pass (one per
+    // 16-lane group), each written by the owner of its unit
+    const int lo = max(si.S, pa * kPage), hi = min(si.S + si.k, pe * kPage);
+    for (int pos0 = lo; pos0 < hi; pos0 += kWave / kRowLanes) {
+      const int pos = pos0 + group;                     // uniform per 16-lane row
+      const int lp = pos / kPage;
+      const int u = (lp - pa) >> 1;
+      if (pos >= hi || u % NW != wave || lp >= p.max_pages) continue;
+      const int page = p.block_table[int64_t(b) * p.max_pages + lp];
+      if (page < 0 || page >= p.num_pages) continue;
+      if (first && u / NW < S_RING) early = true;
+      const int64_t src_row = int64_t(si.q0 + (pos - si.S)) * p.Hkv + g;
+      const int64_t dst_row = (int64_t(page) * p.Hkv + g) * kPage + (pos % kPage);
+#pragma unroll
+      for (int which = 0; which < 2; ++which) {
+        float v[N];
+        Chunk<Src, N>::load(static_cast<const Src*>(which ? p.v_new : p.k_new) + src_row * D + sub * N,
+                            v);
+        if constexpr (sizeof(KV) == 1) {
+          int8_t c[N];
+          const uint16_t s16 = quant_row<N>(v, c);
+          store_codes<N>(static_cast<int8_t*>(const_cast<void*>(which ? p.v : p.k)) + dst_row * D + sub * N,
+                         c);
+          if (sub == 0) const_cast<uint16_t*>(which ? p.v_scale : p.k_scale)[dst_row] = s16;
+        } else {
+          Chunk<KV, N>::store(static_cast<KV*>(const_cast<void*>(which ? p.v : p.k)) + dst_row * D + sub * N,
+                              v);
+        }
+      }
+    }
+    first = false;
+    cur = se;
+  }
+  return __ballot(early) != 0;
+}
+
 template <typename KV, int D, bool MF>
 __global__ __launch_bounds__((AttnLds<KV, D, MF>::NT), 1) void verify_attn_kernel(AttnParams p) {
   using L = AttnLds<KV, D, MF>;
@@ -1813,6 +1893,11 @@ __global__ __launch_bounds__((AttnLds<KV, D, MF>::NT), 1) void verify_attn_kerne
   __syncthreads();
   int b = s_info[1];
   int64_t sb = s_info[2];
+  if (p.k_new) {                                      // this wave's new rows first
+    const bool early = p.src_f32 ? append_wave_rows<KV, float, D, L::NW>(p, g0, g1, b, sb)
+                                 : append_wave_rows<KV, uint16_t, D, L::NW>(p, g0, g1, b, sb);
+    if (early) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
   SeqInfo si = seq_info(p, b);
 
   int64_t cur = g0;
@@ -2126,10 +2211,14 @@ static hipError_t attn_launch(const AttnParams& p, bool mfma, hipStream_t st) {
 hipError_t launch_verify_attn(const sva_batch* batch, const void* q, int q_dtype, int Hq,
                               const sva_paged_kv* kv, const uint32_t* draft_mask,
                               float softmax_scale, void* out, int out_dtype, int path,
-                              const AttnPlan& plan, void* workspace, hipStream_t st) {
+                              const AttnPlan& plan, void* workspace, hipStream_t st,
+                              const void* k_new, const void* v_new, int src_dtype) {
   AttnParams p;
   p.q = q;
   p.draft_mask = draft_mask;
+  p.k_new = k_new;
+  p.v_new = v_new;
+  p.src_f32 = src_dtype == SVA_F32;
   p.k = kv->k;
   p.v = kv->v;
   p.k_scale = static_cast<const uint16_t*>(kv->k_scale);
@@ -2155,6 +2244,12 @@ hipError_t launch_verify_attn(const sva_batch* batch, const void* q, int q_dtype
   p.W = plan.num_wg;
   const bool mfma = path != 1;         // fp32 caches always take the VALU kernel
   if (plan.rows_kernel) {
+    // the row-block kernel reads a pair's draft pages from several
+    // workgroups: the new rows are appended by their own launch first
+    if (k_new) {
+      const hipError_t e = launch_kv_append(batch, k_new, v_new, src_dtype, kv, st);
+      if (e != hipSuccess) return e;
+    }
     if (plan.rows_grid <= 0) return hipSuccess;
     if (kv->kv_dtype == SVA_BF16)
       return kv->d == 64 ? attn_rows_launch<uint16_t, 64>(p, plan.rows_grid, st)
