@@ -76,7 +76,7 @@ def other_bytes(w, ctx, ks, max_pages):
     return 2 * T * w.Hq * w.d * qe + 4 * len(ctx) * max_pages + 8 * len(ctx)
 
 
-KERNEL_SOURCES = ("verify_attn.hip", "common.h", "launch.h")
+KERNEL_SOURCES = ("verify_attn.hip", "common.h", "launch.h", "kv_rows.h")
 
 
 def kernel_source_hash():
