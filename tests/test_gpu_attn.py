@@ -212,19 +212,26 @@ def test_full_size_workloads_sampled(name):
     assert torch.isfinite(out.float()).all()
 
 
-def test_one_workspace_serves_calls_of_any_grid_size():
+@pytest.mark.parametrize("variant", ["fused", "two_pass", "valu"])
+def test_one_workspace_serves_calls_of_any_grid_size(variant):
     """Regression: partial slots of a call with a small grid must not land on
-    the completion counters of a later call with a larger grid."""
+    the completion counters of a later call with a larger grid, and every call
+    leaves the counters zero -- on the fused merge (at most 32 query rows per
+    pair), the per-pass merge (64 rows: two passes) and the VALU path."""
+    ks = [16, 9, 2, 12] if variant == "two_pass" else [4, 8, 2, 3]
+    path = tva.PATH_VALU if variant == "valu" else tva.PATH_AUTO
     w = _wk("ws-reuse", 32, 8, 128, "bf16", "bf16", ident=64)
-    case = _case(w, [2000, 700, 33, 1500], [4, 8, 2, 3])
+    case = _case(w, [2000, 700, 33, 1500], ks)
     kv = paged_kv(case)
     batch = batch_of(case)
-    nmax = max(tva.verify_workspace_bytes(batch, kv, w.Hq, num_workgroups=n)
+    nmax = max(tva.verify_workspace_bytes(batch, kv, w.Hq, path=path, num_workgroups=n)
                for n in (3, 5, 17, 256, 1024))
     ws = torch.zeros(nmax, dtype=torch.uint8, device=DEV)
     ref = oracle_attn(case)
     for n in (5, 256, 3, 1024, 17, 0):
-        out = tva.spec_verify_attn(batch, case["q"], kv, workspace=ws, num_workgroups=n)
+        say(f"workspace reuse {variant} nwg={n}")
+        out = tva.spec_verify_attn(batch, case["q"], kv, workspace=ws, num_workgroups=n,
+                                   path=path)
         torch.cuda.synchronize()
         assert_close(out, ref, "bf16")
         assert int(ws[:32768].count_nonzero()) == 0, n

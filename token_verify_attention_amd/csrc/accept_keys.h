@@ -13,11 +13,11 @@ __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int o) {
 // Argmax tokens of rows row0 .. row0 + n - 1 (n <= 64) from their chunk keys
 // (keys[row * chunks + c]: the largest 64-bit key of chunk c, the complemented
 // index in the low half): lane j reduces row j and returns its token (0 on
-// lanes >= n).  A lane's loads are issued 8 at a time, so a row costs one
-// memory round trip per 8 chunks instead of one per chunk.
+// lanes >= n).  A lane's loads are issued 32 at a time, so a row of up to 32
+// chunks (the acceptance plan's usual maximum) costs one memory round trip.
 __device__ __forceinline__ int row_tokens_from_keys(const uint64_t* __restrict__ keys, int chunks,
                                                     int64_t row0, int n) {
-  constexpr int kBatch = 8;
+  constexpr int kBatch = 32;
   const int lane = lane_id();
   if (lane >= n) return 0;
   const uint64_t* kp = keys + (row0 + lane) * chunks;

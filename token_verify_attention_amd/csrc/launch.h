@@ -76,9 +76,11 @@ hipError_t launch_kv_commit_path(const sva_batch* batch, const int32_t* accept_l
 // per-chunk weight sums of the sampled rows.
 struct SamplePlan {
   int stat_rows;
-  int chunks;
+  int chunks;                               // row statistics: chunks per row
   int chunk_len;
-  int per;                                  // elements per thread range of a chunk
+  int s_chunks;                             // sampled rows: chunks per row
+  int s_len;
+  int per;                                  // elements per thread range of a sampled chunk
   size_t stats_off, rec_off, sums_off, parts_off;
   size_t total_bytes;
 };

@@ -67,12 +67,22 @@ SamplePlan plan_sample(const sva_batch* batch, int V) {
   len = (len + 3) & ~3;
   p.chunk_len = len;
   p.chunks = (V + len - 1) / len;
+  // kernels 3 and 4 read only the B sampled rows: finer chunks (at least 1024
+  // values) keep about 2048 workgroups in flight and the pick's last serial
+  // walk short
+  int sw = batch->B > 0 ? (2048 + batch->B - 1) / batch->B : 1;
+  sw = std::max(1, std::min(std::min(sw, kMaxChunks), (V + 1023) / 1024));
+  int sl = (V + sw - 1) / sw;
+  sl = (sl + 3) & ~3;
+  p.s_len = sl;
+  p.s_chunks = (V + sl - 1) / sl;
+  p.per = ((sl + kSmThreads - 1) / kSmThreads + 3) & ~3;    // elements per thread range
   p.stats_off = 0;
   p.rec_off = (size_t(p.stat_rows) * p.chunks * sizeof(MS) + 255) & ~size_t(255);
-  p.per = ((len + kSmThreads - 1) / kSmThreads + 3) & ~3;   // elements per thread range
   p.sums_off = p.rec_off + ((size_t(batch->B) * 8 * sizeof(float) + 255) & ~size_t(255));
-  p.parts_off = p.sums_off + ((size_t(batch->B) * p.chunks * 2 * sizeof(float) + 255) & ~size_t(255));
-  p.total_bytes = p.parts_off + size_t(batch->B) * p.chunks * kSmThreads * 2 * sizeof(float);
+  p.parts_off =
+      p.sums_off + ((size_t(batch->B) * p.s_chunks * 2 * sizeof(float) + 255) & ~size_t(255));
+  p.total_bytes = p.parts_off + size_t(batch->B) * p.s_chunks * kSmThreads * 2 * sizeof(float);
   return p;
 }
 
@@ -428,24 +438,24 @@ hipError_t launch_accept_stochastic(const sva_batch* batch, const float* target_
                      draft_logits, V, c, stats, plan.chunks, batch->cu_q, T, batch->max_q,
                      draft_ids, u_accept, accept_len, recs);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  const dim3 g3(unsigned(B) * plan.chunks);
+  const dim3 g3(unsigned(B) * plan.s_chunks);
   if (vec4) {
     hipLaunchKernelGGL(sample_chunk_sums_kernel<true>, g3, dim3(kSmThreads), 0, st,
-                       target_logits, draft_logits, V, c, recs, plan.chunks, plan.chunk_len,
+                       target_logits, draft_logits, V, c, recs, plan.s_chunks, plan.s_len,
                        plan.per, sums, parts);
   } else {
     hipLaunchKernelGGL(sample_chunk_sums_kernel<false>, g3, dim3(kSmThreads), 0, st,
-                       target_logits, draft_logits, V, c, recs, plan.chunks, plan.chunk_len,
+                       target_logits, draft_logits, V, c, recs, plan.s_chunks, plan.s_len,
                        plan.per, sums, parts);
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (vec4) {
     hipLaunchKernelGGL(sample_pick_kernel<true>, dim3(B), dim3(kWave), 0, st, target_logits,
-                       draft_logits, V, c, recs, plan.chunks, plan.chunk_len, plan.per, sums,
+                       draft_logits, V, c, recs, plan.s_chunks, plan.s_len, plan.per, sums,
                        parts, u_sample, next_token);
   } else {
     hipLaunchKernelGGL(sample_pick_kernel<false>, dim3(B), dim3(kWave), 0, st, target_logits,
-                       draft_logits, V, c, recs, plan.chunks, plan.chunk_len, plan.per, sums,
+                       draft_logits, V, c, recs, plan.s_chunks, plan.s_len, plan.per, sums,
                        parts, u_sample, next_token);
   }
   return hipGetLastError();
