@@ -11,9 +11,9 @@
 //   key = (order-preserving float bits << 32) | (0xffffffff - index)
 // so that the maximum key is the maximum value with the lowest index among
 // ties.  NaN maps to the top key (first NaN wins) and -0.0 to +0.0.
-// Kernel 2 runs one wave per sequence: the lanes reduce the chunk keys of the
-// sequence's rows (eight rows per pass, lane c reading chunk c of each), lane
-// j keeps row j's token, and a ballot finds the first draft that disagrees.
+// Kernel 2 runs one wave per sequence: lane j reduces the chunk keys of the
+// sequence's row j (all of a row's keys loaded together) and keeps its token,
+// and a ballot finds the first draft that disagrees.
 #include "common.h"
 #include "launch.h"
 #include "accept_keys.h"
@@ -46,14 +46,15 @@ __global__ __launch_bounds__(kArgThreads) void argmax_chunks_kernel(
   uint64_t best = 0;                        // below every real key
   if constexpr (kVec4) {
     // begin, chunk_len and V are multiples of 4 and rows are 16-byte aligned;
-    // eight 16-byte loads in flight per thread
+    // eight 16-byte loads in flight per thread, non-temporal (the logits are
+    // read once)
     constexpr int kBatch = 8;
     for (int i0 = begin + 4 * threadIdx.x; i0 < end; i0 += 4 * kArgThreads * kBatch) {
       f32x4 v[kBatch];
 #pragma unroll
       for (int u = 0; u < kBatch; ++u) {
         const int i = i0 + 4 * kArgThreads * u;
-        if (i < end) v[u] = *reinterpret_cast<const f32x4*>(rp + i);
+        if (i < end) v[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(rp + i));
       }
 #pragma unroll
       for (int u = 0; u < kBatch; ++u) {

@@ -97,13 +97,14 @@ __global__ __launch_bounds__(kSmThreads) void row_stats_kernel(
   const int begin = ch * chunk_len, end = min(V, begin + chunk_len);
   MS acc{-INFINITY, 0.f};
   if constexpr (kVec4) {
-    constexpr int kBatch = 8;               // f32x4 loads in flight per thread
+    constexpr int kBatch = 8;               // f32x4 loads in flight per thread (non-temporal:
+                                            // kernel 3 re-reads only the sampled rows)
     for (int i0 = begin + 4 * threadIdx.x; i0 < end; i0 += 4 * kSmThreads * kBatch) {
       f32x4 v[kBatch];
 #pragma unroll
       for (int u = 0; u < kBatch; ++u) {
         const int i = i0 + 4 * kSmThreads * u;
-        v[u] = i < end ? *reinterpret_cast<const f32x4*>(rp + i)
+        v[u] = i < end ? __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(rp + i))
                        : f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
       }
 #pragma unroll
