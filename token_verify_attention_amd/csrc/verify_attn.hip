@@ -249,7 +249,7 @@ struct Geo {
   static constexpr int SCALES = ES == 1 ? 64 : 0;    // INT8: 16 K + 16 V fp16 scales
   static constexpr int SLOT = 2 * PAGE + SCALES;     // one ring slot: K page, V page, scales
   static constexpr int DMA = PAGE / 1024;            // dwordx4 DMA instructions per page half
-  static constexpr int P = 2 * DMA + (ES == 1 ? 2 : 0);   // DMA instructions per page
+  static constexpr int P = 2 * DMA + (ES == 1 ? 1 : 0);   // DMA instructions per page
   static constexpr int S_RAW = kRingBudget / (NW * 2 * SLOT);
   static constexpr int S = S_RAW < 1 ? 1 : (S_RAW > 3 ? 3 : S_RAW);   // steps held in the ring
   static constexpr int RING = 2 * S * SLOT;          // bytes per wave
@@ -293,9 +293,11 @@ __device__ __forceinline__ void dma16(const void* base, uint32_t off, void* l) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
                ::"v"(off), "s"(base), "s"(lds_addr(l)) : "memory", "m0");
 }
-__device__ __forceinline__ void dma4(const void* base, uint32_t off, void* l) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1 nt"
-               ::"v"(off), "s"(base), "s"(lds_addr(l)) : "memory", "m0");
+// 4 bytes per lane from a per-lane 64-bit address (lanes may read different
+// arrays).
+__device__ __forceinline__ void dma4(const void* src, void* l) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off nt"
+               ::"v"(src), "s"(lds_addr(l)) : "memory", "m0");
 }
 
 // Page `pid` of kv head g -> ring slot (K page, V page, INT8 scales).
@@ -314,11 +316,10 @@ __device__ __forceinline__ void dma_page(const AttnParams& p, int pid, int g, ch
     dma16(vb, uint32_t(rho * Gm::RB + (phi ^ Gm::swz_v(rho)) * 16), slot + Gm::PAGE + 1024 * e);
   }
   if constexpr (Gm::ES == 1) {
+    // one copy for both scale rows: lanes 0-7 the 16 K scales, lanes 8-15
+    // the 16 V scales, landing side by side
     const int64_t so = (int64_t(pid) * p.Hkv + g) * kPage;
-    if (lane < 8) {
-      dma4(p.k_scale + so, uint32_t(4 * lane), slot + 2 * Gm::PAGE);
-      dma4(p.v_scale + so, uint32_t(4 * lane), slot + 2 * Gm::PAGE + 32);
-    }
+    if (lane < 16) dma4((lane < 8 ? p.k_scale : p.v_scale) + so + 2 * (lane & 7), slot + 2 * Gm::PAGE);
   }
 }
 
