@@ -46,9 +46,9 @@ __global__ __launch_bounds__(kArgThreads) void argmax_chunks_kernel(
   uint64_t best = 0;                        // below every real key
   if constexpr (kVec4) {
     // begin, chunk_len and V are multiples of 4 and rows are 16-byte aligned;
-    // eight 16-byte loads in flight per thread, non-temporal (the logits are
-    // read once)
-    constexpr int kBatch = 8;
+    // sixteen 16-byte loads in flight per thread (a 16K-value chunk in one
+    // round), non-temporal (the logits are read once)
+    constexpr int kBatch = 16;
     for (int i0 = begin + 4 * threadIdx.x; i0 < end; i0 += 4 * kArgThreads * kBatch) {
       f32x4 v[kBatch];
 #pragma unroll
@@ -116,8 +116,8 @@ __global__ __launch_bounds__(kWave) void accept_scan_kernel(
 AcceptPlan plan_accept(const sva_batch* batch, int V) {
   AcceptPlan p;
   p.rows = batch->total_q + batch->B;
-  // about 2048 workgroups in flight, each chunk at least 4096 values
-  int want = p.rows > 0 ? (2048 + p.rows - 1) / p.rows : 1;
+  // about 3072 workgroups, each chunk at least 4096 values
+  int want = p.rows > 0 ? (3072 + p.rows - 1) / p.rows : 1;
   const int max_chunks = (V + 4095) / 4096;
   if (want > max_chunks) want = max_chunks;
   if (want < 1) want = 1;
