@@ -60,7 +60,7 @@ __device__ __forceinline__ MS ms_wave(MS v) {
 SamplePlan plan_sample(const sva_batch* batch, int V) {
   SamplePlan p;
   p.stat_rows = 2 * batch->total_q + batch->B;
-  int want = p.stat_rows > 0 ? (2048 + p.stat_rows - 1) / p.stat_rows : 1;
+  int want = p.stat_rows > 0 ? (4096 + p.stat_rows - 1) / p.stat_rows : 1;
   const int max_chunks = (V + 4095) / 4096;
   want = std::max(1, std::min(want, max_chunks));
   int len = std::max((V + want - 1) / want, (V + kMaxChunks - 1) / kMaxChunks);
@@ -97,7 +97,7 @@ __global__ __launch_bounds__(kSmThreads) void row_stats_kernel(
   const int begin = ch * chunk_len, end = min(V, begin + chunk_len);
   MS acc{-INFINITY, 0.f};
   if constexpr (kVec4) {
-    constexpr int kBatch = 8;               // f32x4 loads in flight per thread (non-temporal:
+    constexpr int kBatch = 16;              // f32x4 loads in flight per thread (non-temporal:
                                             // kernel 3 re-reads only the sampled rows)
     for (int i0 = begin + 4 * threadIdx.x; i0 < end; i0 += 4 * kSmThreads * kBatch) {
       f32x4 v[kBatch];
