@@ -5,8 +5,9 @@ One step = one pass of the whole hot path over one synthetic batch:
   the cache -- INT8 caches quantise on write -- and the drafts verified, one
   launch) -> accept_prefix (argmax over the vocabulary and the longest
   accepted prefix).  Token-tree workloads (--workload tree8b) run
-  tree_masks -> the same call with the tree masks -> accept_tree ->
-  kv_commit_path; --workload ragged_sampled replaces greedy acceptance by
+  tree_masks -> the same call with the tree masks -> accept_tree_commit (the
+  tree walk and the commit of the accepted branch, one launch after the
+  argmax); --workload ragged_sampled replaces greedy acceptance by
   stochastic acceptance (rejection sampling over target and drafter logits);
   --workload prm7b_step verifies long speculated steps (128 drafts per
   sequence, the attention shape of a 7B process reward model): kv_append ->
@@ -151,15 +152,10 @@ class Inputs:
                                                         case["k_new"], case["v_new"], self.out,
                                                         draft_mask=self.masks)
             self.append = lambda stream=None: None
-            acc = tva.prepare_accept_tree(self.batch, case["logits"], case["draft_ids"],
-                                          case["parents"], self.ids, self.alen, self.nxt,
-                                          self.path)
-            commit = tva.prepare_kv_commit_path(self.batch, self.alen, self.path, self.kv)
-
-            def accept(stream=None):
-                acc(stream)
-                commit(stream)
-            self.accept = accept
+            self.accept = tva.prepare_accept_tree_commit(self.batch, case["logits"],
+                                                         case["draft_ids"], case["parents"],
+                                                         self.kv, self.ids, self.alen, self.nxt,
+                                                         self.path)
             masks_call = self.tree_masks
 
             def step_attn(stream=None):

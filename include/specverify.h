@@ -272,6 +272,24 @@ sva_status sva_accept_tree(const sva_batch *batch, const float *logits, int32_t 
 sva_status sva_kv_commit_path(const sva_batch *batch, const int32_t *accept_len,
                               const int32_t *accept_path, const sva_paged_kv *kv, void *stream);
 
+/* Tree acceptance and the commit of the accepted branch in one call: the same
+ * results as sva_accept_tree followed by sva_kv_commit_path with its
+ * accept_len and accept_path ("Decoding Speculative Decoding from First
+ * Principles", section "Tree based verification"; "HeteroReason", KVMU).  The
+ * walk of each sequence runs in the workgroups that move its rows, so the
+ * branch is committed without a launch of its own.  Arguments as for those
+ * two calls (every output written as they write it; workspace >=
+ * sva_accept_workspace_bytes(batch, V) bytes, 8-byte aligned); K/V buffers
+ * 16-byte aligned, d in {64, 128, 256}.  Errors: SVA_ERR_INVALID_ARG for NULL
+ * pointers, a short or misaligned workspace or misaligned K/V buffers;
+ * SVA_ERR_UNSUPPORTED for other d or B * Hkv above 2^31 - 1. */
+sva_status sva_accept_tree_commit(const sva_batch *batch, const float *logits, int32_t V,
+                                  const int32_t *draft_ids, const int32_t *parents,
+                                  const sva_paged_kv *kv, int32_t *argmax_ids,
+                                  int32_t *accept_len, int32_t *next_token,
+                                  int32_t *accept_path, void *workspace,
+                                  size_t workspace_bytes, void *stream);
+
 /* ---- Stochastic acceptance -------------------------------------------------
  * "Decoding Speculative Decoding from First Principles", section "How does
  * this drafter maintain the same distribution of the target?": with p the

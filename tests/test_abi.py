@@ -66,6 +66,8 @@ def test_host_checked_errors_need_no_gpu():
     assert lib.sva_accept_tree(None, None, 10, None, None, None, None, None, None, None, 0,
                                None) == 1
     assert lib.sva_kv_commit_path(None, None, None, None, None) == 1
+    assert lib.sva_accept_tree_commit(None, None, 10, None, None, None, None, None, None, None,
+                                      None, 0, None) == 1
     assert lib.sva_accept_stochastic(None, None, None, 10, ctypes.c_float(1.0), None, None, None,
                                      None, None, None, 0, None) == 1
     # append-and-verify: NULL batch, then NULL new rows and a bad source dtype

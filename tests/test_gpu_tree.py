@@ -224,6 +224,62 @@ def test_commit_path_bit_exact(kvd):
     assert np.array_equal(np_(kv.v).view(np.uint8), rv.view(np.uint8))
 
 
+def _two_caches(case, kvd):
+    """Two independent copies of the case's cache in its stored format."""
+    if kvd == "int8":
+        kc, ks = tva.kv_quant_int8(case["k_pool"])
+        vc, vs = tva.kv_quant_int8(case["v_pool"])
+        mk = lambda: tva.PagedKV(kc.clone(), vc.clone(), case["block_table"], ks.clone(),
+                                 vs.clone())
+    else:
+        dt = torch.float32 if kvd == "f32" else torch.bfloat16
+        k, v = case["k_pool"].to(dt), case["v_pool"].to(dt)
+        mk = lambda: tva.PagedKV(k.clone(), v.clone(), case["block_table"])
+    return mk(), mk()
+
+
+def _accept_commit_both_ways(case, parents, kvd):
+    batch = batch_of(case)
+    kv_a, kv_b = _two_caches(case, kvd)
+    outs_a = tva.accept_tree(batch, case["logits"], case["draft_ids"], parents)
+    tva.kv_commit_path(batch, outs_a[1], outs_a[3], kv_a)
+    outs_b = tva.accept_tree_commit(batch, case["logits"], case["draft_ids"], parents, kv_b)
+    torch.cuda.synchronize()
+    for a, b in zip(outs_a, outs_b):
+        assert torch.equal(a, b)
+    for a, b in ((kv_a.k, kv_b.k), (kv_a.v, kv_b.v)):
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
+    if kvd == "int8":
+        assert torch.equal(kv_a.k_scale.view(torch.int16), kv_b.k_scale.view(torch.int16))
+        assert torch.equal(kv_a.v_scale.view(torch.int16), kv_b.v_scale.view(torch.int16))
+    return outs_b
+
+
+@pytest.mark.parametrize("kvd", ["bf16", "int8", "f32"])
+def test_accept_tree_commit_equals_the_two_calls(kvd):
+    """sva_accept_tree_commit gives the outputs of sva_accept_tree and the cache
+    bytes of sva_kv_commit_path after it (ragged trees, empty and 16-node ones)."""
+    ks = [16, 8, 5, 1, 0, 12]
+    w = _wk(f"tc-{kvd}", 8, 4, 128 if kvd != "f32" else 64, kvd, "bf16", ident=86, vocab=4099,
+            match=0.9)
+    case = wl.make_case(w, device=DEV, ctx=[0, 15, 100, 7, 3, 33], k=ks, with_logits=False)
+    parents = wl.make_tree(ks, device=DEV, seed=11)
+    case.update(wl.make_tree_logits(w, ks, parents, device=DEV))
+    say(f"accept_tree_commit {kvd}")
+    outs = _accept_commit_both_ways(case, parents, kvd)
+    assert int(outs[1].max()) > 1                      # some branch actually moves rows
+
+
+def test_accept_tree_commit_full_size():
+    """The token-tree benchmark shape (B=32, Hkv=8, d=128, V=128256)."""
+    w = wl.WORKLOADS["tree8b"]
+    case = wl.make_case(w, device=DEV, with_logits=False)
+    parents = wl.make_tree(case["k_host"], device=DEV, seed=w.ident)
+    case.update(wl.make_tree_logits(w, case["k_host"], parents, device=DEV))
+    say("accept_tree_commit tree8b")
+    _accept_commit_both_ways(case, parents, w.kv_dtype)
+
+
 def test_tree_step_then_commit_matches_causal_after():
     """append -> tree attention -> accept -> commit; then the last accepted
     node's output equals causal attention over the committed cache."""

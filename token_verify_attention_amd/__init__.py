@@ -22,7 +22,7 @@ import torch
 __all__ = [
     "load", "SvaError", "Batch", "PagedKV", "kv_quant_int8", "kv_append", "spec_verify_attn",
     "verify_workspace_bytes", "accept_prefix", "accept_workspace_bytes", "LIB_PATH",
-    "tree_masks", "accept_tree", "kv_commit_path", "accept_stochastic",
+    "tree_masks", "accept_tree", "kv_commit_path", "accept_tree_commit", "accept_stochastic",
     "accept_stochastic_workspace_bytes", "kvmu_apply", "KVMU_INIT", "KVMU_SPECULATE",
     "KVMU_ACCEPT", "KVMU_ROLLBACK", "KVMU_PREFIX",
 ]
@@ -103,6 +103,9 @@ def load():
         lib.sva_accept_tree.argtypes = [vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         lib.sva_kv_commit_path.restype = ctypes.c_int
         lib.sva_kv_commit_path.argtypes = [vp, vp, vp, vp, vp]
+        lib.sva_accept_tree_commit.restype = ctypes.c_int
+        lib.sva_accept_tree_commit.argtypes = [vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz,
+                                               vp]
         lib.sva_kvmu_apply.restype = ctypes.c_int
         lib.sva_kvmu_apply.argtypes = [i32, vp, i32, vp, vp, vp, vp]
         lib.sva_accept_stochastic_workspace_bytes.restype = sz
@@ -509,6 +512,49 @@ def kv_commit_path(batch, accept_len, accept_path, kv, stream=None):
         _stream(stream, kv.k.device)))
 
 
+def _tree_commit_args(batch, logits, draft_ids, parents, kv, argmax_ids, accept_len,
+                      next_token, accept_path, workspace):
+    dev = logits.device
+    V = int(logits.shape[1])
+    if argmax_ids is None:
+        argmax_ids = torch.empty(logits.shape[0], dtype=torch.int32, device=dev)
+    if accept_len is None:
+        accept_len = torch.empty(batch.B, dtype=torch.int32, device=dev)
+    if next_token is None:
+        next_token = torch.empty(batch.B, dtype=torch.int32, device=dev)
+    if accept_path is None:
+        accept_path = torch.empty(batch.total_q, dtype=torch.int32, device=dev)
+    _check_accept(batch, logits, draft_ids, argmax_ids, accept_len, next_token)
+    _int32_vec(parents, batch.total_q, "parents")
+    _int32_vec(accept_path, batch.total_q, "accept_path")
+    _check_batch_kv(batch, kv)
+    _same_device(logits, parents, accept_path, kv.k)
+    if workspace is None:
+        workspace = torch.empty(max(accept_workspace_bytes(batch, V), 8), dtype=torch.uint8,
+                                device=dev)
+    cb, ckv = batch._c(), kv._c()
+    args = (ctypes.byref(cb), _ptr(logits), V, _ptr(draft_ids), _ptr(parents), ctypes.byref(ckv),
+            _ptr(argmax_ids), _ptr(accept_len), _ptr(next_token), _ptr(accept_path),
+            _ptr(workspace), workspace.numel() * workspace.element_size())
+    keep = (cb, ckv, batch, logits, draft_ids, parents, kv, argmax_ids, accept_len, next_token,
+            accept_path, workspace)
+    return args, (argmax_ids, accept_len, next_token, accept_path), keep
+
+
+def accept_tree_commit(batch, logits, draft_ids, parents, kv, argmax_ids=None, accept_len=None,
+                       next_token=None, accept_path=None, workspace=None, stream=None):
+    """accept_tree followed by kv_commit_path, in one call (one launch after the
+    argmax).  Returns (argmax_ids, accept_len, next_token, accept_path) as
+    accept_tree does; the cache ends as kv_commit_path leaves it."""
+    lib = load()
+    _need(logits, "logits", 2)
+    args, outs, _ = _tree_commit_args(batch, logits, draft_ids, parents, kv, argmax_ids,
+                                      accept_len, next_token, accept_path, workspace)
+    _check("sva_accept_tree_commit",
+           lib.sva_accept_tree_commit(*args, _stream(stream, logits.device)))
+    return outs
+
+
 def accept_stochastic_workspace_bytes(batch, V):
     lib = load()
     cb = batch._c()
@@ -716,6 +762,15 @@ def prepare_kv_commit_path(batch, accept_len, accept_path, kv):
     args = (ctypes.byref(cb), _ptr(accept_len), _ptr(accept_path), ctypes.byref(ckv))
     return _Prepared("sva_kv_commit_path", lib.sva_kv_commit_path, args, kv.k.device,
                      (cb, ckv, batch, accept_len, accept_path, kv))
+
+
+def prepare_accept_tree_commit(batch, logits, draft_ids, parents, kv, argmax_ids, accept_len,
+                               next_token, accept_path, workspace=None):
+    lib = load()
+    args, _, keep = _tree_commit_args(batch, logits, draft_ids, parents, kv, argmax_ids,
+                                      accept_len, next_token, accept_path, workspace)
+    return _Prepared("sva_accept_tree_commit", lib.sva_accept_tree_commit, args, logits.device,
+                     keep)
 
 
 def prepare_accept_stochastic(batch, target_logits, draft_logits, draft_ids, u_accept, u_sample,

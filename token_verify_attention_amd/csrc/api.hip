@@ -108,6 +108,16 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 
 
 }  // namespace
 
+namespace sva {
+// Tree walk and branch commit in one launch after the argmax (tree.hip).
+hipError_t launch_accept_tree_commit(const sva_batch* batch, const float* logits, int V,
+                                     const int32_t* draft_ids, const int32_t* parents,
+                                     const sva_paged_kv* kv, int32_t* argmax_ids,
+                                     int32_t* accept_len, int32_t* next_token,
+                                     int32_t* accept_path, const AcceptPlan& plan,
+                                     void* workspace, hipStream_t st);
+}  // namespace sva
+
 extern "C" {
 
 const char* sva_status_string(sva_status s) {
@@ -331,6 +341,38 @@ sva_status sva_accept_tree(const sva_batch* batch, const float* logits, int32_t 
                                          accept_len, next_token, accept_path, plan, workspace,
                                          as_stream(stream));
   return e == hipSuccess ? SVA_OK : hip_fail(e, "accept_tree launch");
+}
+
+sva_status sva_accept_tree_commit(const sva_batch* batch, const float* logits, int32_t V,
+                                  const int32_t* draft_ids, const int32_t* parents,
+                                  const sva_paged_kv* kv, int32_t* argmax_ids,
+                                  int32_t* accept_len, int32_t* next_token, int32_t* accept_path,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  if (sva_status s = check_batch(batch)) return s;
+  if (sva_status s = check_kv(kv, true)) return s;
+  if (kv->d != 64 && kv->d != 128 && kv->d != 256) return fail(SVA_ERR_UNSUPPORTED, "d = %d", kv->d);
+  if (V < 1) return fail(SVA_ERR_INVALID_ARG, "V = %d < 1", V);
+  if (batch->B == 0) return SVA_OK;
+  if (!logits || !argmax_ids || !accept_len || !next_token ||
+      (batch->total_q > 0 && (!draft_ids || !parents || !accept_path)))
+    return fail(SVA_ERR_INVALID_ARG, "NULL pointer");
+  if (!aligned16(kv->k) || !aligned16(kv->v))
+    return fail(SVA_ERR_INVALID_ARG, "K/V buffers must be 16-byte aligned");
+  if (int64_t(batch->B) * kv->Hkv > 0x7fffffff)
+    return fail(SVA_ERR_UNSUPPORTED, "B * Hkv too large");
+  const sva::AcceptPlan plan = sva::plan_accept(batch, V);
+  if (!workspace || workspace_bytes < plan.total_bytes)
+    return fail(SVA_ERR_INVALID_ARG, "workspace of %zu bytes < %zu needed", workspace_bytes,
+                plan.total_bytes);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 7) != 0)
+    return fail(SVA_ERR_INVALID_ARG, "workspace must be 8-byte aligned");
+  const DeviceInfo* dev;
+  if (sva_status s = current_device(&dev)) return s;
+  hipError_t e = sva::launch_accept_tree_commit(batch, logits, V, draft_ids, parents, kv,
+                                                argmax_ids, accept_len, next_token, accept_path,
+                                                plan, workspace, as_stream(stream));
+  return e == hipSuccess ? SVA_OK : hip_fail(e, "accept_tree_commit launch");
 }
 
 size_t sva_accept_stochastic_workspace_bytes(const sva_batch* batch, int32_t V) {

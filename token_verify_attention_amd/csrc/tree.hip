@@ -67,22 +67,29 @@ __global__ __launch_bounds__(kWave) void tree_masks_kernel(const int32_t* __rest
   if (lane < k) masks[q0 + lane] = m;
 }
 
-__global__ __launch_bounds__(kWave) void accept_tree_scan_kernel(
-    const uint64_t* __restrict__ keys, int chunks, const int32_t* __restrict__ cu_q, int T,
-    int max_q, const int32_t* __restrict__ draft_ids, const int32_t* __restrict__ parents,
-    int32_t* __restrict__ argmax_ids, int32_t* __restrict__ accept_len,
-    int32_t* __restrict__ next_token, int32_t* __restrict__ accept_path) {
-  const int b = blockIdx.x;
+// Outputs of the tree walk (nullptr: not written).
+struct TreeOut {
+  int32_t* argmax_ids;
+  int32_t* accept_len;
+  int32_t* next_token;
+  int32_t* accept_path;
+};
+
+// The greedy walk down sequence b's tree, run by one wave: row 0 scores the
+// root, row 1 + i the token after node i.  Lane j returns path node j (-1 past
+// the accepted branch); n is the branch length.  Writes the outputs unless
+// they are nullptr.
+__device__ __forceinline__ int tree_walk(const uint64_t* keys, int chunks, int b, int q0, int k,
+                                         const int32_t* draft_ids, const int32_t* parents,
+                                         const TreeOut& o, int& n) {
   const int lane = lane_id();
-  int q0, k;
-  tree_range(cu_q, T, max_q, b, q0, k);
   const int row0 = q0 + b;
-  // row 0: the root; row 1 + i: after node i
   const int tok = row_tokens_from_keys(keys, chunks, row0, k + 1);
-  if (lane <= k) argmax_ids[row0 + lane] = tok;
+  if (o.argmax_ids && lane <= k) o.argmax_ids[row0 + lane] = tok;
   const int par = lane < k ? tree_parent(parents, q0, lane) : -2;
   const int draft = lane < k ? draft_ids[q0 + lane] : 0;
-  int cur = -1, n = 0, mine = -1;           // lane j keeps path node j
+  int cur = -1, mine = -1;                  // lane j keeps path node j
+  n = 0;
   for (int step = 0; step < k; ++step) {
     const int t = __shfl(tok, cur + 1, kWave);
     const uint64_t hit = __ballot(par == cur && draft == t);
@@ -93,11 +100,23 @@ __global__ __launch_bounds__(kWave) void accept_tree_scan_kernel(
     cur = c;
   }
   const int nxt = __shfl(tok, cur + 1, kWave);
-  if (lane < k) accept_path[q0 + lane] = lane < n ? mine : -1;
+  const int node = lane < n ? mine : -1;
+  if (o.accept_path && lane < k) o.accept_path[q0 + lane] = node;
   if (lane == 0) {
-    accept_len[b] = n;
-    next_token[b] = nxt;
+    if (o.accept_len) o.accept_len[b] = n;
+    if (o.next_token) o.next_token[b] = nxt;
   }
+  return node;
+}
+
+__global__ __launch_bounds__(kWave) void accept_tree_scan_kernel(
+    const uint64_t* __restrict__ keys, int chunks, const int32_t* __restrict__ cu_q, int T,
+    int max_q, const int32_t* __restrict__ draft_ids, const int32_t* __restrict__ parents,
+    TreeOut o) {
+  const int b = blockIdx.x;
+  int q0, k, n;
+  tree_range(cu_q, T, max_q, b, q0, k);
+  tree_walk(keys, chunks, b, q0, k, draft_ids, parents, o, n);
 }
 
 struct CommitParams {
@@ -124,55 +143,94 @@ __device__ __forceinline__ int64_t scale_index(const CommitParams& p, int b, int
   return row_offset(p, b, g, pos) / p.row_bytes;
 }
 
-__global__ __launch_bounds__(kCommitThreads) void kv_commit_path_kernel(CommitParams p) {
-  __shared__ __attribute__((aligned(16))) char s_k[kMaxTree * kMaxRowBytes];
-  __shared__ __attribute__((aligned(16))) char s_v[kMaxTree * kMaxRowBytes];
-  __shared__ uint16_t s_sc[2][kMaxTree];
-  __shared__ int s_src[kMaxTree];
-  const int b = blockIdx.x / p.Hkv;
-  const int g = blockIdx.x % p.Hkv;
+// LDS staging of one (sequence, kv head)'s moved rows.
+struct CommitLds {
+  char k[kMaxTree * kMaxRowBytes];
+  char v[kMaxTree * kMaxRowBytes];
+  uint16_t sc[2][kMaxTree];
+  int src[kMaxTree];                        // the node whose row goes to position S + j
+  int n;
+};
+
+// Moves the accepted branch of (b, g) once c.src[0 .. n-1] and c.n are set
+// (and a barrier has passed): every moved row into LDS, then every row to its
+// place.
+__device__ __forceinline__ void commit_branch(const CommitParams& p, int b, int g, CommitLds& c) {
   const int tid = threadIdx.x;
-  int q0, k;
-  tree_range(p.cu_q, p.T, p.max_q, b, q0, k);
   const int S = max(p.ctx_lens[b], 0);
-  const int n = min(max(p.accept_len[b], 0), k);
-  if (tid < kMaxTree) {
-    int src = tid;                          // identity: nothing to move
-    if (tid < n) {
-      const int pj = p.accept_path[q0 + tid];
-      if (pj > tid && pj < k) src = pj;     // a path node never precedes its index
-    }
-    s_src[tid] = src;
-  }
-  __syncthreads();
+  const int n = c.n;
   const int cpr = p.row_bytes / 16;
   // phase 1: every moved row into LDS
   for (int idx = tid; idx < n * cpr; idx += kCommitThreads) {
     const int j = idx / cpr, ch = idx % cpr;
-    if (s_src[j] == j) continue;
-    const int64_t off = row_offset(p, b, g, S + s_src[j]) + ch * 16;
-    *reinterpret_cast<u32x4*>(s_k + j * p.row_bytes + ch * 16) = *reinterpret_cast<const u32x4*>(p.k + off);
-    *reinterpret_cast<u32x4*>(s_v + j * p.row_bytes + ch * 16) = *reinterpret_cast<const u32x4*>(p.v + off);
+    if (c.src[j] == j) continue;
+    const int64_t off = row_offset(p, b, g, S + c.src[j]) + ch * 16;
+    *reinterpret_cast<u32x4*>(c.k + j * p.row_bytes + ch * 16) = *reinterpret_cast<const u32x4*>(p.k + off);
+    *reinterpret_cast<u32x4*>(c.v + j * p.row_bytes + ch * 16) = *reinterpret_cast<const u32x4*>(p.v + off);
   }
-  if (p.k_scale && tid < n && s_src[tid] != tid) {
-    const int64_t si = scale_index(p, b, g, S + s_src[tid]);
-    s_sc[0][tid] = p.k_scale[si];
-    s_sc[1][tid] = p.v_scale[si];
+  if (p.k_scale && tid < n && c.src[tid] != tid) {
+    const int64_t si = scale_index(p, b, g, S + c.src[tid]);
+    c.sc[0][tid] = p.k_scale[si];
+    c.sc[1][tid] = p.v_scale[si];
   }
   __syncthreads();
   // phase 2: rows to positions S .. S + n - 1
   for (int idx = tid; idx < n * cpr; idx += kCommitThreads) {
     const int j = idx / cpr, ch = idx % cpr;
-    if (s_src[j] == j) continue;
+    if (c.src[j] == j) continue;
     const int64_t off = row_offset(p, b, g, S + j) + ch * 16;
-    *reinterpret_cast<u32x4*>(p.k + off) = *reinterpret_cast<const u32x4*>(s_k + j * p.row_bytes + ch * 16);
-    *reinterpret_cast<u32x4*>(p.v + off) = *reinterpret_cast<const u32x4*>(s_v + j * p.row_bytes + ch * 16);
+    *reinterpret_cast<u32x4*>(p.k + off) = *reinterpret_cast<const u32x4*>(c.k + j * p.row_bytes + ch * 16);
+    *reinterpret_cast<u32x4*>(p.v + off) = *reinterpret_cast<const u32x4*>(c.v + j * p.row_bytes + ch * 16);
   }
-  if (p.k_scale && tid < n && s_src[tid] != tid) {
+  if (p.k_scale && tid < n && c.src[tid] != tid) {
     const int64_t si = scale_index(p, b, g, S + tid);
-    p.k_scale[si] = s_sc[0][tid];
-    p.v_scale[si] = s_sc[1][tid];
+    p.k_scale[si] = c.sc[0][tid];
+    p.v_scale[si] = c.sc[1][tid];
   }
+}
+
+// Where row j of the committed branch comes from: path node pj when it is a
+// later node (a path node never precedes its index), else row j itself.
+__device__ __forceinline__ int branch_source(int j, int n, int k, int pj) {
+  return (j < n && pj > j && pj < k) ? pj : j;
+}
+
+__global__ __launch_bounds__(kCommitThreads) void kv_commit_path_kernel(CommitParams p) {
+  __shared__ __attribute__((aligned(16))) CommitLds c;
+  const int b = blockIdx.x / p.Hkv;
+  const int g = blockIdx.x % p.Hkv;
+  const int tid = threadIdx.x;
+  int q0, k;
+  tree_range(p.cu_q, p.T, p.max_q, b, q0, k);
+  const int n = min(max(p.accept_len[b], 0), k);
+  if (tid < kMaxTree) c.src[tid] = branch_source(tid, n, k, tid < n ? p.accept_path[q0 + tid] : -1);
+  if (tid == 0) c.n = n;
+  __syncthreads();
+  commit_branch(p, b, g, c);
+}
+
+// Tree walk and branch commit in one launch: one workgroup per (sequence, kv
+// head); its first wave walks the tree (the kv-head-0 workgroup writes the
+// acceptance outputs), the workgroup then moves that head's branch rows.  The
+// same operations as accept_tree_scan_kernel followed by kv_commit_path_kernel.
+__global__ __launch_bounds__(kCommitThreads) void accept_tree_commit_kernel(
+    const uint64_t* __restrict__ keys, int chunks, const int32_t* __restrict__ draft_ids,
+    const int32_t* __restrict__ parents, TreeOut o, CommitParams p) {
+  __shared__ __attribute__((aligned(16))) CommitLds c;
+  const int b = blockIdx.x / p.Hkv;
+  const int g = blockIdx.x % p.Hkv;
+  const int tid = threadIdx.x;
+  int q0, k;
+  tree_range(p.cu_q, p.T, p.max_q, b, q0, k);
+  if (tid < kWave) {
+    const TreeOut none{nullptr, nullptr, nullptr, nullptr};
+    int n;
+    const int node = tree_walk(keys, chunks, b, q0, k, draft_ids, parents, g == 0 ? o : none, n);
+    if (tid < kMaxTree) c.src[tid] = branch_source(tid, n, k, node);
+    if (tid == 0) c.n = n;
+  }
+  __syncthreads();
+  commit_branch(p, b, g, c);
 }
 
 hipError_t launch_tree_masks(const sva_batch* batch, const int32_t* parents, uint32_t* masks,
@@ -190,15 +248,15 @@ hipError_t launch_accept_tree(const sva_batch* batch, const float* logits, int V
   uint64_t* keys = static_cast<uint64_t*>(workspace);
   hipError_t e = launch_argmax_keys(logits, V, plan, keys, st);
   if (e != hipSuccess) return e;
+  const TreeOut o{argmax_ids, accept_len, next_token, accept_path};
   hipLaunchKernelGGL(accept_tree_scan_kernel, dim3(batch->B), dim3(kWave), 0, st, keys,
                      plan.chunks, batch->cu_q, batch->total_q, batch->max_q, draft_ids, parents,
-                     argmax_ids, accept_len, next_token, accept_path);
+                     o);
   return hipGetLastError();
 }
 
-hipError_t launch_kv_commit_path(const sva_batch* batch, const int32_t* accept_len,
-                                 const int32_t* accept_path, const sva_paged_kv* kv,
-                                 hipStream_t st) {
+static CommitParams commit_params(const sva_batch* batch, const int32_t* accept_len,
+                                  const int32_t* accept_path, const sva_paged_kv* kv) {
   CommitParams p;
   p.k = static_cast<char*>(kv->k);
   p.v = static_cast<char*>(kv->v);
@@ -217,8 +275,31 @@ hipError_t launch_kv_commit_path(const sva_batch* batch, const int32_t* accept_l
   p.max_pages = kv->max_pages_per_seq;
   const int es = kv->kv_dtype == SVA_F32 ? 4 : (kv->kv_dtype == SVA_BF16 ? 2 : 1);
   p.row_bytes = kv->d * es;
+  return p;
+}
+
+hipError_t launch_kv_commit_path(const sva_batch* batch, const int32_t* accept_len,
+                                 const int32_t* accept_path, const sva_paged_kv* kv,
+                                 hipStream_t st) {
+  const CommitParams p = commit_params(batch, accept_len, accept_path, kv);
   hipLaunchKernelGGL(kv_commit_path_kernel, dim3(unsigned(batch->B) * kv->Hkv),
                      dim3(kCommitThreads), 0, st, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_accept_tree_commit(const sva_batch* batch, const float* logits, int V,
+                                     const int32_t* draft_ids, const int32_t* parents,
+                                     const sva_paged_kv* kv, int32_t* argmax_ids,
+                                     int32_t* accept_len, int32_t* next_token,
+                                     int32_t* accept_path, const AcceptPlan& plan,
+                                     void* workspace, hipStream_t st) {
+  uint64_t* keys = static_cast<uint64_t*>(workspace);
+  hipError_t e = launch_argmax_keys(logits, V, plan, keys, st);
+  if (e != hipSuccess) return e;
+  const TreeOut o{argmax_ids, accept_len, next_token, accept_path};
+  const CommitParams p = commit_params(batch, nullptr, nullptr, kv);
+  hipLaunchKernelGGL(accept_tree_commit_kernel, dim3(unsigned(batch->B) * kv->Hkv),
+                     dim3(kCommitThreads), 0, st, keys, plan.chunks, draft_ids, parents, o, p);
   return hipGetLastError();
 }
 
