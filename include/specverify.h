@@ -11,9 +11,9 @@
  *   sva_spec_verify_attn  causal multi-query attention of the k_b drafts
  *   sva_accept_prefix     greedy longest-prefix acceptance over the logits
  *
- * and, on the same conventions, fused forms of them (sva_spec_verify_attn_
- * append) and the token-tree, stochastic-acceptance and KV-pointer calls
- * further below.
+ * and, on the same conventions, a fused form of two of them
+ * (sva_spec_verify_attn_append) and the token-tree, stochastic-acceptance
+ * and KV-pointer calls further below.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
