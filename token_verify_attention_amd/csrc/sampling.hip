@@ -68,9 +68,9 @@ SamplePlan plan_sample(const sva_batch* batch, int V) {
   p.chunk_len = len;
   p.chunks = (V + len - 1) / len;
   // kernels 3 and 4 read only the B sampled rows: finer chunks (at least 1024
-  // values) keep about 2048 workgroups in flight and the pick's last serial
+  // values) keep about 4096 workgroups in flight and the pick's last serial
   // walk short
-  int sw = batch->B > 0 ? (2048 + batch->B - 1) / batch->B : 1;
+  int sw = batch->B > 0 ? (4096 + batch->B - 1) / batch->B : 1;
   sw = std::max(1, std::min(std::min(sw, kMaxChunks), (V + 1023) / 1024));
   int sl = (V + sw - 1) / sw;
   sl = (sl + 3) & ~3;
