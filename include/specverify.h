@@ -100,10 +100,20 @@ typedef struct {
  *                   1: VALU for every sequence     2: MFMA (same as 0)
  *   num_workgroups  0: chosen from the device and batch; otherwise the grid size,
  *                   1 .. 4096 (must equal the value used for the workspace size
- *                   query) */
+ *                   query)
+ *   wait_polls      bound on the one wait inside the kernel: the workgroup that
+ *                   finishes a pair split over several workgroups waits for the
+ *                   others' partial results (they are all running by then, so
+ *                   the wait takes microseconds).  0: the default, 2^22 polls;
+ *                   n > 0: at most n polls; negative: no poll at all, so every
+ *                   such wait gives up (a way to exercise the failure path).
+ *                   A wait that gives up writes NaN to the rows of that pair and
+ *                   sets bit 0 of the workspace status word (see
+ *                   sva_spec_verify_attn); the workspace stays reusable. */
 typedef struct {
   int32_t path;
   int32_t num_workgroups;
+  int32_t wait_polls;
 } sva_verify_opts;
 
 /* INT8 quantisation of `rows` rows of d values, one fp16 scale per row.
@@ -147,10 +157,15 @@ size_t sva_verify_workspace_bytes(const sva_batch *batch, const sva_paged_kv *kv
  *   out         device [T, Hq, d] of out_dtype (SVA_F32 or SVA_BF16), written
  *   workspace   device, >= sva_verify_workspace_bytes(...) bytes.  Its first
  *               32 KB hold completion counters (two per workgroup, for any grid
- *               size): they must be all-zero before the workspace is first
- *               used, and every call leaves them all-zero again, so one
- *               workspace serves calls of any shape in stream order.  Calls that
- *               may run concurrently need distinct workspaces.
+ *               size), the next 256 bytes a status word (int32 at byte 32768):
+ *               all must be zero before the workspace is first used.  Every
+ *               call leaves the counters all-zero again, so one workspace
+ *               serves calls of any shape in stream order.  The status word is
+ *               only ever set, never cleared, by the library: bit 0 means a
+ *               wait gave up (see sva_verify_opts.wait_polls) and the rows of
+ *               the pair concerned were written as NaN; the caller reads and
+ *               clears it when it wants to know.  Calls that may run
+ *               concurrently need distinct workspaces.
  * Supported: page_size 16, d in {64, 128}, Hq % Hkv == 0, B <= 4096, and
  * max_q <= 16 with max_q * (Hq / Hkv) <= 128 on every path; bf16 and INT8
  * caches on the MFMA path (the default) also take long speculated steps,

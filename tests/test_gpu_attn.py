@@ -269,3 +269,66 @@ def test_long_context_few_pairs_many_segments(kvd, nwg):
     for o in outs[1:]:
         assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
     _check(case, outs[0])
+
+
+def test_wait_that_gives_up_writes_nan_and_leaves_the_workspace_reusable():
+    """Forced from the host: with no poll allowed, the workgroup that finishes
+    each split pair gives up at once instead of waiting for the others'
+    partials.  Its pair's rows must come out NaN (never a fold of partials
+    that may be missing), the status word must say so, and once every
+    workgroup is done the counters must be back at zero, so the same
+    workspace then serves an ordinary call.  Every kernel exits normally."""
+    w = _wk("giveup", 16, 4, 128, "bf16", "bf16", ident=71)
+    case = _case(w, [3000, 40, 1200, 700], [4, 2, 3, 4])
+    batch = batch_of(case)
+    kv = paged_kv(case)
+    ws = torch.zeros(tva.verify_workspace_bytes(batch, kv, w.Hq, num_workgroups=24),
+                     dtype=torch.uint8, device=DEV)
+    say("attn forced give-up")
+    bad = tva.spec_verify_attn(batch, case["q"], kv, workspace=ws, num_workgroups=24,
+                               wait_polls=-1)
+    torch.cuda.synchronize()
+    assert int(ws[:tva.STATUS_OFFSET].count_nonzero()) == 0     # counters back at zero
+    assert tva.verify_status(ws) == 1                           # read and cleared
+    assert tva.verify_status(ws) == 0
+    ref = oracle_attn(case)
+    got = np_(bad).astype(np.float64)
+    G = w.Hq // w.Hkv
+    cu = np_(case["cu_q"])
+    nan_pairs = 0
+    for b in range(case["B"]):
+        for g in range(w.Hkv):
+            blk = got[cu[b]:cu[b + 1], g * G:(g + 1) * G]
+            if np.isnan(blk).any():
+                assert np.isnan(blk).all(), (b, g)              # the whole pair, never a part
+                nan_pairs += 1
+            else:
+                assert_close(blk, ref[cu[b]:cu[b + 1], g * G:(g + 1) * G], "bf16")
+    assert nan_pairs > 0
+    good = tva.spec_verify_attn(batch, case["q"], kv, workspace=ws, num_workgroups=24)
+    torch.cuda.synchronize()
+    assert tva.verify_status(ws) == 0
+    assert_close(good, ref, "bf16")
+
+
+def test_calls_on_a_side_stream():
+    """Outputs and workspaces the binding allocates for a call on another
+    stream are allocated on that stream; results equal the default stream's."""
+    w = W("side-stream", 1, 16, 4, 128, 0, 1, "bf16", "bf16", 1.0, 4099, 0.7, False, 72)
+    case = wl.make_case(w, device=DEV, ctx=[500, 70, 2000], k=[4, 3, 8])
+    batch = batch_of(case)
+    kv = paged_kv(case)
+    ref = tva.spec_verify_attn(batch, case["q"], kv)
+    ref_acc = tva.accept_prefix(batch, case["logits"], case["draft_ids"])
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream(device=DEV)
+    for _ in range(3):
+        out = tva.spec_verify_attn(batch, case["q"], kv, stream=s, num_workgroups=9)
+        acc = tva.accept_prefix(batch, case["logits"], case["draft_ids"], stream=s)
+    s.synchronize()
+    keys = [k for k in tva._ws_cache if k[1] == s.cuda_stream]
+    assert keys, "no workspace of its own for the side stream"
+    assert_close(out, oracle_attn(case), "bf16")
+    assert_close(ref, oracle_attn(case), "bf16")
+    for a, b in zip(acc, ref_acc):
+        assert torch.equal(a, b)

@@ -13,7 +13,10 @@ nothing here falls back to another implementation.
     out = tva.spec_verify_attn(batch, q, kv)
     ids, n, nxt = tva.accept_prefix(batch, logits, draft_ids)
 """
+import contextlib
 import ctypes
+import functools
+import inspect
 import math
 import os
 
@@ -24,7 +27,8 @@ __all__ = [
     "verify_workspace_bytes", "accept_prefix", "accept_workspace_bytes", "LIB_PATH",
     "tree_masks", "accept_tree", "kv_commit_path", "accept_tree_commit", "accept_stochastic",
     "accept_stochastic_workspace_bytes", "kvmu_apply", "KVMU_INIT", "KVMU_SPECULATE",
-    "KVMU_ACCEPT", "KVMU_ROLLBACK", "KVMU_PREFIX",
+    "KVMU_ACCEPT", "KVMU_ROLLBACK", "KVMU_PREFIX", "verify_status", "STATUS_OFFSET",
+    "spec_verify_attn_append",
 ]
 
 KVMU_INIT, KVMU_SPECULATE, KVMU_ACCEPT, KVMU_ROLLBACK, KVMU_PREFIX = 0, 1, 2, 3, 4
@@ -32,6 +36,7 @@ KVMU_INIT, KVMU_SPECULATE, KVMU_ACCEPT, KVMU_ROLLBACK, KVMU_PREFIX = 0, 1, 2, 3,
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "_lib", "libspecverify.so")
 
 SVA_F32, SVA_BF16, SVA_F16, SVA_INT8 = 0, 1, 2, 3
+SVA_OK, SVA_ERR_INVALID_ARG, SVA_ERR_UNSUPPORTED, SVA_ERR_HIP = 0, 1, 2, 3
 _DTYPE = {torch.float32: SVA_F32, torch.bfloat16: SVA_BF16, torch.float16: SVA_F16,
           torch.int8: SVA_INT8}
 
@@ -59,7 +64,18 @@ class _Batch(ctypes.Structure):
 
 
 class _Opts(ctypes.Structure):
-    _fields_ = [("path", ctypes.c_int32), ("num_workgroups", ctypes.c_int32)]
+    _fields_ = [("path", ctypes.c_int32), ("num_workgroups", ctypes.c_int32),
+                ("wait_polls", ctypes.c_int32)]
+
+
+# Byte offset of the attention workspace's status word (after the 2 x 4096
+# completion counters); bit 0: a split pair's wait gave up and its rows were
+# written as NaN.
+STATUS_OFFSET = 2 * 4096 * 4
+
+# With TVA_DEBUG set (non-empty, not "0"), every attention call through this
+# binding synchronises its stream and raises if the call set the status word.
+DEBUG = os.environ.get("TVA_DEBUG", "") not in ("", "0")
 
 
 _lib = None
@@ -134,6 +150,45 @@ def _stream(stream, device):
     if stream is None:
         stream = torch.cuda.current_stream(device)
     return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _on_stream(fn):
+    """Run a call's own allocations (outputs, workspaces) on the stream its
+    kernels go to, so the caching allocator never hands their memory to other
+    work while those kernels may still run, and a zero fill is ordered before
+    them."""
+    sig = inspect.signature(fn)
+
+    @functools.wraps(fn)
+    def wrapped(*args, **kwargs):
+        stream = sig.bind(*args, **kwargs).arguments.get("stream")
+        ctx = contextlib.nullcontext() if stream is None else torch.cuda.stream(stream)
+        with ctx:
+            return fn(*args, **kwargs)
+    return wrapped
+
+
+def verify_status(workspace, stream=None, clear=True):
+    """The status word of an attention workspace (synchronises the stream):
+    bit 0 is set when a split pair's wait gave up (its rows were written as
+    NaN).  clear=True zeroes it afterwards."""
+    s = torch.cuda.current_stream(workspace.device) if stream is None else stream
+    s.synchronize()
+    word = workspace[STATUS_OFFSET:STATUS_OFFSET + 4]
+    value = int(word.cpu().view(torch.int32)[0])
+    if clear and value:
+        with torch.cuda.stream(s):
+            word.zero_()
+        s.synchronize()
+    return value
+
+
+def _debug_check(name, workspace, stream):
+    if DEBUG and workspace is not None:
+        v = verify_status(workspace, stream)
+        if v:
+            raise SvaError(name, 3, f"status word {v:#x}: a split pair's wait gave up; its "
+                           "rows are NaN")
 
 
 def _dtype_code(t, what):
@@ -269,6 +324,7 @@ def _check_accept(batch, logits, draft_ids, argmax_ids, accept_len, next_token):
     _same_device(logits, draft_ids, argmax_ids, accept_len, next_token, batch.cu_q)
 
 
+@_on_stream
 def kv_quant_int8(x, codes=None, scales=None, stream=None):
     """INT8 codes and fp16 scales of the rows of x [..., d] (float32 or
     bfloat16).  Returns (codes int8 [..., d], scales float16 [...])."""
@@ -292,6 +348,7 @@ def kv_quant_int8(x, codes=None, scales=None, stream=None):
     return codes, scales
 
 
+@_on_stream
 def kv_append(batch, k_new, v_new, kv, stream=None):
     """Write the k_b new rows of every sequence (k_new, v_new [T, Hkv, d]) at
     positions ctx_lens[b] .. ctx_lens[b] + k_b - 1 of the paged cache."""
@@ -303,8 +360,8 @@ def kv_append(batch, k_new, v_new, kv, stream=None):
         ctypes.byref(ckv), _stream(stream, k_new.device)))
 
 
-def _opts(path, num_workgroups):
-    return _Opts(int(path), int(num_workgroups))
+def _opts(path, num_workgroups, wait_polls=0):
+    return _Opts(int(path), int(num_workgroups), int(wait_polls))
 
 
 def verify_workspace_bytes(batch, kv, Hq, path=PATH_AUTO, num_workgroups=0):
@@ -321,9 +378,12 @@ _ws_cache = {}
 
 
 def _zeroed_workspace(device, nbytes):
-    """A zero-filled workspace kept per device; the attention kernels leave
-    their counters at zero, so it stays reusable (calls on one stream)."""
-    key = torch.device(device).index
+    """A zero-filled workspace kept per (device, stream) -- the current stream,
+    which is the call's (see _on_stream) -- so calls on different streams never
+    share counters or partial slots.  The attention kernels leave the counters
+    at zero, so it stays reusable in stream order."""
+    s = torch.cuda.current_stream(device)
+    key = (torch.device(device).index, s.cuda_stream)
     ws = _ws_cache.get(key)
     if ws is None or ws.numel() < nbytes:
         ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
@@ -341,9 +401,10 @@ def _check_mask(batch, draft_mask, dev):
     _same_device(draft_mask, dev)
 
 
+@_on_stream
 def spec_verify_attn(batch, q, kv, softmax_scale=None, out=None, out_dtype=None,
                      workspace=None, path=PATH_AUTO, num_workgroups=0, stream=None,
-                     draft_mask=None):
+                     draft_mask=None, wait_polls=0):
     """Verification attention of the drafts q [T, Hq, d] over the paged
     cache: causal among the drafts, or tree attention when draft_mask [T]
     (bit j: draft j of the sequence is visible, see tree_masks) is given.
@@ -362,7 +423,7 @@ def spec_verify_attn(batch, q, kv, softmax_scale=None, out=None, out_dtype=None,
     if workspace is None:
         workspace = _zeroed_workspace(q.device, nbytes)
     _need(workspace, "workspace")
-    cb, ckv, co = batch._c(), kv._c(), _opts(path, num_workgroups)
+    cb, ckv, co = batch._c(), kv._c(), _opts(path, num_workgroups, wait_polls)
     if draft_mask is None:
         _check("sva_spec_verify_attn", lib.sva_spec_verify_attn(
             ctypes.byref(cb), _ptr(q), _dtype_code(q, "q"), Hq, ctypes.byref(ckv),
@@ -375,12 +436,14 @@ def spec_verify_attn(batch, q, kv, softmax_scale=None, out=None, out_dtype=None,
             _ptr(draft_mask), float(softmax_scale), _ptr(out), _dtype_code(out, "out"),
             ctypes.byref(co), _ptr(workspace), workspace.numel() * workspace.element_size(),
             _stream(stream, q.device)))
+    _debug_check("spec_verify_attn", workspace, stream)
     return out
 
 
+@_on_stream
 def spec_verify_attn_append(batch, q, kv, k_new, v_new, softmax_scale=None, out=None,
                             out_dtype=None, workspace=None, path=PATH_AUTO, num_workgroups=0,
-                            stream=None, draft_mask=None):
+                            stream=None, draft_mask=None, wait_polls=0):
     """kv_append(batch, k_new, v_new, kv) then spec_verify_attn(...) in one
     call (one launch on the split-KV kernels): the new rows enter the cache
     and the drafts are verified.  Same results as the two calls."""
@@ -398,13 +461,14 @@ def spec_verify_attn_append(batch, q, kv, k_new, v_new, softmax_scale=None, out=
     if workspace is None:
         workspace = _zeroed_workspace(q.device, nbytes)
     _need(workspace, "workspace")
-    cb, ckv, co = batch._c(), kv._c(), _opts(path, num_workgroups)
+    cb, ckv, co = batch._c(), kv._c(), _opts(path, num_workgroups, wait_polls)
     _check("sva_spec_verify_attn_append", lib.sva_spec_verify_attn_append(
         ctypes.byref(cb), _ptr(q), _dtype_code(q, "q"), Hq, ctypes.byref(ckv), _ptr(k_new),
         _ptr(v_new), _dtype_code(k_new, "k_new"),
         _ptr(draft_mask) if draft_mask is not None else None, float(softmax_scale), _ptr(out),
         _dtype_code(out, "out"), ctypes.byref(co), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream, q.device)))
+    _debug_check("spec_verify_attn_append", workspace, stream)
     return out
 
 
@@ -414,6 +478,7 @@ def accept_workspace_bytes(batch, V):
     return int(lib.sva_accept_workspace_bytes(ctypes.byref(cb), int(V)))
 
 
+@_on_stream
 def accept_prefix(batch, logits, draft_ids, argmax_ids=None, accept_len=None, next_token=None,
                   workspace=None, stream=None):
     """Greedy longest-prefix acceptance.  logits [T+B, V] float32, draft_ids
@@ -447,6 +512,7 @@ def _int32_vec(t, n, what):
     _shape(t, (n,), what)
 
 
+@_on_stream
 def tree_masks(batch, parents, masks=None, stream=None):
     """Ancestor bitmasks of token trees: parents [T] int32 (-1: child of the
     last committed token, else an earlier node of the same sequence).
@@ -464,6 +530,7 @@ def tree_masks(batch, parents, masks=None, stream=None):
     return masks
 
 
+@_on_stream
 def accept_tree(batch, logits, draft_ids, parents, argmax_ids=None, accept_len=None,
                 next_token=None, accept_path=None, workspace=None, stream=None):
     """Greedy acceptance over token trees.  logits [T+B, V] float32 (row 0 of a
@@ -498,6 +565,7 @@ def accept_tree(batch, logits, draft_ids, parents, argmax_ids=None, accept_len=N
     return argmax_ids, accept_len, next_token, accept_path
 
 
+@_on_stream
 def kv_commit_path(batch, accept_len, accept_path, kv, stream=None):
     """Move each sequence's accepted branch (accept_path, from accept_tree) to
     the positions right after its committed context, every kv head."""
@@ -541,6 +609,7 @@ def _tree_commit_args(batch, logits, draft_ids, parents, kv, argmax_ids, accept_
     return args, (argmax_ids, accept_len, next_token, accept_path), keep
 
 
+@_on_stream
 def accept_tree_commit(batch, logits, draft_ids, parents, kv, argmax_ids=None, accept_len=None,
                        next_token=None, accept_path=None, workspace=None, stream=None):
     """accept_tree followed by kv_commit_path, in one call (one launch after the
@@ -584,6 +653,7 @@ def _check_stochastic(batch, target_logits, draft_logits, draft_ids, u_accept, u
                  next_token, batch.cu_q)
 
 
+@_on_stream
 def accept_stochastic(batch, target_logits, draft_logits, draft_ids, u_accept, u_sample,
                       temperature=1.0, accept_len=None, next_token=None, workspace=None,
                       stream=None):
@@ -612,6 +682,7 @@ def accept_stochastic(batch, target_logits, draft_logits, draft_ids, u_accept, u
     return accept_len, next_token
 
 
+@_on_stream
 def kvmu_apply(state, mode, arg=None, ctx_lens=None, stream=None):
     """Apply KVMU modes to the pointer triplets state [B, 3] int32 (valid,
     curr, ahead) in place.  mode: one KVMU_* value for every sequence, or a
@@ -639,14 +710,19 @@ def kvmu_apply(state, mode, arg=None, ctx_lens=None, stream=None):
 
 class _Prepared:
     """A call with every argument marshalled once; calling it only enqueues
-    the C entry point on the stream (current stream of the device by default)."""
+    the C entry point on the stream (current stream of the device by default).
+    Workspaces it allocates are filled before it returns (the fill is
+    synchronised), so any stream may run the call."""
 
-    def __init__(self, name, fn, args, device, keep):
+    def __init__(self, name, fn, args, device, keep, status_ws=None):
         self._name, self._fn, self._args, self._device = name, fn, args, device
         self._keep = keep                        # keeps tensors and structs alive
+        self._status_ws = status_ws
+        torch.cuda.current_stream(device).synchronize()
 
     def __call__(self, stream=None):
         _check(self._name, self._fn(*self._args, _stream(stream, self._device)))
+        _debug_check(self._name, self._status_ws, stream)
 
 
 def prepare_kv_append(batch, k_new, v_new, kv):
@@ -676,12 +752,13 @@ def prepare_spec_verify_attn(batch, q, kv, out, softmax_scale=None, workspace=No
                 _ptr(draft_mask), float(softmax_scale), _ptr(out), _dtype_code(out, "out"),
                 ctypes.byref(co), _ptr(workspace), workspace.numel() * workspace.element_size())
         return _Prepared("sva_spec_verify_attn_tree", lib.sva_spec_verify_attn_tree, args,
-                         q.device, (cb, ckv, co, batch, q, kv, out, workspace, draft_mask))
+                         q.device, (cb, ckv, co, batch, q, kv, out, workspace, draft_mask),
+                         workspace)
     args = (ctypes.byref(cb), _ptr(q), _dtype_code(q, "q"), Hq, ctypes.byref(ckv),
             float(softmax_scale), _ptr(out), _dtype_code(out, "out"), ctypes.byref(co),
             _ptr(workspace), workspace.numel() * workspace.element_size())
     return _Prepared("sva_spec_verify_attn", lib.sva_spec_verify_attn, args, q.device,
-                     (cb, ckv, co, batch, q, kv, out, workspace))
+                     (cb, ckv, co, batch, q, kv, out, workspace), workspace)
 
 
 def prepare_spec_verify_attn_append(batch, q, kv, k_new, v_new, out, softmax_scale=None,
@@ -705,7 +782,7 @@ def prepare_spec_verify_attn_append(batch, q, kv, k_new, v_new, out, softmax_sca
             workspace.numel() * workspace.element_size())
     return _Prepared("sva_spec_verify_attn_append", lib.sva_spec_verify_attn_append, args,
                      q.device, (cb, ckv, co, batch, q, kv, out, workspace, k_new, v_new,
-                                draft_mask))
+                                draft_mask), workspace)
 
 
 def prepare_accept_prefix(batch, logits, draft_ids, argmax_ids, accept_len, next_token,

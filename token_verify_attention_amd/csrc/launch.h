@@ -17,11 +17,13 @@ hipError_t launch_kv_append(const sva_batch* batch, const void* k_new, const voi
                             int src_dtype, const sva_paged_kv* kv, hipStream_t st);
 
 // Verification attention.  `num_wg` is the grid size; the workspace holds the
-// completion counters followed by the partial-result slots.
+// completion counters and the status word, followed by the partial-result
+// slots.
 struct AttnPlan {
   bool rows_kernel;     // row-block kernel (many query rows per pair); no workspace
   int rows_grid;        // its grid (an upper bound on the row blocks)
   int num_wg;
+  int wait_polls;       // bound on a split pair's wait for the others' partials
   int slot_rows;
   size_t counter_bytes;
   size_t slot_bytes;

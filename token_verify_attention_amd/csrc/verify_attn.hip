@@ -88,6 +88,8 @@ struct AttnParams {
   void* out;
   float* partials;
   int32_t* counters;
+  int32_t* status;      // workspace status word: bit 0 set when a split-pair wait gave up
+  int wait_polls;       // bound on the polls of that wait
   float scale_log2;     // softmax_scale * log2(e)
   int q_f32, out_f32;
   int B, T, Hq, Hkv, G, num_pages, max_pages, max_q;
@@ -1515,7 +1517,13 @@ __device__ __forceinline__ void merge_pair(const AttnParams& p, const Seg& sg, i
 // through combine_partial: the same operations whichever workgroup is last.
 // Saves the last workgroup a write, a fence and a reload of its own partial.
 // Split pairs of at most 32 query rows (one pass over the pages) take this
-// path; the last workgroup resets both counters.
+// path.  The last workgroup resets the arrival counter (every workgroup of
+// the pair has arrived) and takes the others' publications back off the
+// publication counter.  Its wait is bounded (p.wait_polls polls); if it
+// gives up, the pair's output rows are written as NaN (never a fold of
+// partials that may not be there), bit 0 of the status word is set, and the
+// publications still to come bring the counter back to zero before the
+// kernel ends, so the workspace stays reusable.
 constexpr int kSpinLimit = 1 << 22;
 
 // The current segment's pair: global page range [pb, pend) and total pages N,
@@ -1533,6 +1541,11 @@ __device__ __forceinline__ int logical_wg(int W) {
 __device__ __forceinline__ int& pair_last() {
   __shared__ int s_last;
   return s_last;
+}
+// Whether the last workgroup's wait for the others' partials succeeded.
+__device__ __forceinline__ int& pair_ok() {
+  __shared__ int s_ok;
+  return s_ok;
 }
 // The current pair's arrival counter and its number of segments.
 __device__ __forceinline__ int32_t* pair_arrivals(const AttnParams& p) {
@@ -1575,12 +1588,19 @@ __device__ __forceinline__ void merge_fused(const AttnParams& p, const Seg& sg, 
   }
   if (tid == 0) {
     const int others = pair_segments(wf, wl, N, p.W) - 1;
-    for (int n = 0; n < kSpinLimit; ++n) {
-      if (__hip_atomic_load(published, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= others) break;
+    int ok = 0;
+    for (int n = 0; n < p.wait_polls; ++n) {
+      if (__hip_atomic_load(published, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= others) {
+        ok = 1;
+        break;
+      }
       __builtin_amdgcn_s_sleep(2);
     }
+    if (!ok) __hip_atomic_fetch_or(p.status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    pair_ok() = ok;
   }
   __syncthreads();
+  const bool ok = pair_ok() != 0;
   float Mc[J], Lc[J];
   f32x4 Oc[J];
 #pragma unroll
@@ -1594,7 +1614,7 @@ __device__ __forceinline__ void merge_fused(const AttnParams& p, const Seg& sg, 
   constexpr int kBatch = 3;
   const int self = logical_wg(p.W);
   const int first_slot = slot_of(wf, pb, N, p.W);
-  int w = wf;
+  int w = ok ? wf : wl + 1;            // after a give-up nothing is read
   while (w <= wl) {
     int ws[kBatch];
     int n = 0;
@@ -1634,12 +1654,13 @@ __device__ __forceinline__ void merge_fused(const AttnParams& p, const Seg& sg, 
     const float inv = 1.f / Lc[j];
     f32x4 o = Oc[j];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) o[i] *= inv;
+    for (int i = 0; i < 4; ++i) o[i] = ok ? o[i] * inv : __builtin_nanf("");
     store_out4(p, out_row(p, sg, it % RW) * D + 4 * (it / RW), o);
   }
   if (tid == 0) {
+    const int others = pair_segments(wf, wl, N, p.W) - 1;
     __hip_atomic_store(p.counters + wf, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(published, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_fetch_add(published, -others, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -2171,8 +2192,11 @@ AttnPlan plan_verify_attn(const sva_batch* batch, const sva_paged_kv* kv, int Hq
                               pairs * seg_cap));
   }
   pl.num_wg = W;
+  pl.wait_polls = !opts || opts->wait_polls == 0 ? kSpinLimit : std::max(opts->wait_polls, 0);
   pl.slot_rows = std::max(batch->max_q, 1) * G;
-  pl.counter_bytes = size_t(2 * kMaxWorkgroups) * 4;   // arrival and publication counters
+  // arrival and publication counters, then the status word (256 bytes keep
+  // the partial slots aligned)
+  pl.counter_bytes = size_t(2 * kMaxWorkgroups) * 4 + 256;
   pl.slot_bytes = size_t(2) * W * pl.slot_rows * (kv->d + 2) * sizeof(float);
   pl.total_bytes = pl.counter_bytes + pl.slot_bytes;
   if (pl.rows_kernel) {                 // no workspace needed
@@ -2229,6 +2253,8 @@ hipError_t launch_verify_attn(const sva_batch* batch, const void* q, int q_dtype
   p.cu_q = batch->cu_q;
   p.out = out;
   p.counters = static_cast<int32_t*>(workspace);
+  p.status = p.counters + 2 * kMaxWorkgroups;
+  p.wait_polls = plan.wait_polls;
   p.partials = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.counter_bytes);
   p.scale_log2 = softmax_scale * kLog2e;
   p.q_f32 = q_dtype == SVA_F32;
