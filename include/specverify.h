@@ -239,6 +239,30 @@ sva_status sva_spec_verify_attn_tree(const sva_batch *batch, const void *q, int3
                                      int32_t out_dtype, const sva_verify_opts *opts,
                                      void *workspace, size_t workspace_bytes, void *stream);
 
+/* sva_spec_verify_attn for callers that cannot allocate -- code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc: the
+ * same kernels and results, with the workspace taken from a static device
+ * array of the library instead of an argument.  Every other argument is as
+ * for sva_spec_verify_attn (causal drafts; no tree mask).
+ *   - The array holds 16 MiB per device (allocated when the library's code is
+ *     loaded on that device, held until the process ends).  A shape whose
+ *     workspace (sva_verify_workspace_bytes) exceeds it returns
+ *     SVA_ERR_UNSUPPORTED before anything is enqueued; at d = 128 and 256
+ *     workgroups that is above 62 query rows (k_b * G) per pair.
+ *   - The first call on a device takes the array's address and enqueues one
+ *     small kernel on `stream` that zeroes its counters; no call allocates
+ *     memory.
+ *   - Every call on a device shares that device's array, which keeps the last
+ *     call's contents: calls that may overlap on one device (different streams
+ *     or threads without ordering) race and give undefined results.
+ *   - A wait that gives up writes NaN to the rows of its pair, as documented
+ *     for sva_verify_opts.wait_polls; the array's status word is not visible
+ *     to the caller. */
+sva_status sva_spec_verify_attn_noalloc(const sva_batch *batch, const void *q, int32_t q_dtype,
+                                        int32_t Hq, const sva_paged_kv *kv, float softmax_scale,
+                                        void *out, int32_t out_dtype,
+                                        const sva_verify_opts *opts, void *stream);
+
 /* Append, then verify, in one call: the same results as sva_kv_append(batch,
  * k_new, v_new, src_dtype, kv) followed by sva_spec_verify_attn (draft_mask
  * NULL) or sva_spec_verify_attn_tree (draft_mask given) on the same stream,

@@ -28,7 +28,7 @@ __all__ = [
     "tree_masks", "accept_tree", "kv_commit_path", "accept_tree_commit", "accept_stochastic",
     "accept_stochastic_workspace_bytes", "kvmu_apply", "KVMU_INIT", "KVMU_SPECULATE",
     "KVMU_ACCEPT", "KVMU_ROLLBACK", "KVMU_PREFIX", "verify_status", "STATUS_OFFSET",
-    "spec_verify_attn_append",
+    "spec_verify_attn_append", "spec_verify_attn_noalloc",
 ]
 
 KVMU_INIT, KVMU_SPECULATE, KVMU_ACCEPT, KVMU_ROLLBACK, KVMU_PREFIX = 0, 1, 2, 3, 4
@@ -103,6 +103,9 @@ def load():
         lib.sva_spec_verify_attn.restype = ctypes.c_int
         lib.sva_spec_verify_attn.argtypes = [vp, vp, i32, i32, vp, ctypes.c_float, vp, i32, vp,
                                              vp, sz, vp]
+        lib.sva_spec_verify_attn_noalloc.restype = ctypes.c_int
+        lib.sva_spec_verify_attn_noalloc.argtypes = [vp, vp, i32, i32, vp, ctypes.c_float, vp,
+                                                     i32, vp, vp]
         lib.sva_accept_workspace_bytes.restype = sz
         lib.sva_accept_workspace_bytes.argtypes = [vp, i32]
         lib.sva_accept_prefix.restype = ctypes.c_int
@@ -437,6 +440,29 @@ def spec_verify_attn(batch, q, kv, softmax_scale=None, out=None, out_dtype=None,
             ctypes.byref(co), _ptr(workspace), workspace.numel() * workspace.element_size(),
             _stream(stream, q.device)))
     _debug_check("spec_verify_attn", workspace, stream)
+    return out
+
+
+@_on_stream
+def spec_verify_attn_noalloc(batch, q, kv, softmax_scale=None, out=None, out_dtype=None,
+                             path=PATH_AUTO, num_workgroups=0, stream=None, wait_polls=0):
+    """spec_verify_attn with the library's static scratch as the workspace
+    (sva_spec_verify_attn_noalloc: the entry point itself allocates nothing;
+    pass `out` to keep this wrapper from allocating it either).  Calls that may
+    overlap on one device race on that scratch."""
+    lib = load()
+    _need(q, "q", 3)
+    Hq, d = int(q.shape[1]), int(q.shape[2])
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
+    _check_attn(batch, q, kv, out)
+    cb, ckv, co = batch._c(), kv._c(), _opts(path, num_workgroups, wait_polls)
+    _check("sva_spec_verify_attn_noalloc", lib.sva_spec_verify_attn_noalloc(
+        ctypes.byref(cb), _ptr(q), _dtype_code(q, "q"), Hq, ctypes.byref(ckv),
+        float(softmax_scale), _ptr(out), _dtype_code(out, "out"), ctypes.byref(co),
+        _stream(stream, q.device)))
     return out
 
 

@@ -14,6 +14,14 @@
 #include "launch.h"
 #include "specverify.h"
 
+// Static scratch of sva_spec_verify_attn_noalloc: one array per device, loaded
+// with the code object and held until the process ends -- the attention
+// workspace (completion counters, status word, partial slots) of callers that
+// cannot allocate.  Kernels get its device address, taken once per device with
+// hipGetSymbolAddress; in host code the array's name is not a device address.
+constexpr size_t kScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -103,6 +111,46 @@ sva_status check_kv(const sva_paged_kv* kv, bool need_scales) {
 }
 
 hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+// ---- static scratch of sva_spec_verify_attn_noalloc --------------------------
+// Counters and status word at the start of the workspace (must start at zero).
+constexpr int kScratchClearWords = (2 * 4096 * 4 + 256) / 4;
+
+__global__ void clear_words_kernel(int32_t* p, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0;
+}
+
+struct ScratchSlot {
+  bool ready = false;
+  void* ptr = nullptr;
+};
+ScratchSlot g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// The current device's scratch address.  The first call on a device looks the
+// address up and clears the counters on `stream` (a kernel, so the clear is
+// ordered before the call's own launch and may be captured into a graph).
+sva_status scratch_for_current_device(void** out, hipStream_t stream) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(SVA_ERR_UNSUPPORTED, "device index %d", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  ScratchSlot& sl = g_scratch[dev];
+  if (!sl.ready) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    hipLaunchKernelGGL(clear_words_kernel, dim3((kScratchClearWords + 255) / 256), dim3(256), 0,
+                       stream, static_cast<int32_t*>(ptr), kScratchClearWords);
+    e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "scratch clear launch");
+    sl.ptr = ptr;
+    sl.ready = true;
+  }
+  *out = sl.ptr;
+  return SVA_OK;
+}
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
@@ -243,6 +291,26 @@ sva_status sva_spec_verify_attn(const sva_batch* batch, const void* q, int32_t q
   g_last_error.clear();
   return verify_attn(batch, q, q_dtype, Hq, kv, nullptr, softmax_scale, out, out_dtype, opts,
                      workspace, workspace_bytes, stream);
+}
+
+sva_status sva_spec_verify_attn_noalloc(const sva_batch* batch, const void* q, int32_t q_dtype,
+                                        int32_t Hq, const sva_paged_kv* kv, float softmax_scale,
+                                        void* out, int32_t out_dtype, const sva_verify_opts* opts,
+                                        void* stream) {
+  g_last_error.clear();
+  if (sva_status s = check_attn_shape(batch, kv, Hq, opts, false)) return s;
+  const DeviceInfo* dev;
+  if (sva_status s = current_device(&dev)) return s;
+  const size_t need = sva::plan_verify_attn(batch, kv, Hq, dev->num_cus, opts).total_bytes;
+  if (need > kScratchBytes)
+    return fail(SVA_ERR_UNSUPPORTED,
+                "this call needs %zu bytes of workspace; the static scratch holds %zu "
+                "(fewer workgroups or fewer query rows per pair fit)",
+                need, kScratchBytes);
+  void* ws = nullptr;
+  if (sva_status s = scratch_for_current_device(&ws, as_stream(stream))) return s;
+  return verify_attn(batch, q, q_dtype, Hq, kv, nullptr, softmax_scale, out, out_dtype, opts, ws,
+                     kScratchBytes, stream);
 }
 
 sva_status sva_spec_verify_attn_append(const sva_batch* batch, const void* q, int32_t q_dtype,
