@@ -13,25 +13,34 @@ One step = one pass of the whole hot path over one synthetic batch:
   sequence, the attention shape of a 7B process reward model): kv_append ->
   verification attention, whose roofline is MFMA throughput (the reward
   model's threshold is not part of this path).
-Default workload: 7B-MHA shape, B=8, Hq=Hkv=32, d=128, S=2048, k=4, bf16 paged
-KV (16-token pages, random page permutation).  That shape names no vocabulary;
-acceptance runs over fp32 logits [B*(k+1), 128256] with drafts agreeing with
-the target argmax with probability 0.8 (the ragged serving batch's vocabulary
-and agreement rate).
+
+Default workload: the ragged serving batch -- B=64, S_b ~ U[256, 16384],
+k_b ~ U{1..8}, Hq=32, Hkv=8, d=128, bf16 paged KV (16-token pages, random page
+permutation), acceptance over fp32 logits [sum(k_b+1), 128256] with drafts
+agreeing with the target argmax with probability 0.8 -- the largest of the
+single-GPU workloads.  The same run also times the other workloads (tiny,
+7B MHA, 8B GQA, 70B-shaped INT8) under "configs", and a streaming-read probe
+kernel as the achievable ceiling of the KV stream.
 
 Prints ONE JSON line.  `value` is verified draft tokens per second for whole
-steps (inputs resident in HBM); `roofline` is the attention kernel's KV bytes
-over its own average launch time against 8 TB/s; `cpu_baseline` is the fp64
-oracle on the host.  The attention kernel's average launch time comes from
-the same number of back-to-back launches of the attention call alone
-(sva_spec_verify_attn, no append) after the timed steps, between one pair of
-HIP events on its stream; `roofline.traffic` is HBM traffic from committed rocprofv3
-counter readings (null when they no longer match the kernel's sources).
+steps (inputs resident in HBM); `goodput_accepted_tokens_per_s` counts the
+tokens the steps emit (sum of n_b + 1); `roofline` is the attention kernel's
+KV bytes over its own average launch time against 8 TB/s; `cpu_baseline` is
+the fp64 oracle on the host's cores.  The attention kernel's average launch
+time comes from the same number of back-to-back launches of the attention
+call alone (sva_spec_verify_attn, no append) after the timed steps, between
+one pair of HIP events on its stream; `roofline.traffic` is HBM traffic from
+committed rocprofv3 counter readings (null when they no longer match the
+kernel's sources).
+
+The CPU baseline's worker processes are forked, with the host copy of the
+workload, before anything touches the GPU; they never use it.
 """
 import argparse
 import dataclasses
 import json
 import math
+import multiprocessing
 import os
 import sys
 import time
@@ -43,6 +52,8 @@ METRIC = "verify-attn KV HBM GB/s (% of peak) and verified draft tokens/sec, 1 G
 HBM_PEAK_GBPS = 8000.0
 MALL_BYTES = 256 << 20
 MFMA_BF16_PEAK_TFLOPS = 2500.0
+MAX_CPU_WORKERS = 16
+EXTRA_CONFIGS = ("tiny", "mha7b", "gqa8b", "gqa70b_int8")
 
 
 def log(*a):
@@ -114,6 +125,162 @@ def measured_traffic(workload, attn_ms):
     return {"bytes": nbytes, "gbps": nbytes / (attn_ms * 1e-3) / 1e9}
 
 
+def step_workload(wl, name):
+    """The workload as the step runs it: shapes without a vocabulary get the
+    ragged batch's (128256 tokens, 80 % agreement) for their acceptance."""
+    w = wl.WORKLOADS[name]
+    if w.vocab is None and name not in wl.LONG_WORKLOADS:
+        w = dataclasses.replace(w, vocab=128256, match_p=0.8)
+    return w
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the fp64 oracle on the host's cores
+# ---------------------------------------------------------------------------
+
+_HOST = {}          # the host copy of the workload; inherited by forked workers
+
+
+def _attn_share(share, budget_s):
+    """Worker: the oracle's attention over this worker's (sequence, kv-head)
+    pairs, taken in order and repeated until the time budget is spent."""
+    import oracle
+    from threadpoolctl import threadpool_limits
+    h = _HOST
+    n = 0
+    t0 = time.perf_counter()
+    with threadpool_limits(limits=1):
+        while True:
+            oracle.spec_verify_attn(h["q"], h["k"], h["v"], h["bt"], h["ctx"], h["cu"],
+                                    h["scale"], select=[share[n % len(share)]], **h["kw"])
+            n += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+    return n, time.perf_counter() - t0
+
+
+class CpuBaseline:
+    """The oracle as it stands, on the same workload drawn on the host (same
+    recipe and seeds, the host's generator), timed per step:
+      append     oracle.kv_append of the whole batch, once, one core;
+      attention  every (sequence, kv-head) pair, split over `cores` forked
+                 worker processes (pair i to worker i mod cores), each
+                 repeating its share until its time budget is spent; a pass
+                 takes as long as the slowest worker's share;
+      acceptance every sequence (greedy prefix, tree walk + branch commit, or
+                 rejection sampling), one core, repeated until 0.5 s is spent.
+    Built before the GPU is touched (the workers are forked here)."""
+
+    def __init__(self, wl, w, cores):
+        import oracle
+        from threadpoolctl import threadpool_limits
+        self.w, self.cores = w, cores
+        tree = w.name in wl.TREE_WORKLOADS
+        long = w.name in wl.LONG_WORKLOADS
+        sampled = w.name in wl.SAMPLED_WORKLOADS
+        t0 = time.perf_counter()
+        case = wl.make_case(w, device="cpu", seed_offset=0, with_logits=not (tree or long))
+        np_ = lambda t: (t.float() if t.dtype == torch.bfloat16 else t).numpy()
+        if tree:
+            case["parents"] = wl.make_tree(case["k_host"], device="cpu", seed=w.ident)
+            case.update(wl.make_tree_logits(w, case["k_host"], case["parents"], device="cpu"))
+        bt, ctx, cu = np_(case["block_table"]), np_(case["ctx_lens"]), np_(case["cu_q"])
+        kp, vp = np_(case.pop("k_pool")), np_(case.pop("v_pool"))
+        kn, vn = np_(case["k_new"]), np_(case["v_new"])
+        self.T, self.B = case["T"], case["B"]
+        self.gen_s = time.perf_counter() - t0
+        with threadpool_limits(limits=1):
+            kw = {}
+            if w.kv_dtype == "int8":
+                # the INT8 cache holds oracle codes of the fp32 pool (cache fill, untimed)
+                P, H = kp.shape[:2]
+                kc, ksc = oracle.kv_quant_int8(kp.reshape(-1, w.d))
+                vc, vsc = oracle.kv_quant_int8(vp.reshape(-1, w.d))
+                t0 = time.perf_counter()
+                kp, vp, ksc, vsc = oracle.kv_append(kn, vn, kc.reshape(kp.shape),
+                                                    vc.reshape(vp.shape), bt, ctx, cu, "int8",
+                                                    ksc.reshape(P, H, 16), vsc.reshape(P, H, 16))
+                kw = dict(k_scale=ksc, v_scale=vsc)
+            else:
+                t0 = time.perf_counter()
+                kp, vp, _, _ = oracle.kv_append(kn, vn, kp, vp, bt, ctx, cu, w.kv_dtype)
+            self.t_append = time.perf_counter() - t0
+            if tree:
+                kw["draft_mask"] = oracle.ancestor_masks(np_(case["parents"]), cu)
+        self._acc_args = (wl, case, np_, kp, vp, bt, ctx, cu, tree, long, sampled)
+        _HOST.update(q=np_(case["q"]), k=kp, v=vp, bt=bt, ctx=ctx, cu=cu,
+                     scale=1.0 / math.sqrt(w.d), kw=kw)
+        self.pairs = [(b, g) for b in range(self.B) for g in range(w.Hkv)]
+        self.pool = multiprocessing.get_context("fork").Pool(cores)
+
+    def _time_acceptance(self, wl, case, np_, kp, vp, bt, ctx, cu, tree, long, sampled):
+        import oracle
+        if long:
+            return 0.0, 0
+        w = self.w
+        logits, drafts = np_(case["logits"]), np_(case["draft_ids"])
+        if sampled:
+            dlog = np_(wl.make_draft_logits(case["logits"], case["k_host"], device="cpu",
+                                            seed=w.ident))
+            ua, us = (np_(t) for t in wl.make_uniforms(self.T, self.B, device="cpu",
+                                                       seed=w.ident))
+        parents = np_(case["parents"]) if tree else None
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            for b in range(self.B):
+                r0, r1 = int(cu[b]) + b, int(cu[b + 1]) + b + 1
+                q0, q1 = int(cu[b]), int(cu[b + 1])
+                one = np.array([0, q1 - q0])
+                if tree:
+                    _, n, _, path = oracle.accept_tree(logits[r0:r1], drafts[q0:q1],
+                                                       parents[q0:q1], one)
+                    for pool in (kp, vp):       # after the attention: the pools may change
+                        oracle.commit_path(pool, bt[b:b + 1], ctx[b:b + 1], one, n, path)
+                elif sampled:
+                    oracle.accept_stochastic(logits[r0:r1], dlog[q0:q1], drafts[q0:q1], one, 1.0,
+                                             ua[q0:q1], us[b:b + 1])
+                else:
+                    oracle.accept_prefix(logits[r0:r1], drafts[q0:q1], one)
+            reps += 1
+            if time.perf_counter() - t0 > 0.5:
+                break
+        return (time.perf_counter() - t0) / reps, reps
+
+    def run(self, budget_s):
+        shares = [self.pairs[i::self.cores] for i in range(self.cores)]
+        shares = [s for s in shares if s]
+        res = self.pool.starmap(_attn_share, [(s, budget_s) for s in shares])
+        self.pool.close()
+        self.pool.join()
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            self.t_accept, self.accept_reps = self._time_acceptance(*self._acc_args)
+        # seconds per pass over each worker's share; the pass ends with the slowest
+        per_pass = [t / (n / len(s)) for (n, t), s in zip(res, shares)]
+        t_attn = max(per_pass)
+        n_eval = sum(n for n, _ in res)
+        step_s = self.t_append + t_attn + self.t_accept
+        w = self.w
+        return {
+            "value": self.T / step_s, "unit": "verified draft tokens/s", "cores": len(shares),
+            "kind": "oracle",
+            "sample": (f"{n_eval} (sequence, kv-head) attention pairs over {len(shares)} worker "
+                       f"processes (each repeating its share of the batch's {len(self.pairs)} "
+                       f"pairs for {budget_s:.0f} s; a pass takes {t_attn * 1e3:.1f} ms, the slowest "
+                       f"share), the whole append once ({self.t_append * 1e3:.1f} ms, one core)"
+                       + ("" if w.name == "prm7b_step" else
+                          f", acceptance of all {self.B} sequences x {self.accept_reps} "
+                          f"({self.t_accept * 1e3:.2f} ms each, one core)")
+                       + f"; inputs drawn on the host with the workload's recipe and seeds; "
+                         f"numpy BLAS limited to 1 thread per process"),
+            "seconds_per_step_estimate": step_s,
+        }
+
+
+# ---------------------------------------------------------------------------
+# GPU measurement
+# ---------------------------------------------------------------------------
+
 class Inputs:
     """One resident input set and the prepared calls of one step."""
 
@@ -139,6 +306,7 @@ class Inputs:
         self.ids = torch.empty(case["T"] + B, dtype=torch.int32, device=dev)
         self.alen = torch.empty(B, dtype=torch.int32, device=dev)
         self.nxt = torch.empty(B, dtype=torch.int32, device=dev)
+        self.has_accept = not long
         self.append = tva.prepare_kv_append(self.batch, case["k_new"], case["v_new"], self.kv)
         if tree:
             self.masks = torch.empty(case["T"], dtype=torch.int32, device=dev)
@@ -187,114 +355,136 @@ class Inputs:
                     self.batch, case["q"], self.kv, case["k_new"], case["v_new"], self.out)
                 self.append = lambda stream=None: None
 
+    def step(self):
+        self.append()
+        self.step_attn()
+        self.accept()
 
-def copy_probe_gbps(dev, nbytes=1 << 30, reps=10):
-    """A plain device-to-device copy, the achievable-bandwidth reference."""
-    a = torch.empty(nbytes, dtype=torch.uint8, device=dev)
-    b = torch.empty_like(a)
-    b.copy_(a)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    def emitted_tokens(self):
+        """Tokens the step emits: sum over sequences of n_b + 1 (the accepted
+        drafts and the target's token after them).  The step's inputs are the
+        same every time, so every step of this set emits the same count."""
+        return int(self.alen.sum().item()) + self.case["B"] if self.has_accept else 0
+
+
+def measure(tva, wl, w, dev, steps, warmup, sets=0):
+    """Time `steps` whole steps (inputs resident in HBM), then the same number
+    of back-to-back attention launches and the same launches one by one."""
+    inp0 = Inputs(tva, wl, w, 0, dev)
+    nsets = sets
+    if not nsets:       # enough independent sets that the 256 MB MALL cannot hold them
+        kvb0 = kv_bytes(w, inp0.case["ctx_host"], inp0.case["k_host"])
+        nsets = max(1, min(4, math.ceil(3 * MALL_BYTES / max(kvb0, 1))))
+    ins = [inp0] + [Inputs(tva, wl, w, s_, dev) for s_ in range(1, nsets)]
+    set_bytes = [kv_bytes(w, x.case["ctx_host"], x.case["k_host"]) for x in ins]
+    set_tokens = [x.case["T"] for x in ins]
+    stream = torch.cuda.current_stream(dev)
+    for s in range(warmup):
+        ins[s % nsets].step()
     torch.cuda.synchronize()
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    # Timed steps: nothing but the calls of each step on the stream (an event
+    # between kernels costs a cache flush and a few microseconds of idle GPU).
+    t0, t1 = ev(), ev()
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for s in range(steps):
+        ins[s % nsets].step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    emitted = [x.emitted_tokens() for x in ins]
+    tokens_all = sum(set_tokens[s % nsets] for s in range(steps))
+    emitted_all = sum(emitted[s % nsets] for s in range(steps))
+    # attention alone, back to back, same rotation
+    a0, a1 = ev(), ev()
+    torch.cuda.synchronize()
+    a0.record(stream)
+    for s in range(steps):
+        ins[s % nsets].attn()
+    a1.record(stream)
+    torch.cuda.synchronize()
+    attn_ms = a0.elapsed_time(a1) / steps
+    marks = [ev() for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    marks[0].record(stream)
+    for s in range(steps):
+        ins[s % nsets].attn()
+        marks[s + 1].record(stream)
+    torch.cuda.synchronize()
+    per_launch = np.array([marks[i].elapsed_time(marks[i + 1]) for i in range(steps)]) * 1e3
+    kvb = sum(set_bytes[s % nsets] for s in range(steps)) / steps
+    flops = sum(attn_flops(w, x.case["ctx_host"], x.case["k_host"]) for x in ins) / nsets
+    ctx, ks = ins[0].case["ctx_host"], ins[0].case["k_host"]
+    r = {
+        "nsets": nsets, "ms_per_step": total_ms / steps,
+        "tokens_per_s": tokens_all / (total_ms * 1e-3),
+        "draft_tokens_per_step": tokens_all / steps,
+        "emitted_tokens_per_step": emitted_all / steps,
+        "goodput": emitted_all / (total_ms * 1e-3),
+        "attn_ms": attn_ms,
+        "attn_us_per_launch": {"p10": float(np.percentile(per_launch, 10)),
+                               "p50": float(np.median(per_launch)),
+                               "p90": float(np.percentile(per_launch, 90))},
+        "kv_bytes": kvb, "kv_gbps": kvb / (attn_ms * 1e-3) / 1e9,
+        "flops": flops, "tflops": flops / (attn_ms * 1e-3) / 1e12,
+        "other_bytes": other_bytes(w, ctx, ks, int(ins[0].case["block_table"].shape[1])),
+    }
+    del ins, inp0
+    torch.cuda.empty_cache()
+    return r
+
+
+def probe_ceiling(tva, dev, num_cus, nbytes=1 << 30, reps=10):
+    """Best read rate of the streaming-read probe kernel over a few launch
+    shapes (a 1 GiB buffer, 4x the MALL), and a plain torch device copy."""
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    buf.fill_(1)
+    sink = torch.empty(65536 * 4, dtype=torch.int32, device=dev)
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    shapes = [(0, num_cus * k) for k in (4, 8, 16)] + [(1, num_cus), (1, 2 * num_cus)]
+    rates = {}
+    for mode, nwg in shapes:
+        tva.stream_read_probe(buf, mode, nwg, sink)
+        torch.cuda.synchronize()
+        e0, e1 = ev(), ev()
+        e0.record()
+        for _ in range(reps):
+            tva.stream_read_probe(buf, mode, nwg, sink)
+        e1.record()
+        torch.cuda.synchronize()
+        rates[f"{'regs' if mode == 0 else 'lds'}_wg{nwg}"] = (
+            nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    b = torch.empty_like(buf)
+    b.copy_(buf)
+    torch.cuda.synchronize()
+    e0, e1 = ev(), ev()
     e0.record()
     for _ in range(reps):
-        b.copy_(a)
+        b.copy_(buf)
     e1.record()
     torch.cuda.synchronize()
-    return 2 * nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    copy = 2 * nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del buf, b
+    torch.cuda.empty_cache()
+    best = max(rates, key=rates.get)
+    return {"read_gbps": rates[best], "best_shape": best, "shapes": rates,
+            "torch_copy_gbps_read_plus_write": copy}
 
 
-def cpu_baseline(wl, w, dev, budget_s):
-    """The fp64 oracle (as it stands) on a bounded sample of the same step:
-    append + attention over (sequence, kv-head) pairs taken in order (cycling
-    over the batch when one pass is shorter) until the time budget is spent, +
-    acceptance over the sampled sequences' logit rows (repeated once per whole
-    pass).  Scaled to draft tokens per second of the whole batch.  The inputs
-    are regenerated from the seed of input set 0, so nothing the GPU wrote is
-    used."""
-    import oracle
-    from threadpoolctl import threadpool_limits
-
-    tree = w.name in wl.TREE_WORKLOADS
+def describe(w, wl):
     long = w.name in wl.LONG_WORKLOADS
-    case = wl.make_case(w, device=dev, seed_offset=0, with_logits=not (tree or long))
-    np_ = lambda t: (t.float() if t.dtype == torch.bfloat16 else t).cpu().numpy()
-    if tree:
-        case["parents"] = wl.make_tree(case["k_host"], device=dev, seed=w.ident)
-        case.update(wl.make_tree_logits(w, case["k_host"], case["parents"], device=dev))
-        parents = np_(case["parents"])
-    sampled = w.name in wl.SAMPLED_WORKLOADS
-    if sampled:
-        dlog = np_(wl.make_draft_logits(case["logits"], case["k_host"], device=dev, seed=w.ident))
-        ua, us = (np_(t) for t in wl.make_uniforms(case["T"], case["B"], device=dev, seed=w.ident))
-    kp, vp = np_(case["k_pool"]), np_(case["v_pool"])
-    bt, ctx, cu = np_(case["block_table"]), np_(case["ctx_lens"]), np_(case["cu_q"])
-    qn = np_(case["q"])
-    kn, vn = np_(case["k_new"]), np_(case["v_new"])
-    logits = np_(case["logits"]) if "logits" in case else None
-    drafts = np_(case["draft_ids"]) if "draft_ids" in case else None
-    scale = 1.0 / math.sqrt(w.d)
-    B, H = case["B"], w.Hkv
-    pairs = [(b, g) for b in range(B) for g in range(H)]
-    n_eval, t_attn = 0, 0.0
-    with threadpool_limits(limits=1):
-        t0 = time.perf_counter()
-        if w.kv_dtype == "int8":
-            # the INT8 cache holds oracle codes of the fp32 pool (cache fill, untimed)
-            P = kp.shape[0]
-            kc, ksc = oracle.kv_quant_int8(kp.reshape(-1, w.d))
-            vc, vsc = oracle.kv_quant_int8(vp.reshape(-1, w.d))
-            kp, vp = kc.reshape(kp.shape), vc.reshape(vp.shape)
-            sc = dict(k_scale=ksc.reshape(P, H, 16), v_scale=vsc.reshape(P, H, 16))
-            t0 = time.perf_counter()
-            kp, vp, k_s, v_s = oracle.kv_append(kn, vn, kp, vp, bt, ctx, cu, "int8",
-                                                sc["k_scale"], sc["v_scale"])
-            sc = dict(k_scale=k_s, v_scale=v_s)
-        else:
-            sc = {}
-            kp, vp, _, _ = oracle.kv_append(kn, vn, kp, vp, bt, ctx, cu, w.kv_dtype)
-        t_append = time.perf_counter() - t0
-        t0 = time.perf_counter()
-        if tree:
-            sc["draft_mask"] = oracle.ancestor_masks(parents, cu)
-        while True:
-            oracle.spec_verify_attn(qn, kp, vp, bt, ctx, cu, scale,
-                                    select=[pairs[n_eval % len(pairs)]], **sc)
-            n_eval += 1
-            if time.perf_counter() - t0 > budget_s:
-                break
-        t_attn = time.perf_counter() - t0
-        passes = n_eval / len(pairs)
-        reps = max(1, int(passes))                  # acceptance passes
-        seqs = sorted({b for b, _ in pairs[:min(n_eval, len(pairs))]})
-        t0 = time.perf_counter()
-        for b in ([] if long else seqs * reps):
-            r0, r1 = int(cu[b]) + b, int(cu[b + 1]) + b + 1
-            one = np.array([0, int(cu[b + 1] - cu[b])])
-            if tree:
-                _, n, _, path = oracle.accept_tree(logits[r0:r1], drafts[int(cu[b]):int(cu[b + 1])],
-                                                   parents[int(cu[b]):int(cu[b + 1])], one)
-                for pool in (kp, vp):
-                    oracle.commit_path(pool, bt[b:b + 1], ctx[b:b + 1], one, n, path)
-            elif sampled:
-                q0, q1 = int(cu[b]), int(cu[b + 1])
-                oracle.accept_stochastic(logits[r0:r1], dlog[q0:q1], drafts[q0:q1], one, 1.0,
-                                         ua[q0:q1], us[b:b + 1])
-            else:
-                oracle.accept_prefix(logits[r0:r1], drafts[int(cu[b]):int(cu[b + 1])], one)
-        t_acc = time.perf_counter() - t0
-    frac_seqs = len(seqs) / B
-    step_s = t_append + t_attn / passes + t_acc / (reps * frac_seqs)
-    tokens = case["T"]
-    return {
-        "value": tokens / step_s, "unit": "verified draft tokens/s", "cores": 1, "kind": "oracle",
-        "sample": (f"{n_eval} (sequence, kv-head) attention pairs, {passes:.2f} passes over the "
-                   f"batch's {len(pairs)} ({t_attn:.1f} s), "
-                   + ("" if long else f"acceptance{' and branch commit' if tree else ''} for "
-                      f"{len(seqs)} of {B} sequences x {reps} ({t_acc:.1f} s), ")
-                   + "the whole append once; scaled to one step of the full batch; numpy BLAS "
-                     "limited to 1 thread"),
-        "seconds_per_step_estimate": step_s,
-    }
+    if long:
+        acc = "no acceptance (a reward-model threshold)"
+    elif w.name in wl.SAMPLED_WORKLOADS:
+        acc = ("stochastic acceptance (rejection sampling, temperature 1) over fp32 target logits "
+               f"[sum(k_b+1), {w.vocab}] and drafter logits [sum(k_b), {w.vocab}]")
+    else:
+        acc = f"acceptance over fp32 logits [sum(k_b+1), {w.vocab}]"
+    return (f"{w.name}: B={w.B}, Hq={w.Hq}, Hkv={w.Hkv}, d={w.d}, S={w.ctx}, k={w.k}"
+            f"{' drafts per step (step-level verification)' if long else ''}"
+            f"{' token-tree nodes' if w.name in wl.TREE_WORKLOADS else ''}, "
+            f"{w.kv_dtype} paged KV (16-token pages, random page permutation); {acc}")
 
 
 def main():
@@ -302,140 +492,102 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="mha7b")
+    ap.add_argument("--workload", default="ragged")
     ap.add_argument("--sets", type=int, default=0, help="input sets rotated (0: enough to defeat the 256 MB MALL)")
-    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle attention")
+    ap.add_argument("--cpu-budget", type=float, default=12.0,
+                    help="seconds of oracle attention per CPU worker")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip timing the other workloads (the 'configs' key)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
               "(this path has no multi-GPU mode).", file=sys.stderr)
         sys.exit(2)
 
-    import token_verify_attention_amd as tva
     from token_verify_attention_amd import workloads as wl
+    w = step_workload(wl, args.workload)
+    long = w.name in wl.LONG_WORKLOADS
 
+    # The CPU baseline's host inputs and worker processes come first: the
+    # workers are forked before this process touches the GPU.
+    cpu = None
+    if not args.no_cpu_baseline:
+        cores = max(1, min(len(os.sched_getaffinity(0)), MAX_CPU_WORKERS))
+        log(f"cpu baseline: host inputs and {cores} workers ...")
+        cpu = CpuBaseline(wl, w, cores)
+
+    import token_verify_attention_amd as tva
     tva.load()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    w = wl.WORKLOADS[args.workload]
-    long = w.name in wl.LONG_WORKLOADS
-    if w.vocab is None and not long:
-        w = dataclasses.replace(w, vocab=128256, match_p=0.8)
+    num_cus = torch.cuda.get_device_properties(dev).multi_processor_count
 
-    sets = [Inputs(tva, wl, w, 0, dev)]
-    nsets = args.sets
-    if not nsets:       # enough independent sets that the 256 MB MALL cannot hold them
-        kvb0 = kv_bytes(w, sets[0].case["ctx_host"], sets[0].case["k_host"])
-        nsets = max(1, min(4, math.ceil(3 * MALL_BYTES / max(kvb0, 1))))
-    sets += [Inputs(tva, wl, w, s_, dev) for s_ in range(1, nsets)]
-    nsets = len(sets)
-    set_bytes = [kv_bytes(w, x.case["ctx_host"], x.case["k_host"]) for x in sets]
-    set_tokens = [x.case["T"] for x in sets]
-    kvb = sum(set_bytes) / nsets
-    log(f"workload {w.name}: KV bytes per launch {kvb / 1e6:.1f} MB, {nsets} input set(s)")
-    ctx, ks = sets[0].case["ctx_host"], sets[0].case["k_host"]
-    max_pages = int(sets[0].case["block_table"].shape[1])
-    T = sum(ks)
+    log(f"workload {w.name}: timing {args.steps} steps")
+    m = measure(tva, wl, w, dev, args.steps, args.warmup, args.sets)
+    traffic = measured_traffic(w.name, m["attn_ms"])
+    probe = probe_ceiling(tva, dev, num_cus)
+    log(f"probe ceiling {probe['read_gbps']:.0f} GB/s ({probe['best_shape']})")
 
-    stream = torch.cuda.current_stream(dev)
-    for s in range(args.warmup):
-        inp = sets[s % nsets]
-        inp.append()
-        inp.step_attn()
-        inp.accept()
-    torch.cuda.synchronize()
+    configs = {}
+    if not args.no_configs and w.name == "ragged":
+        for name in EXTRA_CONFIGS:
+            log(f"config {name}")
+            wc = step_workload(wl, name)
+            r = measure(tva, wl, wc, dev, args.steps, args.warmup)
+            configs[name] = {
+                "workload": describe(wc, wl),
+                "attn_us": r["attn_ms"] * 1e3, "kv_bytes_per_launch": r["kv_bytes"],
+                "kv_hbm_gbps": r["kv_gbps"], "kv_frac_of_peak": r["kv_gbps"] / HBM_PEAK_GBPS,
+                "kv_frac_of_probe": r["kv_gbps"] / probe["read_gbps"],
+                "attn_us_per_launch": r["attn_us_per_launch"],
+                "ms_per_step": r["ms_per_step"],
+                "verified_draft_tokens_per_s": r["tokens_per_s"],
+                "goodput_accepted_tokens_per_s": r["goodput"],
+                "emitted_tokens_per_step": r["emitted_tokens_per_step"],
+                "input_sets_rotated": r["nsets"],
+            }
+            if name == "tiny":
+                configs[name]["note"] = ("0.56 MB working set: launch-bound, far below the time "
+                                         "70 % of 8 TB/s would take (0.1 us)")
 
-    ev = lambda: torch.cuda.Event(enable_timing=True)
-    # Timed steps: nothing but the three calls per step on the stream (an event
-    # between kernels costs a cache flush and a few microseconds of idle GPU).
-    t_start, t_end = ev(), ev()
-    torch.cuda.synchronize()
-    t_start.record(stream)
-    for s in range(args.steps):
-        inp = sets[s % nsets]
-        inp.append()
-        inp.step_attn()
-        inp.accept()
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    total_ms = t_start.elapsed_time(t_end)
-    ms_per_step = total_ms / args.steps
-    tokens_all = sum(set_tokens[s % nsets] for s in range(args.steps))
-    value = tokens_all / (total_ms * 1e-3)
-    T = tokens_all / args.steps
-
-    # The attention kernel's average launch duration: the same number of
-    # launches back to back on the same stream (same input-set rotation),
-    # between one pair of HIP events.
-    a_start, a_end = ev(), ev()
-    torch.cuda.synchronize()
-    a_start.record(stream)
-    for s in range(args.steps):
-        sets[s % nsets].attn()
-    a_end.record(stream)
-    torch.cuda.synchronize()
-    attn_avg = a_start.elapsed_time(a_end) / args.steps
-    # Per-launch distribution: each launch between its own pair of events
-    # (the events add a little idle time between launches; the roofline
-    # figures use the back-to-back average above).
-    marks = [ev() for _ in range(args.steps + 1)]
-    torch.cuda.synchronize()
-    marks[0].record(stream)
-    for s in range(args.steps):
-        sets[s % nsets].attn()
-        marks[s + 1].record(stream)
-    torch.cuda.synchronize()
-    per_launch = np.array([marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps)]) * 1e3
-    bytes_all = sum(set_bytes[s % nsets] for s in range(args.steps))
-    kvb = bytes_all / args.steps
-    achieved = kvb / (attn_avg * 1e-3) / 1e9
-    traffic = measured_traffic(w.name, attn_avg)
-    flops = sum(attn_flops(w, x.case["ctx_host"], x.case["k_host"]) for x in sets) / nsets
-    tflops = flops / (attn_avg * 1e-3) / 1e12
-
-    probe = copy_probe_gbps(dev)
+    achieved = m["kv_gbps"]
     result = {
         "metric": METRIC,
-        "value": value,
+        "value": m["tokens_per_s"],
         "unit": "verified draft tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
+        "ms_per_step": m["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": w.kv_dtype if w.kv_dtype != "int8" else "int8 KV, bf16 Q",
         "data": "synthetic (seeded torch Philox; no dataset)",
         "config": {
-            "workload": (f"{w.name}: B={w.B}, Hq={w.Hq}, Hkv={w.Hkv}, d={w.d}, "
-                         f"S={w.ctx}, k={w.k}"
-                         f"{' drafts per step (step-level verification)' if long else ''}"
-                         f"{' token-tree nodes' if w.name in wl.TREE_WORKLOADS else ''}, "
-                         f"{w.kv_dtype} paged KV (16-token pages, random "
-                         f"page permutation); "
-                         f"{'no acceptance (a reward-model threshold)' if long else 'stochastic acceptance (rejection sampling, temperature 1) over fp32 target logits [sum(k_b+1), %d] and drafter logits [sum(k_b), %d]' % (w.vocab, w.vocab) if w.name in wl.SAMPLED_WORKLOADS else 'acceptance over fp32 logits [sum(k_b+1), %d]' % w.vocab}"),
+            "workload": describe(w, wl),
             "global_batch": w.B, "seq_len": w.ctx if isinstance(w.ctx, int) else list(w.ctx),
             "drafts_per_seq": w.k if isinstance(w.k, int) else list(w.k),
-            "parallelism": "single GPU", "input_sets_rotated": nsets,
+            "parallelism": "single GPU", "input_sets_rotated": m["nsets"],
         },
-        "kv_bytes_per_launch": kvb,
+        "goodput_accepted_tokens_per_s": m["goodput"],
+        "emitted_tokens_per_step": m["emitted_tokens_per_step"],
+        "draft_tokens_per_step": m["draft_tokens_per_step"],
+        "kv_bytes_per_launch": m["kv_bytes"],
         "kv_hbm_gbps": achieved,
         "kv_frac_of_peak": achieved / HBM_PEAK_GBPS,
-        "attn_ms_avg": attn_avg,
-        "attn_us_per_launch": {"p10": float(np.percentile(per_launch, 10)),
-                               "p50": float(np.median(per_launch)),
-                               "p90": float(np.percentile(per_launch, 90))},
-        "attn_draft_tokens_per_s": T / (attn_avg * 1e-3),
-        "draft_tokens_per_step": T,
-        "other_bytes_per_launch": other_bytes(w, ctx, ks, max_pages),
-        "copy_probe_gbps": probe,
-        "attn_flops_per_launch": flops,
-        "attn_tflops": tflops,
+        "kv_frac_of_probe": achieved / probe["read_gbps"],
+        "attn_ms_avg": m["attn_ms"],
+        "attn_us_per_launch": m["attn_us_per_launch"],
+        "attn_draft_tokens_per_s": m["draft_tokens_per_step"] / (m["attn_ms"] * 1e-3),
+        "other_bytes_per_launch": m["other_bytes"],
+        "probe": probe,
+        "attn_flops_per_launch": m["flops"],
+        "attn_tflops": m["tflops"],
         "roofline": ({
-            "bound": "mfma", "achieved": tflops, "peak": MFMA_BF16_PEAK_TFLOPS,
-            "unit": "TFLOP/s", "frac": tflops / MFMA_BF16_PEAK_TFLOPS,
+            "bound": "mfma", "achieved": m["tflops"], "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": m["tflops"] / MFMA_BF16_PEAK_TFLOPS,
             "traffic": traffic and traffic["gbps"], "traffic_unit": "GB/s",
             "kernel": "verify_attn_rows_kernel",
             "traffic_bytes_per_launch": traffic and traffic["bytes"],
@@ -445,13 +597,12 @@ def main():
             "kernel": "verify_attn_kernel",
             "traffic_bytes_per_launch": traffic and traffic["bytes"],
         }),
+        "configs": configs,
         "cpu_baseline": None,
     }
-    if not args.no_cpu_baseline:
+    if cpu is not None:
         log("cpu baseline (oracle) ...")
-        del sets
-        torch.cuda.empty_cache()
-        result["cpu_baseline"] = cpu_baseline(wl, w, dev, args.cpu_budget)
+        result["cpu_baseline"] = cpu.run(args.cpu_budget)
     print(json.dumps(result), flush=True)
 
 

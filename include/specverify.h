@@ -397,6 +397,24 @@ typedef enum {
 sva_status sva_kvmu_apply(int32_t B, const int32_t *mode, int32_t uniform_mode,
                           const int32_t *arg, int32_t *state, int32_t *ctx_lens, void *stream);
 
+/* ---- Measurement ------------------------------------------------------------
+ * Streaming-read probe: the rate at which one kernel reads HBM on this device,
+ * the achievable ceiling of the verification kernel's KV stream (every KV byte
+ * is read once per call; "Decoding Speculative Decoding from First
+ * Principles", prerequisite section on the roofline: decode is bound by
+ * reading the cache from memory).  Not a step of the method.
+ *   buf             device, 16-byte aligned; `bytes` (a multiple of 1024) are
+ *                   read once with non-temporal 16-byte loads
+ *   mode            0: into registers (8 loads in flight per thread);
+ *                   1: through global -> LDS copies, the verification kernel's
+ *                   path (up to 32 KB in flight per wave)
+ *   num_workgroups  1 .. 65536 workgroups of 256 threads, each reading one
+ *                   contiguous range
+ *   sink            device [num_workgroups * 4] uint32 (written: one word per
+ *                   wave, so no load is dead) */
+sva_status sva_stream_read_probe(const void *buf, size_t bytes, int32_t mode,
+                                 int32_t num_workgroups, uint32_t *sink, void *stream);
+
 const char *sva_status_string(sva_status status);
 const char *sva_last_error(void);
 

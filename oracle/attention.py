@@ -74,18 +74,19 @@ def spec_verify_attn(q, k_pool, v_pool, block_table, ctx_lens, cu_q, softmax_sca
         V = _dequant(v_pool, v_scale, pages, g, slots)
         for i in range(k):
             if draft_mask is None:
-                keys = np.arange(S + i + 1)                # keys 0 .. S+i
+                Ki, Vi = K[:S + i + 1], V[:S + i + 1]      # keys 0 .. S+i
             else:
                 m = int(draft_mask[q0 + i])
                 keys = np.concatenate([np.arange(S),
                                        [S + j for j in range(k) if (m >> j) & 1]]).astype(np.int64)
+                Ki, Vi = K[keys], V[keys]
             for j in range(G):
                 h = g * G + j
                 qv = q[q0 + i, h].astype(np.float64)
-                s = float(softmax_scale) * (K[keys] @ qv)
+                s = float(softmax_scale) * (Ki @ qv)
                 e = np.exp(s - s.max())
                 w = e / e.sum()
-                out[q0 + i, h] = w @ V[keys]
+                out[q0 + i, h] = w @ Vi
                 if weights is not None:
                     weights[(b, i, h)] = w
     if return_weights:

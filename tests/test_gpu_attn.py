@@ -3,8 +3,8 @@
 Small cases span several pages, ragged tails (S = 0, 1, 15, 16, 17, ...), k = 1..16,
 GQA groups 1..8, d = 64 / 128, fp32 / bf16 / INT8 caches and both inner paths,
 and grid sizes that force pairs to be split over workgroups (the cross-workgroup
-merge).  Full-size workloads are checked on sampled (sequence, kv-head) pairs
-in the launch configuration the benchmark uses.
+merge).  Full-size workloads are checked on every (sequence, kv-head) pair, through
+the call and launch configuration the benchmark times.
 """
 import math
 
@@ -162,53 +162,71 @@ def test_zero_drafts():
     assert out.shape == (0, 8, 128)
 
 
-def _sample_pairs(case, n, seed):
-    w = case["workload"]
-    B, H = case["B"], w.Hkv
-    rng = np.random.default_rng(seed)
-    pairs = {(0, 0), (B - 1, H - 1)}
-    while len(pairs) < n:
-        pairs.add((int(rng.integers(B)), int(rng.integers(H))))
-    return sorted(pairs)
+def _own_cache(case):
+    """A cache of the case's own (an INT8 cache is quantised afresh; float
+    pools are cloned), so two calls never write the same memory."""
+    if case["workload"].kv_dtype == "int8":
+        return paged_kv(case)
+    return tva.PagedKV(case["k_pool"].clone(), case["v_pool"].clone(), case["block_table"])
+
+
+def _cache_bits(kv):
+    parts = [kv.k.view(torch.int8), kv.v.view(torch.int8)]
+    if kv.k_scale is not None:
+        parts += [kv.k_scale.view(torch.int16), kv.v_scale.view(torch.int16)]
+    return parts
 
 
 @pytest.mark.parametrize("name", ["tiny", "mha7b", "gqa8b", "gqa70b_int8", "gqa70b_int8_tp8",
                                   "ragged"])
-def test_full_size_workloads_sampled(name):
+def test_full_size_workloads_every_pair(name):
+    """The call the benchmark times -- sva_spec_verify_attn_append: the k_b new
+    rows appended and the drafts verified in one launch, default launch
+    configuration -- at the workload's full size, against the oracle's append
+    then attention on every (sequence, kv-head) pair; the same step as two
+    calls (sva_kv_append, then sva_spec_verify_attn) gives the same bits and
+    the same cache."""
     w = wl.WORKLOADS[name]
     say(f"attn full-size {name}: generating")
     case = wl.make_case(w, device=DEV, with_logits=False)
     kp, vp = np_(case["k_pool"]), np_(case["v_pool"])        # before the GPU append
     batch = batch_of(case)
-    kv = paged_kv(case)
-    if w.append:
-        tva.kv_append(batch, case["k_new"], case["v_new"], kv)
-    out = tva.spec_verify_attn(batch, case["q"], kv)
+    kv_fused, kv_two = _own_cache(case), _own_cache(case)
+    out = tva.spec_verify_attn_append(batch, case["q"], kv_fused, case["k_new"], case["v_new"])
+    tva.kv_append(batch, case["k_new"], case["v_new"], kv_two)
+    out_two = tva.spec_verify_attn(batch, case["q"], kv_two)
     torch.cuda.synchronize()
-    say(f"attn full-size {name}: kernel done, oracle on sampled pairs")
-    pairs = _sample_pairs(case, 6 if name != "tiny" else 8, 7)
-    if name == "tiny":
-        pairs = [(b, g) for b in range(w.B) for g in range(w.Hkv)]
+    assert torch.equal(out.view(torch.int8), out_two.view(torch.int8))
+    for a, b in zip(_cache_bits(kv_fused), _cache_bits(kv_two)):
+        assert torch.equal(a, b)
+    del kv_two, out_two
+    say(f"attn full-size {name}: kernels done, oracle on every pair")
     ctx, cu, bt = np_(case["ctx_lens"]), np_(case["cu_q"]), np_(case["block_table"])
-    if w.append:
-        kp, vp, _, _ = oracle.kv_append(np_(case["k_new"]), np_(case["v_new"]), kp, vp, bt, ctx,
-                                        cu, w.kv_dtype)
+    kn, vn = np_(case["k_new"]), np_(case["v_new"])
     scale = 1.0 / math.sqrt(w.d)
     qn = np_(case["q"])
-    rows = rows_of_pairs(case, pairs)
     if w.kv_dtype == "int8":
         P, H = kp.shape[:2]
         kc, ksc = oracle.kv_quant_int8(kp.reshape(-1, w.d))
         vc, vsc = oracle.kv_quant_int8(vp.reshape(-1, w.d))
-        ref_q = oracle.spec_verify_attn(qn, kc.reshape(kp.shape), vc.reshape(vp.shape), bt, ctx,
-                                        cu, scale, k_scale=ksc.reshape(P, H, 16),
-                                        v_scale=vsc.reshape(P, H, 16), select=pairs)
-        ref_u = oracle.spec_verify_attn(qn, kp, vp, bt, ctx, cu, scale, select=pairs)
-        assert_close(out, ref_q, "int8_deq", rows)
-        assert_close(out, ref_u, "int8", rows)
+        kc, vc, ksc, vsc = oracle.kv_append(kn, vn, kc.reshape(kp.shape), vc.reshape(vp.shape),
+                                            bt, ctx, cu, "int8", ksc.reshape(P, H, 16),
+                                            vsc.reshape(P, H, 16))
+        # the cache the GPU wrote: codes and scales bit-exact
+        assert np.array_equal(np_(kv_fused.k), kc) and np.array_equal(np_(kv_fused.v), vc)
+        assert np.array_equal(np_(kv_fused.k_scale).view(np.uint16), ksc.view(np.uint16))
+        assert np.array_equal(np_(kv_fused.v_scale).view(np.uint16), vsc.view(np.uint16))
+        ref_q = oracle.spec_verify_attn(qn, kc, vc, bt, ctx, cu, scale, k_scale=ksc,
+                                        v_scale=vsc)
+        assert_close(out, ref_q, "int8_deq")
+        del kc, vc
+        kp, vp, _, _ = oracle.kv_append(kn, vn, kp, vp, bt, ctx, cu, "f32")
+        ref_u = oracle.spec_verify_attn(qn, kp, vp, bt, ctx, cu, scale)
+        assert_close(out, ref_u, "int8")
     else:
-        ref = oracle.spec_verify_attn(qn, kp, vp, bt, ctx, cu, scale, select=pairs)
-        assert_close(out, ref, "f32" if w.kv_dtype == "f32" else "bf16", rows)
+        kp, vp, _, _ = oracle.kv_append(kn, vn, kp, vp, bt, ctx, cu, w.kv_dtype)
+        ref = oracle.spec_verify_attn(qn, kp, vp, bt, ctx, cu, scale)
+        assert_close(out, ref, "f32" if w.kv_dtype == "f32" else "bf16")
     assert torch.isfinite(out.float()).all()
 
 
@@ -332,3 +350,33 @@ def test_calls_on_a_side_stream():
     assert_close(ref, oracle_attn(case), "bf16")
     for a, b in zip(acc, ref_acc):
         assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("vmode", ["small", "mixed", "large"])
+def test_int8_value_rows_of_other_magnitudes(vmode):
+    """INT8 caches at S = 8192 with V rows far from N(0, 0.5): all small
+    (N(0, 1e-2): scales near 2e-4, so most weight x scale products are fp16
+    subnormals), magnitudes spread over four decades row by row, and large
+    rows (scales near 200, the products' upper range).  Both bars hold and no
+    output is non-finite."""
+    w = _wk(f"int8-v-{vmode}", 32, 4, 128, "int8", "bf16", 0.5, ident=73)
+    case = _case(w, [8192, 3000], [4, 3])
+    v = case["v_pool"]
+    g = torch.Generator(device=DEV)
+    g.manual_seed(7300)
+    if vmode == "small":
+        v.mul_(0.02)
+    elif vmode == "mixed":
+        u = torch.rand(v.shape[:3], generator=g, device=DEV) * -4.0
+        v.mul_(torch.pow(10.0, u).unsqueeze(-1))
+    else:
+        v.mul_(12000.0 / v.abs().amax())
+    say(f"attn int8 V magnitudes {vmode}")
+    out = tva.spec_verify_attn(batch_of(case), case["q"], paged_kv(case))
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all()
+    ref_q = oracle_attn(case, quantised=True)
+    err, bound = assert_close(out, ref_q, "int8_deq")
+    rel = err / np.abs(ref_q).max()
+    say(f"  max err {err:.3e}, {rel:.2e} of max|ref| (bound {bound:.3e})")
+    assert_close(out, oracle_attn(case, quantised=False), "int8")

@@ -28,7 +28,7 @@ __all__ = [
     "tree_masks", "accept_tree", "kv_commit_path", "accept_tree_commit", "accept_stochastic",
     "accept_stochastic_workspace_bytes", "kvmu_apply", "KVMU_INIT", "KVMU_SPECULATE",
     "KVMU_ACCEPT", "KVMU_ROLLBACK", "KVMU_PREFIX", "verify_status", "STATUS_OFFSET",
-    "spec_verify_attn_append", "spec_verify_attn_noalloc",
+    "spec_verify_attn_append", "spec_verify_attn_noalloc", "stream_read_probe",
 ]
 
 KVMU_INIT, KVMU_SPECULATE, KVMU_ACCEPT, KVMU_ROLLBACK, KVMU_PREFIX = 0, 1, 2, 3, 4
@@ -106,6 +106,8 @@ def load():
         lib.sva_spec_verify_attn_noalloc.restype = ctypes.c_int
         lib.sva_spec_verify_attn_noalloc.argtypes = [vp, vp, i32, i32, vp, ctypes.c_float, vp,
                                                      i32, vp, vp]
+        lib.sva_stream_read_probe.restype = ctypes.c_int
+        lib.sva_stream_read_probe.argtypes = [vp, sz, i32, i32, vp, vp]
         lib.sva_accept_workspace_bytes.restype = sz
         lib.sva_accept_workspace_bytes.argtypes = [vp, i32]
         lib.sva_accept_prefix.restype = ctypes.c_int
@@ -732,6 +734,25 @@ def kvmu_apply(state, mode, arg=None, ctx_lens=None, stream=None):
         B, _ptr(mode) if per_seq else None, 0 if per_seq else int(mode), _ptr(arg), _ptr(state),
         _ptr(ctx_lens), _stream(stream, state.device)))
     return state
+
+
+@_on_stream
+def stream_read_probe(buf, mode=0, num_workgroups=2048, sink=None, stream=None):
+    """Read the device buffer `buf` once (its byte size a multiple of 1024)
+    with the library's streaming-read probe kernel (mode 0: into registers,
+    1: through global -> LDS copies).  Returns the sink words."""
+    lib = load()
+    _need(buf, "buf")
+    nbytes = buf.numel() * buf.element_size()
+    if sink is None:
+        sink = torch.empty(num_workgroups * 4, dtype=torch.int32, device=buf.device)
+    _need(sink, "sink", 1)
+    if sink.numel() < num_workgroups * 4 or sink.dtype != torch.int32:
+        raise ValueError("sink must be int32 with num_workgroups * 4 entries")
+    _check("sva_stream_read_probe", lib.sva_stream_read_probe(
+        _ptr(buf), nbytes, int(mode), int(num_workgroups), _ptr(sink),
+        _stream(stream, buf.device)))
+    return sink
 
 
 class _Prepared:

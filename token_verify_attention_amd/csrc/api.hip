@@ -490,6 +490,23 @@ sva_status sva_kvmu_apply(int32_t B, const int32_t* mode, int32_t uniform_mode,
   return e == hipSuccess ? SVA_OK : hip_fail(e, "kvmu_apply launch");
 }
 
+sva_status sva_stream_read_probe(const void* buf, size_t bytes, int32_t mode,
+                                 int32_t num_workgroups, uint32_t* sink, void* stream) {
+  g_last_error.clear();
+  if (mode != 0 && mode != 1) return fail(SVA_ERR_INVALID_ARG, "mode = %d (0 or 1)", mode);
+  if (num_workgroups < 1 || num_workgroups > 65536)
+    return fail(SVA_ERR_INVALID_ARG, "num_workgroups = %d (1 .. 65536)", num_workgroups);
+  if (bytes % 1024 != 0) return fail(SVA_ERR_INVALID_ARG, "bytes = %zu is not a multiple of 1024", bytes);
+  if (bytes == 0) return SVA_OK;
+  if (!buf || !sink) return fail(SVA_ERR_INVALID_ARG, "buf / sink is NULL");
+  if (!aligned16(buf)) return fail(SVA_ERR_INVALID_ARG, "buf must be 16-byte aligned");
+  const DeviceInfo* dev;
+  if (sva_status s = current_device(&dev)) return s;
+  hipError_t e = sva::launch_stream_read_probe(buf, bytes, mode, num_workgroups, sink,
+                                               as_stream(stream));
+  return e == hipSuccess ? SVA_OK : hip_fail(e, "stream_read_probe launch");
+}
+
 sva_status sva_kv_commit_path(const sva_batch* batch, const int32_t* accept_len,
                               const int32_t* accept_path, const sva_paged_kv* kv, void* stream) {
   g_last_error.clear();

@@ -94,6 +94,12 @@ hipError_t launch_accept_stochastic(const sva_batch* batch, const float* target_
                                     int32_t* next_token, const SamplePlan& plan, void* workspace,
                                     hipStream_t st);
 
+// Streaming-read probe: `bytes` (a multiple of 1 KB) read once by `num_wg`
+// workgroups, into registers (mode 0) or through global -> LDS copies (mode
+// 1); sink [num_wg * 4] receives one word per wave.
+hipError_t launch_stream_read_probe(const void* buf, size_t bytes, int mode, int num_wg,
+                                    uint32_t* sink, hipStream_t st);
+
 // KVMU pointer triplets: one thread per sequence applies its mode.
 hipError_t launch_kvmu(int B, const int32_t* mode, int uniform_mode, const int32_t* arg,
                        int32_t* state, int32_t* ctx_lens, hipStream_t st);
