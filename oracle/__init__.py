@@ -38,6 +38,9 @@ What each function follows (pages cited by title and section):
 * ``kvmu_apply`` -- "HeteroReason", KV Cache Management Unit (Fig. 7): the
   valid / current / step-ahead pointer triplet and its Initialization,
   Speculation, Accept and Rollback modes, plus a token-level prefix commit.
+  ``reclaim_pages`` / ``alloc_pages`` -- the same section (speculative
+  history discarded by pointer moves): pages wholly past the valid pointer
+  return to a free list; the next step's rows take pages from it.
 
 Pins (tests marked ``not gpu``): a torch float64 SDPA with an explicit mask and
 a pure-Python triple loop for attention; closed forms (constant V rows,
@@ -49,7 +52,8 @@ transitive closure for the masks, torch SDPA with the tree mask, brute-force
 path enumeration and chain trees reducing to the causal case; for stochastic
 acceptance, the page's worked example, the output-distribution identity
 located from the oracle's own decision boundaries, and the greedy limit; for
-the KVMU, the page's mode table and invariants of the state machine.  No function here is
+the KVMU, the page's mode table and invariants of the state machine; for the
+page lists, page conservation, uniqueness and hand-worked cases.  No function here is
 "parity unpinned".
 """
 from .attention import spec_verify_attn
@@ -58,7 +62,7 @@ from .kv_append import kv_append
 from .accept import argmax_rows, accept_prefix
 from .tree import ancestor_masks, accept_tree, commit_path
 from .stochastic import accept_stochastic
-from .kvmu import kvmu_apply
+from .kvmu import kvmu_apply, reclaim_pages, alloc_pages
 
 __all__ = [
     "spec_verify_attn",
@@ -73,4 +77,6 @@ __all__ = [
     "commit_path",
     "accept_stochastic",
     "kvmu_apply",
+    "reclaim_pages",
+    "alloc_pages",
 ]

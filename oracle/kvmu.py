@@ -49,3 +49,57 @@ def kvmu_apply(state, mode, arg):
             curr = ahead = valid
         out[b] = (valid, curr, ahead)
     return out
+
+
+# ---------------------------------------------------------------------------
+# Pages of the speculative history
+# ---------------------------------------------------------------------------
+#
+# The same section: rejected speculative history is discarded by moving the
+# pointers alone.  Reading used here for the pages that history occupied: once
+# a sequence's valid pointer is final for the step, every page of its block
+# table that lies wholly at or past it (logical page j with 16 j >= valid)
+# holds nothing valid, so it goes back to the caller's free list and its entry
+# becomes -1.  Before the next step writes rows at positions S_b .. S_b+k_b-1,
+# each unassigned logical page those positions (or any earlier one) fall in
+# takes a page from the top of the free list.  Orders are fixed so that the
+# result is one definite array: pages are returned sequence by sequence,
+# logical page by logical page, appended after the list's current entries;
+# they are taken in the same order, each from the current top of the list.
+# A list with too few pages leaves the remaining entries -1; a full list keeps
+# counting (entries past its capacity are not stored).
+
+def reclaim_pages(block_table, valid_lens, free_list, free_count, page=16):
+    """Returns (block_table, free_list, free_count) after returning every page
+    wholly at or past valid_lens[b] of every sequence b.  Entries < 0 are
+    unassigned and stay so.  free_list is a 1-D array (its length is the
+    capacity); free_count the number of entries in use."""
+    bt = np.array(block_table, dtype=np.int64).copy()
+    fl = np.array(free_list, dtype=np.int64).copy()
+    count = int(free_count)
+    B, max_pages = bt.shape
+    for b in range(B):
+        valid = max(int(valid_lens[b]), 0)
+        for j in range(max_pages):
+            if page * j >= valid and bt[b, j] >= 0:
+                if count < len(fl):
+                    fl[count] = bt[b, j]
+                count += 1
+                bt[b, j] = -1
+    return bt, fl, count
+
+
+def alloc_pages(block_table, ctx_lens, cu_q, free_list, free_count, page=16):
+    """Returns (block_table, free_count) after giving every unassigned logical
+    page j with 16 j < S_b + k_b (k_b = cu_q[b+1] - cu_q[b]) a page taken
+    from the top of the free list (free_list[free_count - 1] first)."""
+    bt = np.array(block_table, dtype=np.int64).copy()
+    count = int(free_count)
+    B, max_pages = bt.shape
+    for b in range(B):
+        end = max(int(ctx_lens[b]), 0) + max(int(cu_q[b + 1]) - int(cu_q[b]), 0)
+        for j in range(max_pages):
+            if page * j < end and bt[b, j] < 0 and count > 0:
+                count -= 1
+                bt[b, j] = int(free_list[count])
+    return bt, count

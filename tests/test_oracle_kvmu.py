@@ -86,3 +86,76 @@ def test_prefix_commit_composes_page_modes():
         s = kvmu_apply(np.array([(v, v + n, v + k)]), [ACCEPT], [0])   # valid <- v + n
         s = kvmu_apply(s, [ROLLBACK], [0])
         assert tuple(a) == tuple(s[0])
+
+
+# ---- pages of the speculative history ---------------------------------------
+
+from oracle.kvmu import alloc_pages, reclaim_pages   # noqa: E402
+
+
+def test_reclaim_hand_worked():
+    """Two sequences of four logical pages.  Sequence 0 keeps 20 rows: pages
+    0 (rows 0-15) and 1 (rows 16-19, partly valid) stay, pages 2 and 3 go.
+    Sequence 1 keeps 32 rows (exactly two pages): pages 2 (id 9) and 3
+    (unassigned) -- only id 9 goes.  Appended after the list's 2 entries,
+    sequence 0's pages first, in logical order."""
+    bt = [[4, 7, 2, 5], [8, 1, 9, -1]]
+    fl = np.full(8, -7)
+    fl[:2] = [30, 31]
+    nbt, nfl, n = reclaim_pages(bt, [20, 32], fl, 2)
+    assert nbt.tolist() == [[4, 7, -1, -1], [8, 1, -1, -1]]
+    assert nfl.tolist()[:5] == [30, 31, 2, 5, 9] and n == 5
+    # a valid length of 0 frees everything; a length past the table frees nothing
+    nbt, _, n = reclaim_pages(bt, [0, 1000], np.zeros(8), 0)
+    assert nbt.tolist() == [[-1, -1, -1, -1], [8, 1, 9, -1]] and n == 4
+
+
+def test_alloc_hand_worked():
+    """Sequence 0: S=20, k=5 -> rows up to 24 -> pages 0 and 1 needed, page 1
+    unassigned takes the list's top (id 12).  Sequence 1: S=31, k=3 -> rows up
+    to 33 -> pages 0..2; pages 1 and 2 unassigned take 11 then 10."""
+    bt = [[3, -1, -1, -1], [6, -1, -1, -1]]
+    fl = [10, 11, 12]
+    nbt, n = alloc_pages(bt, [20, 31], [0, 5, 8], fl, 3)
+    assert nbt.tolist() == [[3, 12, -1, -1], [6, 11, 10, -1]] and n == 0
+    # too few pages: the rest stay unassigned, the count stops at zero
+    nbt, n = alloc_pages(bt, [20, 31], [0, 5, 8], [10], 1)
+    assert nbt.tolist() == [[3, 10, -1, -1], [6, -1, -1, -1]] and n == 0
+
+
+def test_pages_are_conserved_and_unique_over_a_random_loop():
+    """Over many steps of alloc -> (random acceptance) -> reclaim, every page
+    is either in exactly one block-table entry or on the free list, never
+    both; rows below each valid length keep their pages; and after a reclaim
+    no assigned page lies wholly past its sequence's valid length."""
+    rng = np.random.default_rng(3)
+    B, max_pages, P = 6, 40, 200
+    lens = rng.integers(0, 300, B)
+    bt = np.full((B, max_pages), -1)
+    free = list(range(P))
+    rng.shuffle(free)
+    fl = np.array(free + [-1] * 50)
+    count = P
+    # initial contexts take their pages
+    bt, count = alloc_pages(bt, lens, np.zeros(B + 1, int), fl, count)
+    for _ in range(300):
+        ks = rng.integers(0, 9, B)
+        cu = np.concatenate([[0], np.cumsum(ks)])
+        before = bt.copy()
+        bt, count = alloc_pages(bt, lens, cu, fl, count)
+        for b in range(B):
+            for j in range(max_pages):
+                if 16 * j < lens[b]:
+                    assert bt[b, j] == before[b, j]      # valid rows never move
+        n = np.array([rng.integers(0, k + 1) for k in ks])
+        lens = lens + n
+        if rng.random() < 0.1:
+            lens = np.maximum(lens - rng.integers(0, 40, B), 0)   # a deeper rollback
+        bt, fl, count = reclaim_pages(bt, lens, fl, count)
+        assigned = bt[bt >= 0].tolist()
+        listed = fl[:count].tolist()
+        assert sorted(assigned + listed) == list(range(P))
+        for b in range(B):
+            for j in range(max_pages):
+                if bt[b, j] >= 0:
+                    assert 16 * j < lens[b]
