@@ -284,7 +284,7 @@ class CpuBaseline:
 class Inputs:
     """One resident input set and the prepared calls of one step."""
 
-    def __init__(self, tva, wl, w, seed_offset, dev):
+    def __init__(self, tva, wl, w, seed_offset, dev, path=0):
         tree = w.name in wl.TREE_WORKLOADS
         long = w.name in wl.LONG_WORKLOADS
         self.case = case = wl.make_case(w, device=dev, seed_offset=seed_offset,
@@ -331,7 +331,8 @@ class Inputs:
                 fused(stream)
             self.step_attn = step_attn
         else:
-            self.attn = tva.prepare_spec_verify_attn(self.batch, case["q"], self.kv, self.out)
+            self.attn = tva.prepare_spec_verify_attn(self.batch, case["q"], self.kv, self.out,
+                                                     path=path)
             if long:
                 self.accept = lambda stream=None: None
             elif w.name in wl.SAMPLED_WORKLOADS:
@@ -352,7 +353,8 @@ class Inputs:
             else:
                 # the step appends and verifies in one call (one launch)
                 self.step_attn = tva.prepare_spec_verify_attn_append(
-                    self.batch, case["q"], self.kv, case["k_new"], case["v_new"], self.out)
+                    self.batch, case["q"], self.kv, case["k_new"], case["v_new"], self.out,
+                    path=path)
                 self.append = lambda stream=None: None
 
     def step(self):
@@ -367,15 +369,15 @@ class Inputs:
         return int(self.alen.sum().item()) + self.case["B"] if self.has_accept else 0
 
 
-def measure(tva, wl, w, dev, steps, warmup, sets=0):
+def measure(tva, wl, w, dev, steps, warmup, sets=0, path=0):
     """Time `steps` whole steps (inputs resident in HBM), then the same number
     of back-to-back attention launches and the same launches one by one."""
-    inp0 = Inputs(tva, wl, w, 0, dev)
+    inp0 = Inputs(tva, wl, w, 0, dev, path)
     nsets = sets
     if not nsets:       # enough independent sets that the 256 MB MALL cannot hold them
         kvb0 = kv_bytes(w, inp0.case["ctx_host"], inp0.case["k_host"])
         nsets = max(1, min(4, math.ceil(3 * MALL_BYTES / max(kvb0, 1))))
-    ins = [inp0] + [Inputs(tva, wl, w, s_, dev) for s_ in range(1, nsets)]
+    ins = [inp0] + [Inputs(tva, wl, w, s_, dev, path) for s_ in range(1, nsets)]
     set_bytes = [kv_bytes(w, x.case["ctx_host"], x.case["k_host"]) for x in ins]
     set_tokens = [x.case["T"] for x in ins]
     stream = torch.cuda.current_stream(dev)
@@ -499,6 +501,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip timing the other workloads (the 'configs' key)")
+    ap.add_argument("--path", type=int, default=0,
+                    help="attention inner path: 0 default (MFMA for bf16 / INT8), 1 VALU")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
@@ -524,7 +528,7 @@ def main():
     num_cus = torch.cuda.get_device_properties(dev).multi_processor_count
 
     log(f"workload {w.name}: timing {args.steps} steps")
-    m = measure(tva, wl, w, dev, args.steps, args.warmup, args.sets)
+    m = measure(tva, wl, w, dev, args.steps, args.warmup, args.sets, args.path)
     traffic = measured_traffic(w.name, m["attn_ms"])
     probe = probe_ceiling(tva, dev, num_cus)
     log(f"probe ceiling {probe['read_gbps']:.0f} GB/s ({probe['best_shape']})")
@@ -570,6 +574,7 @@ def main():
             "global_batch": w.B, "seq_len": w.ctx if isinstance(w.ctx, int) else list(w.ctx),
             "drafts_per_seq": w.k if isinstance(w.k, int) else list(w.k),
             "parallelism": "single GPU", "input_sets_rotated": m["nsets"],
+            "attention_path": {0: "default", 1: "VALU", 2: "MFMA"}[args.path],
         },
         "goodput_accepted_tokens_per_s": m["goodput"],
         "emitted_tokens_per_step": m["emitted_tokens_per_step"],

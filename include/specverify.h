@@ -397,6 +397,38 @@ typedef enum {
 sva_status sva_kvmu_apply(int32_t B, const int32_t *mode, int32_t uniform_mode,
                           const int32_t *arg, int32_t *state, int32_t *ctx_lens, void *stream);
 
+/* Pages of the speculative history.  The management unit discards rejected
+ * speculation by moving pointers; these two calls keep the pages in step, on
+ * the device, so a whole verification loop (allocate, append and verify,
+ * accept, commit, reclaim) runs without a host round trip and can be captured
+ * in a HIP graph.  The caller owns the free list and the pages; the library
+ * only moves page ids.  Both calls use one workgroup and fixed orders:
+ * sequence by sequence, logical page by logical page.
+ *   block_table   device [B, max_pages_per_seq] int32 (entries < 0: unassigned)
+ *   free_list     device [free_capacity] int32 page ids; entries
+ *                 0 .. *free_count - 1 are free pages, the top is the last
+ *   free_count    device int32 [1], updated in place
+ *
+ * Reclaim: for every sequence b, every logical page j with 16 j >= valid_lens[b]
+ * (wholly at or past the valid pointer) that holds a page is appended to the
+ * list (after its current entries) and its entry set to -1.  Entries past
+ * free_capacity are not stored, but *free_count still counts them (a count
+ * above the capacity means the list overflowed).
+ *   valid_lens    device [B] int32: the committed lengths (for instance the
+ *                 ctx_lens that sva_kvmu_apply wrote) */
+sva_status sva_kv_reclaim_pages(int32_t B, const int32_t *valid_lens, int32_t *block_table,
+                                int32_t max_pages_per_seq, int32_t *free_list,
+                                int32_t *free_count, int32_t free_capacity, void *stream);
+
+/* Allocate: before a step appends rows S_b .. S_b + k_b - 1, every unassigned
+ * logical page j with 16 j < S_b + k_b takes the page on top of the list
+ * (free_list[*free_count - 1] first).  If the list runs out, the remaining
+ * entries stay unassigned (the append then skips their rows) and *free_count
+ * ends at 0.  *free_count must not exceed free_capacity. */
+sva_status sva_kv_alloc_pages(const sva_batch *batch, int32_t *block_table,
+                              int32_t max_pages_per_seq, const int32_t *free_list,
+                              int32_t *free_count, int32_t free_capacity, void *stream);
+
 /* ---- Measurement ------------------------------------------------------------
  * Streaming-read probe: the rate at which one kernel reads HBM on this device,
  * the achievable ceiling of the verification kernel's KV stream (every KV byte

@@ -82,3 +82,29 @@ def test_unaligned_vocab_scalar_path():
     x = big[1:].view(sum(ks) + 2, V)                     # rows not 16-byte aligned
     drafts = torch.zeros(sum(ks), dtype=torch.int32, device=DEV)
     _run_and_compare(batch, x, drafts, cu)
+
+
+def test_one_workspace_serves_calls_of_any_shape():
+    """One workspace reused across batches, vocabularies and chunkings (the
+    chunk keys of one call never leak into the next)."""
+    shapes = [([3, 2, 4, 0, 1, 16], 128256), ([1], 1000), ([8] * 40, 4099),
+              ([2, 5], 70001), ([16] * 3, 128256)]
+    nmax = 0
+    for ks, V in shapes:
+        batch, _ = _batch(ks)
+        nmax = max(nmax, tva.accept_workspace_bytes(batch, V))
+    ws = torch.zeros(nmax, dtype=torch.uint8, device=DEV)
+    for i, (ks, V) in enumerate(shapes * 2):
+        say(f"accept workspace reuse {i}: B={len(ks)} V={V}")
+        batch, cu = _batch(ks)
+        g = torch.Generator(device=DEV).manual_seed(100 + i)
+        x = torch.randn((sum(ks) + len(ks), V), generator=g, device=DEV)
+        t = oracle.argmax_rows(np_(x))
+        d = [int(t[cu[b] + b + j]) if (j + b) % 3 else (int(t[cu[b] + b + j]) + 1) % V
+             for b, k in enumerate(ks) for j in range(k)]
+        drafts = torch.tensor(d, dtype=torch.int32, device=DEV)
+        ids, n, nxt = tva.accept_prefix(batch, x, drafts, workspace=ws)
+        torch.cuda.synchronize()
+        rt, rn, rx = oracle.accept_prefix(np_(x), np_(drafts), cu)
+        assert np.array_equal(np_(ids), rt) and np.array_equal(np_(n), rn)
+        assert np.array_equal(np_(nxt), rx)

@@ -83,14 +83,30 @@ def test_tree_mask_on_row_block_kernel():
 
 
 def test_row_block_kernel_equals_split_kernel_on_short_steps():
-    """A shape both kernels take (k*G = 64 rows): same results within the bar."""
+    """Sequences both kernels take (k*G = 64 and 48 rows per pair).  In a batch
+    of 128 such sequences the row blocks fill the device and the row-block
+    kernel runs (its workspace is the counters alone); the first two of them
+    as a batch of their own run on the split kernel.  Both agree with the
+    oracle, and with each other within the bar."""
     w = _wk("both", 16, 4, 128, "bf16", "bf16", ident=118)
-    case = wl.make_case(w, device=DEV, ctx=[400, 33], k=[16, 12], with_logits=False)
+    case = wl.make_case(w, device=DEV, ctx=[400, 33] * 64, k=[16, 12] * 64, with_logits=False)
     kv = paged_kv(case)
-    batch = batch_of(case)
-    a = tva.spec_verify_attn(batch, case["q"], kv, out_dtype=torch.float32)      # split (small B)
-    ref = oracle_attn(case)
-    assert_close(a, ref, "bf16")
+    big = batch_of(case)
+    assert tva.verify_workspace_bytes(big, kv, w.Hq) == tva.STATUS_OFFSET + 256   # row blocks
+    rows_out = tva.spec_verify_attn(big, case["q"], kv, out_dtype=torch.float32)
+    t2 = 16 + 12                                     # the first two sequences' drafts
+    small = tva.Batch(case["ctx_lens"][:2].contiguous(), case["cu_q"][:3].contiguous(),
+                      total_q=t2, max_q=16, max_len=416)
+    kv2 = tva.PagedKV(kv.k, kv.v, case["block_table"][:2].contiguous())
+    assert tva.verify_workspace_bytes(small, kv2, w.Hq) > tva.STATUS_OFFSET + 256   # split
+    split_out = tva.spec_verify_attn(small, case["q"][:t2].contiguous(), kv2,
+                                     out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    pairs = [(b, g) for b in range(2) for g in range(w.Hkv)]
+    ref = oracle_attn(case, select=pairs)[:t2]
+    assert_close(rows_out[:t2], ref, "bf16")
+    assert_close(split_out, ref, "bf16")
+    assert_close(split_out, np_(rows_out[:t2]).astype(np.float64), "bf16")
 
 
 def test_prm7b_step_full_size_sampled():

@@ -29,6 +29,7 @@ __all__ = [
     "accept_stochastic_workspace_bytes", "kvmu_apply", "KVMU_INIT", "KVMU_SPECULATE",
     "KVMU_ACCEPT", "KVMU_ROLLBACK", "KVMU_PREFIX", "verify_status", "STATUS_OFFSET",
     "spec_verify_attn_append", "spec_verify_attn_noalloc", "stream_read_probe",
+    "kv_reclaim_pages", "kv_alloc_pages",
 ]
 
 KVMU_INIT, KVMU_SPECULATE, KVMU_ACCEPT, KVMU_ROLLBACK, KVMU_PREFIX = 0, 1, 2, 3, 4
@@ -106,6 +107,10 @@ def load():
         lib.sva_spec_verify_attn_noalloc.restype = ctypes.c_int
         lib.sva_spec_verify_attn_noalloc.argtypes = [vp, vp, i32, i32, vp, ctypes.c_float, vp,
                                                      i32, vp, vp]
+        lib.sva_kv_reclaim_pages.restype = ctypes.c_int
+        lib.sva_kv_reclaim_pages.argtypes = [i32, vp, vp, i32, vp, vp, i32, vp]
+        lib.sva_kv_alloc_pages.restype = ctypes.c_int
+        lib.sva_kv_alloc_pages.argtypes = [vp, vp, i32, vp, vp, i32, vp]
         lib.sva_stream_read_probe.restype = ctypes.c_int
         lib.sva_stream_read_probe.argtypes = [vp, sz, i32, i32, vp, vp]
         lib.sva_accept_workspace_bytes.restype = sz
@@ -734,6 +739,50 @@ def kvmu_apply(state, mode, arg=None, ctx_lens=None, stream=None):
         B, _ptr(mode) if per_seq else None, 0 if per_seq else int(mode), _ptr(arg), _ptr(state),
         _ptr(ctx_lens), _stream(stream, state.device)))
     return state
+
+
+def _page_lists(block_table, free_list, free_count):
+    _need(block_table, "block_table", 2)
+    _need(free_list, "free_list", 1)
+    _need(free_count, "free_count", 1)
+    for t, n in ((block_table, "block_table"), (free_list, "free_list"),
+                 (free_count, "free_count")):
+        if t.dtype != torch.int32:
+            raise TypeError(f"{n} must be int32")
+    if free_count.numel() != 1:
+        raise ValueError("free_count must hold one int32")
+    _same_device(block_table, free_list, free_count)
+
+
+@_on_stream
+def kv_reclaim_pages(valid_lens, block_table, free_list, free_count, stream=None):
+    """Return every page wholly at or past valid_lens[b] (device int32 [B]) of
+    block_table [B, max_pages] to the free list (free_list [capacity] int32,
+    free_count [1] int32; pages appended after the list's entries) and mark
+    its entry -1.  In place, on the device."""
+    lib = load()
+    _page_lists(block_table, free_list, free_count)
+    B = int(block_table.shape[0])
+    _int32_vec(valid_lens, B, "valid_lens")
+    _same_device(valid_lens, block_table)
+    _check("sva_kv_reclaim_pages", lib.sva_kv_reclaim_pages(
+        B, _ptr(valid_lens), _ptr(block_table), int(block_table.shape[1]), _ptr(free_list),
+        _ptr(free_count), int(free_list.numel()), _stream(stream, block_table.device)))
+
+
+@_on_stream
+def kv_alloc_pages(batch, block_table, free_list, free_count, stream=None):
+    """Give every unassigned logical page below S_b + k_b a page from the top
+    of the free list (in place, on the device)."""
+    lib = load()
+    _page_lists(block_table, free_list, free_count)
+    if int(block_table.shape[0]) != batch.B:
+        raise ValueError(f"block_table has {block_table.shape[0]} rows for B = {batch.B}")
+    _same_device(batch.ctx_lens, block_table)
+    cb = batch._c()
+    _check("sva_kv_alloc_pages", lib.sva_kv_alloc_pages(
+        ctypes.byref(cb), _ptr(block_table), int(block_table.shape[1]), _ptr(free_list),
+        _ptr(free_count), int(free_list.numel()), _stream(stream, block_table.device)))
 
 
 @_on_stream

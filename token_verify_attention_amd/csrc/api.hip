@@ -490,6 +490,42 @@ sva_status sva_kvmu_apply(int32_t B, const int32_t* mode, int32_t uniform_mode,
   return e == hipSuccess ? SVA_OK : hip_fail(e, "kvmu_apply launch");
 }
 
+sva_status sva_kv_reclaim_pages(int32_t B, const int32_t* valid_lens, int32_t* block_table,
+                                int32_t max_pages_per_seq, int32_t* free_list,
+                                int32_t* free_count, int32_t free_capacity, void* stream) {
+  g_last_error.clear();
+  if (B < 0 || B > 4096) return fail(SVA_ERR_INVALID_ARG, "B = %d (0 .. 4096)", B);
+  if (max_pages_per_seq < 1)
+    return fail(SVA_ERR_INVALID_ARG, "max_pages_per_seq = %d", max_pages_per_seq);
+  if (free_capacity < 0) return fail(SVA_ERR_INVALID_ARG, "free_capacity = %d", free_capacity);
+  if (B == 0) return SVA_OK;
+  if (!valid_lens || !block_table || !free_list || !free_count)
+    return fail(SVA_ERR_INVALID_ARG, "NULL pointer");
+  const DeviceInfo* dev;
+  if (sva_status s = current_device(&dev)) return s;
+  hipError_t e = sva::launch_kv_reclaim_pages(B, valid_lens, block_table, max_pages_per_seq,
+                                              free_list, free_count, free_capacity,
+                                              as_stream(stream));
+  return e == hipSuccess ? SVA_OK : hip_fail(e, "kv_reclaim_pages launch");
+}
+
+sva_status sva_kv_alloc_pages(const sva_batch* batch, int32_t* block_table,
+                              int32_t max_pages_per_seq, const int32_t* free_list,
+                              int32_t* free_count, int32_t free_capacity, void* stream) {
+  g_last_error.clear();
+  if (sva_status s = check_batch(batch, kMaxDraftsLong)) return s;
+  if (max_pages_per_seq < 1)
+    return fail(SVA_ERR_INVALID_ARG, "max_pages_per_seq = %d", max_pages_per_seq);
+  if (free_capacity < 0) return fail(SVA_ERR_INVALID_ARG, "free_capacity = %d", free_capacity);
+  if (batch->B == 0) return SVA_OK;
+  if (!block_table || !free_list || !free_count) return fail(SVA_ERR_INVALID_ARG, "NULL pointer");
+  const DeviceInfo* dev;
+  if (sva_status s = current_device(&dev)) return s;
+  hipError_t e = sva::launch_kv_alloc_pages(batch, block_table, max_pages_per_seq, free_list,
+                                            free_count, free_capacity, as_stream(stream));
+  return e == hipSuccess ? SVA_OK : hip_fail(e, "kv_alloc_pages launch");
+}
+
 sva_status sva_stream_read_probe(const void* buf, size_t bytes, int32_t mode,
                                  int32_t num_workgroups, uint32_t* sink, void* stream) {
   g_last_error.clear();

@@ -100,6 +100,15 @@ hipError_t launch_accept_stochastic(const sva_batch* batch, const float* target_
 hipError_t launch_stream_read_probe(const void* buf, size_t bytes, int mode, int num_wg,
                                     uint32_t* sink, hipStream_t st);
 
+// Pages of the speculative history: return pages wholly past the valid
+// lengths to a free list; give unassigned pages below S_b + k_b pages from it.
+hipError_t launch_kv_reclaim_pages(int B, const int32_t* valid_lens, int32_t* block_table,
+                                   int max_pages, int32_t* free_list, int32_t* free_count,
+                                   int capacity, hipStream_t st);
+hipError_t launch_kv_alloc_pages(const sva_batch* batch, int32_t* block_table, int max_pages,
+                                 const int32_t* free_list, int32_t* free_count, int capacity,
+                                 hipStream_t st);
+
 // KVMU pointer triplets: one thread per sequence applies its mode.
 hipError_t launch_kvmu(int B, const int32_t* mode, int uniform_mode, const int32_t* arg,
                        int32_t* state, int32_t* ctx_lens, hipStream_t st);
