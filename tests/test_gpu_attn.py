@@ -380,3 +380,24 @@ def test_int8_value_rows_of_other_magnitudes(vmode):
     rel = err / np.abs(ref_q).max()
     say(f"  max err {err:.3e}, {rel:.2e} of max|ref| (bound {bound:.3e})")
     assert_close(out, oracle_attn(case, quantised=False), "int8")
+
+
+@pytest.mark.parametrize("kvd,path", [("bf16", 0), ("bf16", 1), ("int8", 0), ("f32", 0)])
+@pytest.mark.parametrize("scale", [-0.05, 0.3, 1e-3])
+def test_softmax_scales_other_than_the_default(kvd, path, scale):
+    """Any finite non-zero softmax scale, negative included (the bf16 MFMA
+    path moves a negative scale's sign into Q), on the split kernel and on
+    the row-block kernel (40 drafts)."""
+    w = _wk(f"scale-{kvd}", 16, 4, 128 if kvd != "f32" else 64, kvd,
+            "bf16" if kvd != "f32" else "f32", 0.5 if kvd == "int8" else 1.0, ident=74)
+    ks = [4, 9, 2] if kvd == "f32" or path == 1 else [4, 40, 2]
+    case = _case(w, [300, 70, 1000], ks)
+    say(f"attn scale={scale} {kvd} path={path}")
+    out = tva.spec_verify_attn(batch_of(case), case["q"], paged_kv(case), softmax_scale=scale,
+                               path=path)
+    torch.cuda.synchronize()
+    qn = np_(case["q"])
+    kp, vp = np_(case["k_pool"]), np_(case["v_pool"])
+    bt, ctx, cu = np_(case["block_table"]), np_(case["ctx_lens"]), np_(case["cu_q"])
+    ref = oracle.spec_verify_attn(qn, kp, vp, bt, ctx, cu, scale)
+    assert_close(out, ref, {"int8": "int8", "f32": "f32", "bf16": "bf16"}[kvd])

@@ -291,19 +291,31 @@ __device__ __forceinline__ uint32_t lds_addr(const void* l) {
 }
 // The global address is a wave-uniform base in SGPRs plus a 32-bit per-lane
 // offset (the saddr form), so issuing a page costs no 64-bit vector adds.
+// kNT = false (the row-block kernel: several workgroups read each page) drops
+// the non-temporal hint so the pages stay in L2 for the other readers.
+template <bool kNT = true>
 __device__ __forceinline__ void dma16(const void* base, uint32_t off, void* l) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
-               ::"v"(off), "s"(base), "s"(lds_addr(l)) : "memory", "m0");
+  if constexpr (kNT)
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
+                 ::"v"(off), "s"(base), "s"(lds_addr(l)) : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 ::"v"(off), "s"(base), "s"(lds_addr(l)) : "memory", "m0");
 }
 // 4 bytes per lane from a per-lane 64-bit address (lanes may read different
 // arrays).
+template <bool kNT = true>
 __device__ __forceinline__ void dma4(const void* src, void* l) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off nt"
-               ::"v"(src), "s"(lds_addr(l)) : "memory", "m0");
+  if constexpr (kNT)
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off nt"
+                 ::"v"(src), "s"(lds_addr(l)) : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+                 ::"v"(src), "s"(lds_addr(l)) : "memory", "m0");
 }
 
 // Page `pid` of kv head g -> ring slot (K page, V page, INT8 scales).
-template <typename KV, int D>
+template <typename KV, int D, bool kNT = true>
 __device__ __forceinline__ void dma_page(const AttnParams& p, int pid, int g, char* slot) {
   using Gm = Geo<KV, D, kWavesValu>;      // page geometry only
   const int lane = lane_id();
@@ -314,14 +326,16 @@ __device__ __forceinline__ void dma_page(const AttnParams& p, int pid, int g, ch
   for (int e = 0; e < Gm::DMA; ++e) {
     const int phys = kWave * e + lane;
     const int rho = phys / Gm::CPR, phi = phys % Gm::CPR;
-    dma16(kb, uint32_t(rho * Gm::RB + (phi ^ Gm::swz_k(rho)) * 16), slot + 1024 * e);
-    dma16(vb, uint32_t(rho * Gm::RB + (phi ^ Gm::swz_v(rho)) * 16), slot + Gm::PAGE + 1024 * e);
+    dma16<kNT>(kb, uint32_t(rho * Gm::RB + (phi ^ Gm::swz_k(rho)) * 16), slot + 1024 * e);
+    dma16<kNT>(vb, uint32_t(rho * Gm::RB + (phi ^ Gm::swz_v(rho)) * 16),
+               slot + Gm::PAGE + 1024 * e);
   }
   if constexpr (Gm::ES == 1) {
     // one copy for both scale rows: lanes 0-7 the 16 K scales, lanes 8-15
     // the 16 V scales, landing side by side
     const int64_t so = (int64_t(pid) * p.Hkv + g) * kPage;
-    if (lane < 16) dma4((lane < 8 ? p.k_scale : p.v_scale) + so + 2 * (lane & 7), slot + 2 * Gm::PAGE);
+    if (lane < 16)
+      dma4<kNT>((lane < 8 ? p.k_scale : p.v_scale) + so + 2 * (lane & 7), slot + 2 * Gm::PAGE);
   }
 }
 
@@ -1012,22 +1026,28 @@ struct MfmaStep {
   // scores are masked to -inf later.  A branch around these products would put
   // a read of their accumulators right after a taken jump, where this compiler
   // omits the MFMA result wait states.
-  __device__ __forceinline__ void load(const char* sa, const char* sb) {
+  // S^T of the pages in slots sa, sb (one unit) into dst.
+  __device__ __forceinline__ void scores(const char* sa, const char* sb,
+                                         f32x4 (&dst)[2][NRB]) const {
 #pragma unroll
     for (int pg = 0; pg < 2; ++pg) {
 #pragma unroll
       for (int rb = 0; rb < NRB; ++rb) {
         const float z = I8 ? s0[rb] : 0.f;
-        s[pg][rb] = f32x4{z, z, z, z};
+        dst[pg][rb] = f32x4{z, z, z, z};
       }
       const char* page = pg ? sb : sa;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const Op8 ka = k_operand(page, ks);
 #pragma unroll
-        for (int rb = 0; rb < NRB; ++rb) s[pg][rb] = mfma32(ka, qB[rb][ks], s[pg][rb]);
+        for (int rb = 0; rb < NRB; ++rb) dst[pg][rb] = mfma32(ka, qB[rb][ks], dst[pg][rb]);
       }
     }
+  }
+
+  __device__ __forceinline__ void load(const char* sa, const char* sb) {
+    scores(sa, sb, s);
 #pragma unroll
     for (int db = 0; db < NDB; ++db) vr[db] = v_raw(sa, sb, db);
     if constexpr (I8) {
@@ -1059,7 +1079,7 @@ struct MfmaStep {
       for (int pg = 0; pg < 2; ++pg) asm volatile("" : "+v"(kw[pg]), "+v"(vw[pg]));
     }
     if constexpr (I8) softmax_pv_i8<EDGE>(a, second);
-    else softmax_pv<EDGE>(a, second);
+    else softmax_pv<EDGE>(a, second, s);
   }
 
   // INT8 caches.  Q carries softmax_scale * log2 e, so a token's score in log2
@@ -1146,7 +1166,7 @@ struct MfmaStep {
 
   // bf16 caches: scores times scale * log2 e, lazy maximum, bf16 weights.
   template <bool EDGE>
-  __device__ __forceinline__ void softmax_pv(int a, bool second) {
+  __device__ __forceinline__ void softmax_pv(int a, bool second, const f32x4 (&sc)[2][NRB]) {
     const int npg = second ? 2 : 1;
     Op8 va[NDB];
 #pragma unroll
@@ -1166,7 +1186,9 @@ struct MfmaStep {
     }
     // Masked scores and row maxima of every row block first, then one
     // wave-uniform decision for all of them, so that the blocks' work stays
-    // straight-line code the compiler can interleave.
+    // straight-line code the compiler can interleave.  The maxima are taken
+    // over the unscaled scores (scale_log2 > 0: see ready()) and scaled once
+    // per row; each weight is then exp2 of one fma.
     float x[NRB][2][4], mx[NRB];
     bool move = false;
 #pragma unroll
@@ -1177,12 +1199,11 @@ struct MfmaStep {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int pos = (a + pg) * kPage + 4 * c + i;
-          const float v = s[pg][rb][i] * scale_log2;
-          x[rb][pg][i] = (!EDGE || (pg < npg && visible(pos, rb))) ? v : -INFINITY;
+          x[rb][pg][i] = (!EDGE || (pg < npg && visible(pos, rb))) ? sc[pg][rb][i] : -INFINITY;
           t = fmaxf(t, x[rb][pg][i]);
         }
       }
-      mx[rb] = xrow32_max(xrow16_max(t));                       // over the 4 lanes of the row
+      mx[rb] = xrow32_max(xrow16_max(t)) * scale_log2;          // over the 4 lanes of the row
       move |= mx[rb] > m[rb] + kLazy;
     }
     if (__ballot(move)) {                                       // some row's reference moves
@@ -1205,8 +1226,9 @@ struct MfmaStep {
       u32x4 pw;
 #pragma unroll
       for (int h = 0; h < 4; ++h)
-        pw[h] = pack_bf16x2(__builtin_amdgcn_exp2f(x[rb][h >> 1][2 * (h & 1)] - m[rb]),
-                            __builtin_amdgcn_exp2f(x[rb][h >> 1][2 * (h & 1) + 1] - m[rb]));
+        pw[h] = pack_bf16x2(
+            __builtin_amdgcn_exp2f(fmaf(x[rb][h >> 1][2 * (h & 1)], scale_log2, -m[rb])),
+            __builtin_amdgcn_exp2f(fmaf(x[rb][h >> 1][2 * (h & 1) + 1], scale_log2, -m[rb])));
       const Op8 pb = __builtin_bit_cast(Op8, pw);
       sacc[rb] = mfma32(ones(), pb, sacc[rb]);
 #pragma unroll
@@ -1219,9 +1241,22 @@ struct MfmaStep {
   // (one wait that also covers the first DMAs) instead of inside it.
   // INT8: fp16 operands from bf16 Q (times softmax_scale * log2 e), and the S^T
   // start value -1152 * sum(q).
+  // bf16: a negative softmax scale is moved into Q (a sign flip, exact), so
+  // the score maxima can be taken before scaling.
   __device__ __forceinline__ void ready() {
+    const bool flip = !I8 && scale_log2 < 0.f;
+    if (flip) scale_log2 = -scale_log2;
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
+      if constexpr (!I8) {
+        if (flip) {
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks)
+            qB[rb][ks] = __builtin_bit_cast(
+                Op8, __builtin_bit_cast(u32x4, qB[rb][ks]) ^ u32x4{0x80008000u, 0x80008000u,
+                                                                   0x80008000u, 0x80008000u});
+        }
+      }
       if constexpr (I8) {
         if (qbf16) {
 #pragma unroll
@@ -2005,12 +2040,11 @@ constexpr int kRowBlock = kRowWaves * kMfmaRows;   // 128 query rows per workgro
 constexpr int kRowPages = 4;                       // pages per step, one per copying wave
 
 // Two workgroups per CU (two waves per SIMD: one wave's LDS reads and softmax
-// run while the other's MFMAs do) wherever the step fits in 256 VGPRs; the
-// INT8 d=128 step needs more and runs one workgroup per CU.
+// run while the other's MFMAs do); every step fits in 256 VGPRs.
 template <typename KV, int D>
 struct RowsLds {
   using Gm = Geo<KV, D, kRowWaves>;
-  static constexpr int OCC = (sizeof(KV) == 1 && D == 128) ? 1 : 2;
+  static constexpr int OCC = 2;
   static constexpr int BUDGET = OCC > 1 ? 72 * 1024 : kRingBudget;
   static constexpr int STEP = kRowPages * Gm::SLOT;   // the pages (K, V, scales) of one step
   static constexpr int NS_RAW = BUDGET / STEP;
@@ -2121,7 +2155,8 @@ void verify_attn_rows_kernel(AttnParams p) {
   auto issue = [&](int s) {
     if (!copier) return;
     const int pg = min(kRowPages * s + wave, npages - 1);
-    dma_page<KV, D>(p, page_id(p, b, pg), sg.g, s_ring + (s % NS) * L::STEP + wave * Gm::SLOT);
+    dma_page<KV, D, false>(p, page_id(p, b, pg), sg.g,
+                           s_ring + (s % NS) * L::STEP + wave * Gm::SLOT);
   };
   for (int s = 0; s < NS - 1 && s < nsteps; ++s) issue(s);
   st.ready();
@@ -2134,7 +2169,11 @@ void verify_attn_rows_kernel(AttnParams p) {
     if (s + NS - 1 < nsteps) issue(s + NS - 1);
     if (!active) return;
     const char* base = s_ring + (s % NS) * L::STEP;
-#pragma unroll
+    // one unit (two pages) at a time: unrolled, the compiler hoists the
+    // second unit's LDS reads and holds both units' operands (256 VGPRs and
+    // spills, 5-7 % slower on the 7B reward-model shape); issuing the second
+    // unit's score MFMAs ahead of the first unit's softmax was slower still
+#pragma unroll 1
     for (int u = 0; u < kRowPages / 2; ++u) {
       const int a = kRowPages * s + 2 * u;
       if (EDGE && a >= npages) break;
