@@ -233,7 +233,8 @@ static sva_status check_attn_shape(const sva_batch* batch, const sva_paged_kv* k
     return fail(SVA_ERR_UNSUPPORTED, "max_q * G = %lld too large", (long long)(G * batch->max_q));
   const int64_t pages_ub =
       int64_t(batch->B) * kv->Hkv * std::min<int64_t>(kv->max_pages_per_seq, (int64_t(batch->max_len) + 15) / 16);
-  if (pages_ub >= (int64_t(1) << 31) - 1)
+  // plus the work split's fixed cost per pair (at most 64 pages' worth)
+  if (pages_ub + int64_t(batch->B) * kv->Hkv * 64 >= (int64_t(1) << 31) - 1)
     return fail(SVA_ERR_UNSUPPORTED, "B * Hkv * pages = %lld too large", (long long)pages_ub);
   return SVA_OK;
 }

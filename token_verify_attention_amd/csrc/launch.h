@@ -24,6 +24,7 @@ struct AttnPlan {
   int rows_grid;        // its grid (an upper bound on the row blocks)
   int num_wg;
   int wait_polls;       // bound on a split pair's wait for the others' partials
+  int seg_cost;         // fixed cost of a segment, in pages, for the work split
   int slot_rows;
   size_t counter_bytes;
   size_t slot_bytes;

@@ -66,6 +66,9 @@ constexpr int kMaxDraftsSplit = 16;            // max_q the split kernel takes
 constexpr int kMaxRowsSplit = 128;             // max_q * G the split kernel takes
 constexpr int kRingBudget = 136 * 1024;        // LDS bytes for the page rings of all waves
 constexpr float kNegBig = -1.0e30f;            // finite start value of running maxima
+// Streaming time a segment's fixed work costs (its query rows, first copies
+// and merge), as bytes of KV: the work split counts it once per segment.
+constexpr int kSegCostBytes = 96 * 1024;
 constexpr float kLog2e = 1.4426950408889634f;
 
 #define AS1 __attribute__((address_space(1)))
@@ -95,6 +98,7 @@ struct AttnParams {
   int B, T, Hq, Hkv, G, num_pages, max_pages, max_q;
   int slot_rows;        // rows per partial slot (max_q * G)
   int W;                // grid size
+  int seg_cost;         // fixed cost of a segment, in pages (work split)
 };
 
 struct SeqInfo {
@@ -118,20 +122,49 @@ __device__ __forceinline__ bool key_visible_idx(int pos, int S, int end, int i) 
 }
 
 // Sequence b with every device-resident value clamped into the buffers.
+// The three loads are independent and the page count is computed without a
+// branch, so one memory round trip serves them all.
 __device__ __forceinline__ SeqInfo seq_info(const AttnParams& p, int b) {
-  int q0 = p.cu_q[b], q1 = p.cu_q[b + 1];
-  q0 = min(max(q0, 0), p.T);
-  q1 = min(max(q1, q0), p.T);
+  const int c0 = p.cu_q[b], c1 = p.cu_q[b + 1], ctx = p.ctx_lens[b];
+  const int q0 = min(max(c0, 0), p.T);
+  const int q1 = min(max(c1, q0), p.T);
   SeqInfo s;
   s.q0 = q0;
   s.k = min(q1 - q0, p.max_q);
-  s.S = max(p.ctx_lens[b], 0);
-  s.np = 0;
-  if (s.k > 0) {
-    const int64_t need = (int64_t(s.S) + s.k + kPage - 1) / kPage;
-    s.np = int(min(need, int64_t(p.max_pages)));
-  }
+  s.S = max(ctx, 0);
+  const int64_t need = (int64_t(s.S) + s.k + kPage - 1) / kPage;
+  s.np = s.k > 0 ? int(min(need, int64_t(p.max_pages))) : 0;
   return s;
+}
+
+// The work split runs in cost coordinates: the Hkv pairs of sequence b lie
+// end to end from the sequence's start sb, each taking seg_cost + np units --
+// its np pages between seg_cost / 2 virtual units before and the rest after
+// (the fixed cost of a segment: its query rows, first copies and merge, half
+// at either end so that a pair split in two costs its halves alike) -- and
+// every workgroup takes an equal contiguous range of the total.  A range of
+// many short pairs thus holds fewer pages than a range inside one long pair,
+// and a batch of equal pairs is split exactly as by pages alone.
+__device__ __forceinline__ int64_t seq_cost(const AttnParams& p, const SeqInfo& si) {
+  return si.np > 0 ? int64_t(p.Hkv) * (si.np + p.seg_cost) : 0;
+}
+struct PairPos {
+  int g;              // kv head
+  int pa, pe;         // pages of the pair inside [cur, c1) (empty when pe <= pa)
+  int64_t pb, pend;   // cost coordinates of the pair's first page and past its last
+  int64_t bend;       // end of the pair's block (the next pair's start)
+};
+__device__ __forceinline__ PairPos pair_pos(const AttnParams& p, int64_t cur, int64_t sb,
+                                            int np, int64_t c1) {
+  const int blk = np + p.seg_cost;
+  PairPos r;
+  r.g = int(cur - sb) / blk;
+  r.pb = sb + int64_t(r.g) * blk + p.seg_cost / 2;
+  r.pend = r.pb + np;
+  r.bend = sb + int64_t(r.g + 1) * blk;
+  r.pa = int(max(cur, r.pb) - r.pb);
+  r.pe = int(max(min(c1, r.pend), r.pb) - r.pb);
+  return r;
 }
 
 struct Seg {
@@ -363,11 +396,36 @@ __device__ __forceinline__ void issue_step(const AttnParams& p, const Seg& sg, c
                                            int s) {
   using Gm = Geo<KV, D, NW>;
   const int a = sg.pa + 2 * (wave + NW * s);
+  // both ids with in-range indices and no branch: the loads go out together
+  // (past the segment's end the second slot gets a copy of the first page)
   const int ida = page_id(p, sg.b, a);
-  const int idb = (a + 1 < sg.pe) ? page_id(p, sg.b, a + 1) : ida;
+  const int idb = page_id(p, sg.b, min(a + 1, sg.pe - 1));
   char* slots = ring + (s % Gm::S) * 2 * Gm::SLOT;
   dma_page<KV, D>(p, ida, sg.g, slots);
   dma_page<KV, D>(p, idb, sg.g, slots + Gm::SLOT);
+}
+
+// The first steps of a wave's share of a segment: every page id is loaded
+// before the first copy is issued, so the prologue costs one memory round
+// trip for its ids instead of one per page.
+template <typename KV, int D, int NW, int S>
+__device__ __forceinline__ void issue_first_steps(const AttnParams& p, const Seg& sg, char* ring,
+                                                  int wave, const int (&q)[S]) {
+  using Gm = Geo<KV, D, NW>;
+  int ids[S][2];
+#pragma unroll
+  for (int i = 0; i < S; ++i) {
+    const int a = min(sg.pa + 2 * (wave + NW * i), sg.pe - 1);
+    ids[i][0] = page_id(p, sg.b, a);
+    ids[i][1] = page_id(p, sg.b, min(a + 1, sg.pe - 1));
+  }
+#pragma unroll
+  for (int i = 0; i < S; ++i) {
+    if (q[i] < 0) continue;
+    char* slots = ring + (i % Gm::S) * 2 * Gm::SLOT;
+    dma_page<KV, D>(p, ids[i][0], sg.g, slots);
+    dma_page<KV, D>(p, ids[i][1], sg.g, slots + Gm::SLOT);
+  }
 }
 
 // Steps of a step type that separates its LDS reads (load) from its arithmetic
@@ -422,10 +480,8 @@ __device__ __forceinline__ void run_pages(const AttnParams& p, const Seg& sg, ch
   if constexpr (Step::kSplit) {
     int q[S];
 #pragma unroll
-    for (int i = 0; i < S; ++i) {
-      q[i] = wave + NW * i < npair ? wave + NW * i : -1;
-      if (q[i] >= 0) issue_step<KV, D, NW>(p, sg, ring, wave, i);
-    }
+    for (int i = 0; i < S; ++i) q[i] = wave + NW * i < npair ? wave + NW * i : -1;
+    issue_first_steps<KV, D, NW>(p, sg, ring, wave, q);
     st.ready();
     // units whose two pages lie inside the committed context (and inside the
     // segment) need no masks
@@ -1824,6 +1880,7 @@ __device__ __forceinline__ void process_segment(const AttnParams& p, const Seg& 
 template <typename KV, typename Src, int D, int NW>
 __device__ __forceinline__ bool append_wave_rows(const AttnParams& p, int64_t g0, int64_t g1,
                                                  int b, int64_t sb) {
+  // g0, g1, sb: cost coordinates (see pair_pos)
   constexpr int N = D / kRowLanes;
   constexpr int S_RING = Geo<KV, D, NW>::S;          // steps issued before the first wait
   const int wave = wave_id();
@@ -1833,17 +1890,14 @@ __device__ __forceinline__ bool append_wave_rows(const AttnParams& p, int64_t g0
   SeqInfo si = seq_info(p, b);
   int64_t cur = g0;
   while (cur < g1) {
-    while (cur >= sb + int64_t(p.Hkv) * si.np) {      // next sequence with pages
-      sb += int64_t(p.Hkv) * si.np;
+    while (cur >= sb + seq_cost(p, si)) {             // next sequence with pages
+      sb += seq_cost(p, si);
       ++b;
       si = seq_info(p, b);
     }
-    const int o = int(cur - sb);
-    const int g = o / si.np;
-    const int pa = o - g * si.np;
-    const int64_t pend = sb + int64_t(g + 1) * si.np;
-    const int64_t se = min(g1, pend);
-    const int pe = pa + int(se - cur);
+    const PairPos pp = pair_pos(p, cur, sb, si.np, g1);
+    const int g = pp.g, pa = pp.pa, pe = pp.pe;
+    const int64_t se = min(g1, pp.bend);
     // positions S .. S+k-1 whose page lies in [pa, pe), 4 per pass (one per
     // 16-lane group), each written by the owner of its unit
     const int lo = max(si.S, pa * kPage), hi = min(si.S + si.k, pe * kPage);
@@ -1874,7 +1928,7 @@ __device__ __forceinline__ bool append_wave_rows(const AttnParams& p, int64_t g0
         }
       }
     }
-    first = false;
+    if (pe > pa) first = false;
     cur = se;
   }
   return __ballot(early) != 0;
@@ -1889,17 +1943,30 @@ __global__ __launch_bounds__((AttnLds<KV, D, MF>::NT), 1) void verify_attn_kerne
   __shared__ __attribute__((aligned(16))) char s_ps[L::NW * L::PS];
   __shared__ int32_t s_scan[NT];
   __shared__ int32_t s_info[4];
+  __shared__ int32_t s_seq[4];
   __shared__ int s_flag;
 
   const int tid = threadIdx.x;
   const int B = p.B;
 
   // ---- pages per sequence: each thread sums a contiguous chunk of sequences
+  // (the first kSeqCache of them stay in registers for the search below)
+  constexpr int kSeqCache = 4;
   const int per = (B + NT - 1) / NT;
   int tot = 0;
-  for (int e = 0; e < per; ++e) {
+  SeqInfo cache[kSeqCache];
+#pragma unroll
+  for (int e = 0; e < kSeqCache; ++e) {
     const int b = tid * per + e;
-    if (b < B) tot += p.Hkv * seq_info(p, b).np;
+    cache[e] = SeqInfo{0, 0, 0, 0};
+    if (e < per && b < B) {
+      cache[e] = seq_info(p, b);
+      tot += int(seq_cost(p, cache[e]));
+    }
+  }
+  for (int e = kSeqCache; e < per; ++e) {
+    const int b = tid * per + e;
+    if (b < B) tot += int(seq_cost(p, seq_info(p, b)));
   }
   s_scan[tid] = tot;
   __syncthreads();
@@ -1919,28 +1986,38 @@ __global__ __launch_bounds__((AttnLds<KV, D, MF>::NT), 1) void verify_attn_kerne
     }
     const int excl = incl - run;
     for (int i = 0; i < PER_LANE; ++i) s_scan[tid * PER_LANE + i] += excl;
-    if (tid == kWave - 1) s_info[0] = incl;           // total pages N
+    if (tid == kWave - 1) s_info[0] = incl;           // total cost N
   }
   __syncthreads();
   const int64_t N = s_info[0];
   if (N == 0) return;
 
-  // ---- this workgroup's page range; consecutive ranges go to one XCD
+  // ---- this workgroup's range (cost coordinates); consecutive ranges go to one XCD
   const int w = logical_wg(p.W);
   const int64_t g0 = range_start(w, N, p.W), g1 = range_start(w + 1, N, p.W);
   if (g0 >= g1) return;
 
-  // the sequence holding page g0 and the first page of that sequence
+  // the sequence holding page g0, the first page of that sequence and its
+  // SeqInfo (from the registers above when cached: no second load)
   {
     const int base = s_scan[tid];
     if (tot > 0 && base <= g0 && g0 < base + tot) {
       int run = base;
       for (int e = 0; e < per; ++e) {
         const int b = tid * per + e;
-        const int n = p.Hkv * seq_info(p, b).np;
+        SeqInfo si_e = cache[0];
+#pragma unroll
+        for (int c = 1; c < kSeqCache; ++c)
+          if (e == c) si_e = cache[c];
+        if (e >= kSeqCache) si_e = seq_info(p, b);
+        const int n = int(seq_cost(p, si_e));
         if (g0 < run + n) {
           s_info[1] = b;
           s_info[2] = run;
+          s_seq[0] = si_e.S;
+          s_seq[1] = si_e.k;
+          s_seq[2] = si_e.q0;
+          s_seq[3] = si_e.np;
           break;
         }
         run += n;
@@ -1955,31 +2032,34 @@ __global__ __launch_bounds__((AttnLds<KV, D, MF>::NT), 1) void verify_attn_kerne
                                  : append_wave_rows<KV, uint16_t, D, L::NW>(p, g0, g1, b, sb);
     if (early) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
-  SeqInfo si = seq_info(p, b);
+  SeqInfo si{s_seq[0], s_seq[1], s_seq[2], s_seq[3]};
 
   int64_t cur = g0;
   while (cur < g1) {
-    while (cur >= sb + int64_t(p.Hkv) * si.np) {      // next sequence with pages
-      sb += int64_t(p.Hkv) * si.np;
+    while (cur >= sb + seq_cost(p, si)) {             // next sequence with pages
+      sb += seq_cost(p, si);
       ++b;
       si = seq_info(p, b);
     }
-    const int o = int(cur - sb);
+    const PairPos pp = pair_pos(p, cur, sb, si.np, g1);
+    const int64_t pb = pp.pb, pend = pp.pend;
+    const int64_t se = min(g1, pp.bend);
+    if (pp.pe <= pp.pa) {               // only the pair's fixed cost lies in the range
+      cur = se;
+      continue;
+    }
     Seg sg;
     sg.b = b;
-    sg.g = o / si.np;
-    sg.pa = o - sg.g * si.np;
+    sg.g = pp.g;
+    sg.pa = pp.pa;
+    sg.pe = pp.pe;
     sg.S = si.S;
     sg.k = si.k;
     sg.q0 = si.q0;
     sg.np = si.np;
     sg.R = si.k * p.G;
-    const int64_t pb = sb + int64_t(sg.g) * si.np;
-    const int64_t pend = pb + si.np;
-    const int64_t se = min(g1, pend);
-    sg.pe = int(se - pb);
-    sg.full = (cur == pb) && (se == pend);
-    sg.slot = (cur == g0) ? 2 * w : 2 * w + 1;
+    sg.full = pp.pa == 0 && pp.pe == si.np;
+    sg.slot = slot_of(w, pb, N, p.W);
     sg.fuse = MF && !sg.full && sg.R <= kMfmaRows;
     if (sg.fuse && tid == 0) {          // read after the barriers of the pass
       pair_info()[0] = pb;
@@ -2231,6 +2311,10 @@ AttnPlan plan_verify_attn(const sva_batch* batch, const sva_paged_kv* kv, int Hq
                               pairs * seg_cap));
   }
   pl.num_wg = W;
+  // fixed cost of a segment in pages: about kSegCostBytes of streaming
+  const int page_bytes = 2 * kPage * kv->d * (kv->kv_dtype == SVA_F32 ? 4 : kv->kv_dtype == SVA_BF16 ? 2 : 1) +
+                         (kv->kv_dtype == SVA_INT8 ? 4 * kPage : 0);
+  pl.seg_cost = int((kSegCostBytes + page_bytes / 2) / page_bytes);
   pl.wait_polls = !opts || opts->wait_polls == 0 ? kSpinLimit : std::max(opts->wait_polls, 0);
   pl.slot_rows = std::max(batch->max_q, 1) * G;
   // arrival and publication counters, then the status word (256 bytes keep
@@ -2308,6 +2392,7 @@ hipError_t launch_verify_attn(const sva_batch* batch, const void* q, int q_dtype
   p.max_q = batch->max_q;
   p.slot_rows = plan.slot_rows;
   p.W = plan.num_wg;
+  p.seg_cost = plan.seg_cost;
   const bool mfma = path != 1;         // fp32 caches always take the VALU kernel
   if (plan.rows_kernel) {
     // the row-block kernel reads a pair's draft pages from several
