@@ -34,7 +34,10 @@ __all__ = [
 
 KVMU_INIT, KVMU_SPECULATE, KVMU_ACCEPT, KVMU_ROLLBACK, KVMU_PREFIX = 0, 1, 2, 3, 4
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "_lib", "libspecverify.so")
+# The built library; TVA_LIB names another build of it (a sanitizer build in
+# the CPU tests).  Nothing falls back when the file is missing.
+LIB_PATH = os.environ.get("TVA_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                    "_lib", "libspecverify.so")
 
 SVA_F32, SVA_BF16, SVA_F16, SVA_INT8 = 0, 1, 2, 3
 SVA_OK, SVA_ERR_INVALID_ARG, SVA_ERR_UNSUPPORTED, SVA_ERR_HIP = 0, 1, 2, 3

@@ -55,22 +55,41 @@ def _run(cmd, verbose):
         raise RuntimeError(f"command failed ({res.returncode}): {' '.join(cmd)}")
 
 
-def build(verbose=False, jobs=4):
-    """Compile every HIP source and link the shared library.  Returns its path."""
+# Host-side AddressSanitizer build (the C ABI's argument checks and planning;
+# the GPU code is built as usual).  Each sanitizer flag is marked host-only.
+ASAN_HOST_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer",
+                   "-g"]
+
+
+def asan_runtime():
+    """The clang AddressSanitizer runtime next to hipcc's compiler, or None."""
+    import glob
+    hits = sorted(glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+    return hits[-1] if hits else None
+
+
+def build(verbose=False, jobs=4, out_dir=None, obj_dir=None, asan=False):
+    """Compile every HIP source and link the shared library.  Returns its path.
+    asan=True builds the host code with AddressSanitizer (into out_dir)."""
     if not os.path.exists(HIPCC):
         raise RuntimeError(f"hipcc not found at {HIPCC}")
-    os.makedirs(OUT_DIR, exist_ok=True)
-    os.makedirs(OBJ_DIR, exist_ok=True)
+    out_dir = out_dir or OUT_DIR
+    obj_dir = obj_dir or OBJ_DIR
+    os.makedirs(out_dir, exist_ok=True)
+    os.makedirs(obj_dir, exist_ok=True)
+    extra = ASAN_HOST_FLAGS if asan else []
     srcs = sources()
-    objs = [os.path.join(OBJ_DIR, os.path.basename(s) + ".o") for s in srcs]
+    objs = [os.path.join(obj_dir, os.path.basename(s) + ".o") for s in srcs]
     with ThreadPoolExecutor(max_workers=jobs) as ex:
-        futs = [ex.submit(_run, [HIPCC] + compile_flags() + ["-c", s, "-o", o], verbose)
+        futs = [ex.submit(_run, [HIPCC] + compile_flags() + extra + ["-c", s, "-o", o], verbose)
                 for s, o in zip(srcs, objs)]
         for f in futs:
             f.result()
-    tmp = os.path.join(OUT_DIR, LIB_NAME + ".tmp")
-    _run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs, verbose)
-    final = os.path.join(OUT_DIR, LIB_NAME)
+    tmp = os.path.join(out_dir, LIB_NAME + ".tmp")
+    link_extra = ["-Xarch_host", "-fsanitize=address", "-shared-libsan"] if asan else []
+    _run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + link_extra + objs,
+         verbose)
+    final = os.path.join(out_dir, LIB_NAME)
     shutil.move(tmp, final)
     return final
 
