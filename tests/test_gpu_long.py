@@ -1,8 +1,8 @@
 """GPU parity of verification attention with long speculated steps (through
 the C ABI): tens to hundreds of drafts per sequence, as when a process reward
 model scores a whole reasoning step in one pass ("HeteroReason").  These
-shapes run on the row-block kernel (128 query rows per workgroup, pages shared
-by its four waves).  Small cases cover k from 17 to 300, GQA groups 1 to 7,
+shapes run on the row-block kernel (256 query rows per workgroup, pages shared
+by its eight waves).  Small cases cover k from 17 to 300, GQA groups 1 to 7,
 bf16 and INT8 caches, d = 64 / 128, S = 0 and ragged mixes; a tree mask with
 more than 128 rows per pair takes the same kernel; the full prm7b_step
 workload is checked on sampled pairs.

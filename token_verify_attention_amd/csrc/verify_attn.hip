@@ -293,8 +293,15 @@ struct Geo {
   // that the LDS reads of a 16-lane group hit distinct banks (a 256-byte bank
   // window holds RPW rows).
   static constexpr int RPW = RB >= 256 ? 1 : 256 / RB;
-  // K: 16 lanes read one chunk (or half chunk) of 16 consecutive rows.
-  static __device__ __forceinline__ int swz_k(int rho) { return (rho / RPW) & (CPR - 1); }
+  // K: 16 lanes read one chunk (or half chunk) of 16 consecutive rows.  Rows
+  // of 256 bytes or more XOR the chunk with the row's two 2-bit halves
+  // swapped: with the plain row index (rows 0-3 reading chunks 0-3, ...), a
+  // 16-byte read of the MFMA operand layout measured 4 bank-conflict cycles
+  // per instruction on gfx950 (126 bytes per clock per CU); with the halves
+  // swapped, none (187 bytes per clock).
+  static __device__ __forceinline__ int swz_k(int rho) {
+    return RB >= 256 ? (((rho & 3) << 2) | ((rho >> 2) & 3)) & (CPR - 1) : (rho / RPW) & (CPR - 1);
+  }
   // V: bf16 -- 4 rows x 32 contiguous bytes (transposing 16-bit reads);
   // INT8 -- 4 rows x 16 bytes of each of 2 pages (transposing 8-bit reads);
   // fp32 -- 4-row quads (VALU path).  The 16-lane groups of rows 4c .. 4c+3
@@ -1136,6 +1143,171 @@ struct MfmaStep {
     }
     if constexpr (I8) softmax_pv_i8<EDGE>(a, second);
     else softmax_pv<EDGE>(a, second, s);
+  }
+
+  // ---- phase-split form (row-block kernel) --------------------------------
+  // The same arithmetic as load() + compute(), cut where the products of one
+  // unit end and its softmax begins: mma_phase() runs every matrix product of
+  // a phase (P.V of the previous unit from the weights held in pw / pe, then
+  // S^T of the current unit), softmax_phase() turns S^T into those weights.
+  // Two waves sharing a SIMD can then run one's products beside the other's
+  // softmax.
+  u32x4 pw[NRB];                          // P operand of the last softmax phase
+  u32x4 pe[NRB];                          // INT8: the unscaled weights (denominator)
+
+  template <bool EDGE>
+  __device__ __forceinline__ void mma_phase(const char* va_page, const char* vb_page, int a_prev,
+                                            bool prev, const char* ka_page, const char* kb_page,
+                                            bool cur) {
+    if (prev) {
+      Op8 va[NDB];
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) va[db] = v_operand(v_raw(va_page, vb_page, db));
+      if constexpr (EDGE && !I8) {
+        if ((a_prev + 2) * kPage > valid_end) {     // garbage rows (may be NaN) read as zero
+          u32x4 keep;
+#pragma unroll
+          for (int h = 0; h < 4; ++h) {
+            const int p0 = (a_prev + (h >> 1)) * kPage + 4 * c + 2 * (h & 1);
+            keep[h] = (p0 < valid_end ? 0x0000ffffu : 0u) | (p0 + 1 < valid_end ? 0xffff0000u : 0u);
+          }
+#pragma unroll
+          for (int db = 0; db < NDB; ++db)
+            va[db] = __builtin_bit_cast(Op8, __builtin_bit_cast(u32x4, va[db]) & keep);
+        }
+      }
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb) {
+        const Op8 pb = __builtin_bit_cast(Op8, pw[rb]);
+        if constexpr (I8) lsum[rb] = mfma32(ones(), __builtin_bit_cast(Op8, pe[rb]), lsum[rb]);
+        sacc[rb] = mfma32(ones(), pb, sacc[rb]);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) acc[rb][db] = mfma32(va[db], pb, acc[rb][db]);
+      }
+      // the V operands die here: the K reads below are not hoisted above
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (cur) {
+      scores(ka_page, kb_page, s);
+      if constexpr (I8) {
+#pragma unroll
+        for (int pg = 0; pg < 2; ++pg) {
+          const char* sc = (pg ? kb_page : ka_page) + 2 * Gm::PAGE;
+          kw[pg] = ld64(sc + 8 * c);
+          vw[pg] = ld64(sc + 32 + 8 * c);
+        }
+      }
+    }
+  }
+
+  template <bool EDGE>
+  __device__ __forceinline__ void softmax_phase(int a, bool second) {
+    const int npg = second ? 2 : 1;
+    if constexpr (I8) {
+      // y = s * k_scale - m in one fma against the running maximum; the
+      // exact maxima only when some row's reference moves
+      uint32_t vs[4] = {vw[0][0], vw[0][1], vw[1][0], vw[1][1]};
+      if constexpr (EDGE) {
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {      // garbage rows (scale may be NaN) weigh zero
+          const int p0 = (a + (h >> 1)) * kPage + 4 * c + 2 * (h & 1);
+          vs[h] &= (p0 < valid_end ? 0x0000ffffu : 0u) | (p0 + 1 < valid_end ? 0xffff0000u : 0u);
+        }
+      }
+      float y[NRB][8];
+      bool move = false;
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb) {
+        float t = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int pg = j >> 2, i = j & 3;
+          const int pos = (a + pg) * kPage + 4 * c + i;
+          const float v = fmaf(s[pg][rb][i], f16x2_half(kw[pg][i >> 1], i & 1), -m[rb]);
+          y[rb][j] = (!EDGE || (pg < npg && visible(pos, rb))) ? v : -INFINITY;
+          t = fmaxf(t, y[rb][j]);
+        }
+        move |= xrow32_max(xrow16_max(t)) > kLazy;
+      }
+      if (__ballot(move)) {
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) {
+          float x[8], t = -INFINITY;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int pg = j >> 2, i = j & 3;
+            const int pos = (a + pg) * kPage + 4 * c + i;
+            const float v = s[pg][rb][i] * f16x2_half(kw[pg][i >> 1], i & 1);
+            x[j] = (!EDGE || (pg < npg && visible(pos, rb))) ? v : -INFINITY;
+            t = fmaxf(t, x[j]);
+          }
+          const float xm = xrow32_max(xrow16_max(t));
+          const float mn = (xm > m[rb] + kLazy) ? xm : m[rb];
+          const float alpha = __builtin_amdgcn_exp2f(m[rb] - mn);
+          m[rb] = mn;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            sacc[rb][i] *= alpha;
+            lsum[rb][i] *= alpha;
+          }
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[rb][db][i] *= alpha;
+          }
+#pragma unroll
+          for (int j = 0; j < 8; ++j) y[rb][j] = x[j] - mn;
+        }
+      }
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb) {
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          pe[rb][h] = pack_f16x2(__builtin_amdgcn_exp2f(y[rb][2 * h]),
+                                 __builtin_amdgcn_exp2f(y[rb][2 * h + 1]));
+          pw[rb][h] = mul_f16x2(pe[rb][h], vs[h]);
+        }
+      }
+    } else {
+      // masked unscaled scores, maxima scaled once per row, one fma per weight
+      float x[NRB][8], mx[NRB];
+      bool move = false;
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb) {
+        float t = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int pg = j >> 2, i = j & 3;
+          const int pos = (a + pg) * kPage + 4 * c + i;
+          x[rb][j] = (!EDGE || (pg < npg && visible(pos, rb))) ? s[pg][rb][i] : -INFINITY;
+          t = fmaxf(t, x[rb][j]);
+        }
+        mx[rb] = xrow32_max(xrow16_max(t)) * scale_log2;
+        move |= mx[rb] > m[rb] + kLazy;
+      }
+      if (__ballot(move)) {
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) {
+          const float mn = (mx[rb] > m[rb] + kLazy) ? mx[rb] : m[rb];
+          const float alpha = __builtin_amdgcn_exp2f(m[rb] - mn);
+          m[rb] = mn;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sacc[rb][i] *= alpha;
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[rb][db][i] *= alpha;
+          }
+        }
+      }
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb) {
+#pragma unroll
+        for (int h = 0; h < 4; ++h)
+          pw[rb][h] = pack_bf16x2(__builtin_amdgcn_exp2f(fmaf(x[rb][2 * h], scale_log2, -m[rb])),
+                                  __builtin_amdgcn_exp2f(fmaf(x[rb][2 * h + 1], scale_log2, -m[rb])));
+      }
+    }
   }
 
   // INT8 caches.  Q carries softmax_scale * log2 e, so a token's score in log2
@@ -2104,45 +2276,73 @@ __global__ __launch_bounds__((AttnLds<KV, D, MF>::NT), 1) void verify_attn_kerne
 // of drafts -- in one pass ("HeteroReason": the PRM verifies a complete step
 // in a single parallel pass).  With k*G query rows per (sequence, kv head) far
 // above 32, splitting the keys over waves (the kernel above) would re-stream
-// the pages once per 32 rows.  Here a workgroup owns a block of 128 query rows
-// of one pair, each of its 4 waves 32 of them, and all four share every page:
-// step s brings pages 4s .. 4s+3 into a workgroup ring (one page copied by
-// each wave), and after one barrier every wave runs its rows over all four.
-// A wave never merges with another, and nothing is split over workgroups, so
-// no workspace is used.  Keys are streamed up to the block's last row's
+// the pages once per 32 rows.  Here a workgroup owns a block of 256 query rows
+// of one pair, each of its 8 waves 32 of them, and all eight share every
+// page.  A unit is two pages; units stream through a workgroup ring of up to 8
+// slots, copied by waves 0 and 1 (one page each) several units ahead.  A wave
+// never merges with another, and nothing is split over workgroups, so no
+// workspace is used.  Keys are streamed up to the block's last row's
 // position; the causal (or tree) mask applies on the pages holding drafts.
-// The steps that need no mask run in a loop of their own: with both step
-// kinds in one loop body the compiler keeps two copies of the accumulators
-// at the join and spills the query operands.
+//
+// Each SIMD holds one wave of each half of the workgroup (waves w and w + 4).
+// Per unit a wave runs a product phase (P.V of the previous unit, S^T of this
+// one: matrix cores and LDS reads) and a softmax phase (vector ALU only).  The
+// two halves run them half a unit apart, separated by workgroup barriers:
+//
+//   phase 2w     first half: products of unit w      second half: softmax of unit w-1
+//   phase 2w+1   first half: softmax of unit w       second half: products of unit w
+//
+// so on every SIMD one wave's matrix products run beside the other wave's
+// softmax, and the product phases run at raised wave priority.  Slot of unit
+// u: read in phases 2u .. 2u+3, refilled (unit u + NS) from phase 2u+4 on.
+// Iterations whose units need no mask run in a loop of their own: with both
+// kinds in one loop body the compiler keeps two copies of the accumulators at
+// the join and spills the query operands.
 
-constexpr int kRowWaves = 4;                       // one wave per SIMD per workgroup
-constexpr int kRowBlock = kRowWaves * kMfmaRows;   // 128 query rows per workgroup
-constexpr int kRowPages = 4;                       // pages per step, one per copying wave
+constexpr int kRowWaves = 8;                       // two waves per SIMD
+constexpr int kRowHalf = kRowWaves / 2;
+constexpr int kRowBlock = kRowWaves * kMfmaRows;   // 256 query rows per workgroup
 
-// Two workgroups per CU (two waves per SIMD: one wave's LDS reads and softmax
-// run while the other's MFMAs do); every step fits in 256 VGPRs.
 template <typename KV, int D>
 struct RowsLds {
-  using Gm = Geo<KV, D, kRowWaves>;
-  static constexpr int OCC = 2;
-  static constexpr int BUDGET = OCC > 1 ? 72 * 1024 : kRingBudget;
-  static constexpr int STEP = kRowPages * Gm::SLOT;   // the pages (K, V, scales) of one step
-  static constexpr int NS_RAW = BUDGET / STEP;
-  static constexpr int NS = NS_RAW < 2 ? 2 : (NS_RAW > 4 ? 4 : NS_RAW);   // steps in the ring
-  static constexpr int RING = NS * STEP;
+  using Gm = Geo<KV, D, kWavesValu>;
+  static constexpr int UNIT = 2 * Gm::SLOT;          // K, V (and scales) of two pages
+  static constexpr int NS_RAW = (128 * 1024) / UNIT;
+  static constexpr int NS = NS_RAW > 8 ? 8 : NS_RAW;  // units held in the ring
+  static constexpr int RING = NS * UNIT;
+  static_assert(NS >= 4, "ring too small");
+  static_assert((NS - 3) * Gm::P <= 63, "vmcnt range");
 };
 
-// Row blocks of sequence b: Hkv * ceil(k_b * G / 128).
+// Row blocks of sequence b: Hkv * ceil(k_b * G / 256).
 __device__ __forceinline__ int row_blocks(const AttnParams& p, const SeqInfo& si) {
   return si.k > 0 ? p.Hkv * ((si.k * p.G + kRowBlock - 1) / kRowBlock) : 0;
+}
+
+// Wait until at most n (<= MAXN) later units of P copies each are in flight.
+template <int P, int MAXN>
+__device__ __forceinline__ void wait_units(int n) {
+  if constexpr (MAXN > 0) {
+    if (n >= MAXN) {
+      wait_vm<MAXN * P>();
+      return;
+    }
+    wait_units<P, MAXN - 1>(n);
+  } else {
+    wait_vm<0>();
+  }
+}
+
+__device__ __forceinline__ void block_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 // kTree: the call carries tree masks (at most 32 drafts, mask form); causal
 // calls keep draft indices (any number of drafts).
 template <typename KV, int D, bool kTree>
-__global__ __launch_bounds__(kRowWaves * kWave, (RowsLds<KV, D>::OCC))
+__global__ __launch_bounds__(kRowWaves * kWave, 1)
 void verify_attn_rows_kernel(AttnParams p) {
-  using Gm = Geo<KV, D, kRowWaves>;
+  using Gm = Geo<KV, D, kWavesValu>;
   using L = RowsLds<KV, D>;
   constexpr int NS = L::NS;
   constexpr int NT = kRowWaves * kWave;
@@ -2181,11 +2381,16 @@ void verify_attn_rows_kernel(AttnParams p) {
   }
   __syncthreads();
   const int total = s_info[0];
-  // consecutive blocks (the row blocks of one pair) go to one XCD
+  // Workgroups are dispatched to the 8 XCDs in turn (blockIdx.x % 8), one per
+  // CU here (the ring takes most of the LDS): XCD x takes blocks
+  // x * ceil(total / 8) onwards, so every XCD holds an equal share and
+  // consecutive blocks (the row blocks of one pair, which read the same
+  // pages) share an L2.  The grid is a multiple of 8 at least total.
   const int hw = blockIdx.x;
-  const int W = gridDim.x;
-  const int w = (W % 8 == 0) ? (hw % 8) * (W / 8) + hw / 8 : hw;
-  if (w >= total) return;
+  const int per_xcd = (total + 7) / 8;
+  const int j = hw / 8;
+  const int w = (hw % 8) * per_xcd + j;
+  if (j >= per_xcd || w >= total) return;
   {
     const int base = s_scan[tid];
     if (tot > 0 && base <= w && w < base + tot) {
@@ -2219,58 +2424,81 @@ void verify_attn_rows_kernel(AttnParams p) {
   sg.slot = 0;
   const int r0 = (s_info[2] % nblk) * kRowBlock;
   const int last_row = min(sg.R, r0 + kRowBlock) - 1;
-  // keys up to the last row's position: pages 0 .. npages-1
+  // keys up to the last row's position: pages 0 .. npages-1, in units of two
   const int npages = min(si.np, (si.S + last_row / p.G) / kPage + 1);
   sg.pe = npages;
+  const int nunits = (npages + 1) / 2;
+  // units below u_plain hold committed context only: no masks
+  const int u_plain = min(nunits, si.S / (2 * kPage));
   const int wave = wave_id();
+  const int half = wave / kRowHalf;
   const int rw = r0 + kMfmaRows * wave;            // this wave's first row
   const bool active = rw < sg.R;                    // wave-uniform
   MfmaStep<KV, D, 2, !kTree> st(p, sg, rw);
-  const int nsteps = (npages + kRowPages - 1) / kRowPages;
-  // waves 0 .. kRowPages-1 copy one page each per step (past the end: a copy of
-  // the last page, never used), so their copy counts -- and waits -- are
-  // uniform; any other wave only meets them at the step barrier
-  static_assert(kRowPages <= kRowWaves && kRowPages % 2 == 0, "page copies per step");
-  const bool copier = wave < kRowPages;
-  auto issue = [&](int s) {
-    if (!copier) return;
-    const int pg = min(kRowPages * s + wave, npages - 1);
+  const bool copier = wave < 2;
+  auto slot = [&](int u) -> const char* { return s_ring + (u % NS) * L::UNIT; };
+  auto issue = [&](int u) {                         // wave 0: page 2u, wave 1: page 2u+1
+    if (u >= nunits) return;
+    const int pg = min(2 * u + wave, npages - 1);   // past the end: the last page, unused
     dma_page<KV, D, false>(p, page_id(p, b, pg), sg.g,
-                           s_ring + (s % NS) * L::STEP + wave * Gm::SLOT);
+                           s_ring + (u % NS) * L::UNIT + wave * Gm::SLOT);
   };
-  for (int s = 0; s < NS - 1 && s < nsteps; ++s) issue(s);
+  // copies of unit u landed (this wave's), later units may still fly
+  auto wait_unit = [&](int u) {
+    if (copier && u < nunits) wait_units<Gm::P, NS - 3>(min(NS - 3, nunits - 1 - u));
+  };
+  if (copier) {
+    for (int u = 0; u < NS - 2; ++u) issue(u);
+  }
   st.ready();
-  // One step: wait for this wave's copies of step s; after the barrier every
-  // page of step s is in LDS and slot s-1 (read by every wave) is free.
-  auto step = [&](int s, auto edge) {
+  wait_unit(0);
+  block_barrier();
+
+  auto products = [&](int u, auto edge) {           // P.V of unit u-1, S^T of unit u
     constexpr bool EDGE = decltype(edge)::value;
-    if (copier) wait_steps<Gm::P, NS - 1>(min(NS - 2, nsteps - 1 - s));
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    if (s + NS - 1 < nsteps) issue(s + NS - 1);
-    if (!active) return;
-    const char* base = s_ring + (s % NS) * L::STEP;
-    // one unit (two pages) at a time: unrolled, the compiler hoists the
-    // second unit's LDS reads and holds both units' operands (256 VGPRs and
-    // spills, 5-7 % slower on the 7B reward-model shape); issuing the second
-    // unit's score MFMAs ahead of the first unit's softmax was slower still
-#pragma unroll 1
-    for (int u = 0; u < kRowPages / 2; ++u) {
-      const int a = kRowPages * s + 2 * u;
-      if (EDGE && a >= npages) break;
-      const char* sa = base + 2 * u * Gm::SLOT;
-      st.load(sa, sa + Gm::SLOT);
-      st.template compute<EDGE>(a, !EDGE || a + 1 < npages);
-    }
+    __builtin_amdgcn_s_setprio(1);
+    const char* cu = slot(u);
+    const char* pu = slot(u + NS - 1);              // unit u-1
+    st.template mma_phase<EDGE>(pu, pu + Gm::SLOT, 2 * (u - 1), u > 0, cu, cu + Gm::SLOT,
+                                u < nunits);
+    __builtin_amdgcn_s_setprio(0);
   };
-  // Steps whose pages all lie inside the committed context need no masks;
-  // two separate loops keep each one's body straight-line code, so the
-  // accumulators stay in place across iterations.
-  const int s_plain = min(nsteps, (sg.S / kPage) / kRowPages);
-  int s = 0;
-  for (; s < s_plain; ++s) step(s, std::false_type{});
-  for (; s < nsteps; ++s) step(s, std::true_type{});
-  st.finish();
-  if (active) st.write_rows(p, sg, rw);
+  auto softmax = [&](int u, auto edge) {
+    constexpr bool EDGE = decltype(edge)::value;
+    st.template softmax_phase<EDGE>(2 * u, 2 * u + 1 < npages);
+  };
+  // iteration w: phases 2w and 2w+1 (the copies of unit w + NS - 2 go into
+  // the slot that unit w - 2 left in phase 2w - 1).  Each half runs a loop of
+  // its own, so each loop body is straight-line code; both halves pass the
+  // same number of barriers.  A wave without rows only keeps the barriers
+  // (and its copies).
+  if (half == 0) {
+    auto iteration = [&](int w, auto edge) {
+      if (copier) issue(w + NS - 2);
+      if (active) products(w, edge);
+      block_barrier();
+      if (active && w < nunits) softmax(w, edge);
+      wait_unit(w + 1);
+      block_barrier();
+    };
+    int it = 0;
+    for (; it < u_plain; ++it) iteration(it, std::false_type{});
+    for (; it <= nunits; ++it) iteration(it, std::true_type{});
+  } else {
+    auto iteration = [&](int w, auto edge) {
+      if (active && w > 0) softmax(w - 1, edge);
+      block_barrier();
+      if (active) products(w, edge);
+      block_barrier();
+    };
+    int it = 0;
+    for (; it < u_plain; ++it) iteration(it, std::false_type{});
+    for (; it <= nunits; ++it) iteration(it, std::true_type{});
+  }
+  if (active) {
+    st.finish();
+    st.write_rows(p, sg, rw);
+  }
 }
 
 // ============================================================================
@@ -2290,7 +2518,8 @@ AttnPlan plan_verify_attn(const sva_batch* batch, const sva_paged_kv* kv, int Hq
       int64_t(kv->Hkv) * ((int64_t(batch->total_q) * G + kRowBlock - 1) / kRowBlock + batch->B);
   pl.rows_kernel = mfma_ok && (batch->max_q > kMaxDraftsSplit || rows > kMaxRowsSplit ||
                                (rows > kMfmaRows && blocks_ub >= num_cus));
-  pl.rows_grid = int(std::min<int64_t>(blocks_ub, 0x7fffffff));
+  // a multiple of 8 (the kernel spreads its blocks evenly over the 8 XCDs)
+  pl.rows_grid = int(std::min<int64_t>((blocks_ub + 7) / 8 * 8, 0x7ffffff8));
   const int64_t pages_per_seq =
       std::min<int64_t>(kv->max_pages_per_seq, (int64_t(batch->max_len) + kPage - 1) / kPage);
   const int64_t pages_ub = int64_t(batch->B) * kv->Hkv * std::max<int64_t>(pages_per_seq, 1);
