@@ -1145,171 +1145,6 @@ struct MfmaStep {
     else softmax_pv<EDGE>(a, second, s);
   }
 
-  // ---- phase-split form (row-block kernel) --------------------------------
-  // The same arithmetic as load() + compute(), cut where the products of one
-  // unit end and its softmax begins: mma_phase() runs every matrix product of
-  // a phase (P.V of the previous unit from the weights held in pw / pe, then
-  // S^T of the current unit), softmax_phase() turns S^T into those weights.
-  // Two waves sharing a SIMD can then run one's products beside the other's
-  // softmax.
-  u32x4 pw[NRB];                          // P operand of the last softmax phase
-  u32x4 pe[NRB];                          // INT8: the unscaled weights (denominator)
-
-  template <bool EDGE>
-  __device__ __forceinline__ void mma_phase(const char* va_page, const char* vb_page, int a_prev,
-                                            bool prev, const char* ka_page, const char* kb_page,
-                                            bool cur) {
-    if (prev) {
-      Op8 va[NDB];
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) va[db] = v_operand(v_raw(va_page, vb_page, db));
-      if constexpr (EDGE && !I8) {
-        if ((a_prev + 2) * kPage > valid_end) {     // garbage rows (may be NaN) read as zero
-          u32x4 keep;
-#pragma unroll
-          for (int h = 0; h < 4; ++h) {
-            const int p0 = (a_prev + (h >> 1)) * kPage + 4 * c + 2 * (h & 1);
-            keep[h] = (p0 < valid_end ? 0x0000ffffu : 0u) | (p0 + 1 < valid_end ? 0xffff0000u : 0u);
-          }
-#pragma unroll
-          for (int db = 0; db < NDB; ++db)
-            va[db] = __builtin_bit_cast(Op8, __builtin_bit_cast(u32x4, va[db]) & keep);
-        }
-      }
-#pragma unroll
-      for (int rb = 0; rb < NRB; ++rb) {
-        const Op8 pb = __builtin_bit_cast(Op8, pw[rb]);
-        if constexpr (I8) lsum[rb] = mfma32(ones(), __builtin_bit_cast(Op8, pe[rb]), lsum[rb]);
-        sacc[rb] = mfma32(ones(), pb, sacc[rb]);
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) acc[rb][db] = mfma32(va[db], pb, acc[rb][db]);
-      }
-      // the V operands die here: the K reads below are not hoisted above
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    if (cur) {
-      scores(ka_page, kb_page, s);
-      if constexpr (I8) {
-#pragma unroll
-        for (int pg = 0; pg < 2; ++pg) {
-          const char* sc = (pg ? kb_page : ka_page) + 2 * Gm::PAGE;
-          kw[pg] = ld64(sc + 8 * c);
-          vw[pg] = ld64(sc + 32 + 8 * c);
-        }
-      }
-    }
-  }
-
-  template <bool EDGE>
-  __device__ __forceinline__ void softmax_phase(int a, bool second) {
-    const int npg = second ? 2 : 1;
-    if constexpr (I8) {
-      // y = s * k_scale - m in one fma against the running maximum; the
-      // exact maxima only when some row's reference moves
-      uint32_t vs[4] = {vw[0][0], vw[0][1], vw[1][0], vw[1][1]};
-      if constexpr (EDGE) {
-#pragma unroll
-        for (int h = 0; h < 4; ++h) {      // garbage rows (scale may be NaN) weigh zero
-          const int p0 = (a + (h >> 1)) * kPage + 4 * c + 2 * (h & 1);
-          vs[h] &= (p0 < valid_end ? 0x0000ffffu : 0u) | (p0 + 1 < valid_end ? 0xffff0000u : 0u);
-        }
-      }
-      float y[NRB][8];
-      bool move = false;
-#pragma unroll
-      for (int rb = 0; rb < NRB; ++rb) {
-        float t = -INFINITY;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int pg = j >> 2, i = j & 3;
-          const int pos = (a + pg) * kPage + 4 * c + i;
-          const float v = fmaf(s[pg][rb][i], f16x2_half(kw[pg][i >> 1], i & 1), -m[rb]);
-          y[rb][j] = (!EDGE || (pg < npg && visible(pos, rb))) ? v : -INFINITY;
-          t = fmaxf(t, y[rb][j]);
-        }
-        move |= xrow32_max(xrow16_max(t)) > kLazy;
-      }
-      if (__ballot(move)) {
-#pragma unroll
-        for (int rb = 0; rb < NRB; ++rb) {
-          float x[8], t = -INFINITY;
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const int pg = j >> 2, i = j & 3;
-            const int pos = (a + pg) * kPage + 4 * c + i;
-            const float v = s[pg][rb][i] * f16x2_half(kw[pg][i >> 1], i & 1);
-            x[j] = (!EDGE || (pg < npg && visible(pos, rb))) ? v : -INFINITY;
-            t = fmaxf(t, x[j]);
-          }
-          const float xm = xrow32_max(xrow16_max(t));
-          const float mn = (xm > m[rb] + kLazy) ? xm : m[rb];
-          const float alpha = __builtin_amdgcn_exp2f(m[rb] - mn);
-          m[rb] = mn;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            sacc[rb][i] *= alpha;
-            lsum[rb][i] *= alpha;
-          }
-#pragma unroll
-          for (int db = 0; db < NDB; ++db) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) acc[rb][db][i] *= alpha;
-          }
-#pragma unroll
-          for (int j = 0; j < 8; ++j) y[rb][j] = x[j] - mn;
-        }
-      }
-#pragma unroll
-      for (int rb = 0; rb < NRB; ++rb) {
-#pragma unroll
-        for (int h = 0; h < 4; ++h) {
-          pe[rb][h] = pack_f16x2(__builtin_amdgcn_exp2f(y[rb][2 * h]),
-                                 __builtin_amdgcn_exp2f(y[rb][2 * h + 1]));
-          pw[rb][h] = mul_f16x2(pe[rb][h], vs[h]);
-        }
-      }
-    } else {
-      // masked unscaled scores, maxima scaled once per row, one fma per weight
-      float x[NRB][8], mx[NRB];
-      bool move = false;
-#pragma unroll
-      for (int rb = 0; rb < NRB; ++rb) {
-        float t = -INFINITY;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int pg = j >> 2, i = j & 3;
-          const int pos = (a + pg) * kPage + 4 * c + i;
-          x[rb][j] = (!EDGE || (pg < npg && visible(pos, rb))) ? s[pg][rb][i] : -INFINITY;
-          t = fmaxf(t, x[rb][j]);
-        }
-        mx[rb] = xrow32_max(xrow16_max(t)) * scale_log2;
-        move |= mx[rb] > m[rb] + kLazy;
-      }
-      if (__ballot(move)) {
-#pragma unroll
-        for (int rb = 0; rb < NRB; ++rb) {
-          const float mn = (mx[rb] > m[rb] + kLazy) ? mx[rb] : m[rb];
-          const float alpha = __builtin_amdgcn_exp2f(m[rb] - mn);
-          m[rb] = mn;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) sacc[rb][i] *= alpha;
-#pragma unroll
-          for (int db = 0; db < NDB; ++db) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) acc[rb][db][i] *= alpha;
-          }
-        }
-      }
-#pragma unroll
-      for (int rb = 0; rb < NRB; ++rb) {
-#pragma unroll
-        for (int h = 0; h < 4; ++h)
-          pw[rb][h] = pack_bf16x2(__builtin_amdgcn_exp2f(fmaf(x[rb][2 * h], scale_log2, -m[rb])),
-                                  __builtin_amdgcn_exp2f(fmaf(x[rb][2 * h + 1], scale_log2, -m[rb])));
-      }
-    }
-  }
-
   // INT8 caches.  Q carries softmax_scale * log2 e, so a token's score in log2
   // units is s * k_scale, and y = s * k_scale - m is one v_fma_mix_f32 with the
   // fp16 scale as an operand.  Weights: e = 2^y packed to fp16 (the unscaled
@@ -1664,6 +1499,230 @@ struct MfmaStep {
   }
 };
 
+
+// ---- phase-split form of the MFMA step (row-block kernel) -----------------
+// The arithmetic of MfmaStep (NRB = 2: 32 query rows per wave) on groups of
+// NU units (2 NU pages), cut where the products of a group end and its
+// softmax begins: mma_phase() runs every matrix product of a phase -- P.V of
+// the previous group from the weights held in pw / pe, then S^T of the
+// current group -- and softmax_phase() turns S^T into those weights (one
+// reference update per group).  Two waves sharing a SIMD can then run one's
+// products beside the other's softmax.
+template <typename KV, int D, int NU, bool kIdx>
+struct PhaseStep : MfmaStep<KV, D, 2, kIdx> {
+  using Base = MfmaStep<KV, D, 2, kIdx>;
+  using Op8 = typename Base::Op8;
+  using Gm = typename Base::Gm;
+  static constexpr bool I8 = Base::I8;
+  static constexpr int NRB = 2;
+  static constexpr int NDB = Base::NDB;
+  static constexpr int NP = 2 * NU;       // pages per group
+  static constexpr float kLazy = Base::kLazy;
+  using Base::acc;
+  using Base::sacc;
+  using Base::lsum;
+  using Base::m;
+  using Base::c;
+  using Base::valid_end;
+  using Base::scale_log2;
+
+  f32x4 sp[NP][NRB];                      // S^T of the group (unscaled)
+  u32x4 pw[NU][NRB];                      // P operands of the last softmax phase
+  u32x4 pe[NU][NRB];                      // INT8: the unscaled weights (denominator)
+  u32x2 kwp[NP], vwp[NP];                 // INT8: K and V scales of lane's 4 tokens
+
+  __device__ __forceinline__ PhaseStep(const AttnParams& p, const Seg& sg, int r0)
+      : Base(p, sg, r0) {}
+
+  // pages of a group: NP consecutive ring slots from `base`
+  static __device__ __forceinline__ const char* page(const char* base, int j) {
+    return base + j * Gm::SLOT;
+  }
+
+  template <bool EDGE>
+  __device__ __forceinline__ void mma_phase(const char* prev_base, int a_prev, bool prev,
+                                            const char* cur_base, bool cur) {
+    if (prev) {
+#pragma unroll
+      for (int u = 0; u < NU; ++u) {
+        const char* sa = page(prev_base, 2 * u);
+        const char* sb = page(prev_base, 2 * u + 1);
+        Op8 va[NDB];
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) va[db] = Base::v_operand(this->v_raw(sa, sb, db));
+        if constexpr (EDGE && !I8) {
+          const int a = a_prev + 2 * u;
+          if ((a + 2) * kPage > valid_end) {        // garbage rows (may be NaN) read as zero
+            u32x4 keep;
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+              const int p0 = (a + (h >> 1)) * kPage + 4 * c + 2 * (h & 1);
+              keep[h] = (p0 < valid_end ? 0x0000ffffu : 0u) | (p0 + 1 < valid_end ? 0xffff0000u : 0u);
+            }
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+              va[db] = __builtin_bit_cast(Op8, __builtin_bit_cast(u32x4, va[db]) & keep);
+          }
+        }
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) {
+          const Op8 pb = __builtin_bit_cast(Op8, pw[u][rb]);
+          if constexpr (I8)
+            lsum[rb] = Base::mfma32(Base::ones(), __builtin_bit_cast(Op8, pe[u][rb]), lsum[rb]);
+          sacc[rb] = Base::mfma32(Base::ones(), pb, sacc[rb]);
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) acc[rb][db] = Base::mfma32(va[db], pb, acc[rb][db]);
+        }
+      }
+    }
+    if (cur) {
+#pragma unroll
+      for (int pg = 0; pg < NP; ++pg) {
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) {
+          const float z = I8 ? this->s0[rb] : 0.f;
+          sp[pg][rb] = f32x4{z, z, z, z};
+        }
+#pragma unroll
+        for (int ks = 0; ks < Base::KS; ++ks) {
+          const Op8 ka = this->k_operand(page(cur_base, pg), ks);
+#pragma unroll
+          for (int rb = 0; rb < NRB; ++rb)
+            sp[pg][rb] = Base::mfma32(ka, this->qB[rb][ks], sp[pg][rb]);
+        }
+      }
+      if constexpr (I8) {
+#pragma unroll
+        for (int pg = 0; pg < NP; ++pg) {
+          const char* sc = page(cur_base, pg) + 2 * Gm::PAGE;
+          kwp[pg] = ld64(sc + 8 * c);
+          vwp[pg] = ld64(sc + 32 + 8 * c);
+        }
+      }
+    }
+  }
+
+  // Softmax of the group whose first page is a (pages a .. a + NP - 1; those
+  // at or past npages are copies, masked).
+  template <bool EDGE>
+  __device__ __forceinline__ void softmax_phase(int a, int npages) {
+    constexpr int NV = 4 * NP;            // values per row block and lane
+    if constexpr (I8) {
+      // y = s * k_scale - m in one fma against the running maximum; the
+      // exact maxima only when some row's reference moves
+      float y[NRB][NV];
+      bool move = false;
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb) {
+        float t = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+          const int pg = j >> 2, i = j & 3;
+          const int pos = (a + pg) * kPage + 4 * c + i;
+          const float v = fmaf(sp[pg][rb][i], f16x2_half(kwp[pg][i >> 1], i & 1), -m[rb]);
+          y[rb][j] = (!EDGE || (a + pg < npages && this->visible(pos, rb))) ? v : -INFINITY;
+          t = fmaxf(t, y[rb][j]);
+        }
+        move |= xrow32_max(xrow16_max(t)) > kLazy;
+      }
+      if (__ballot(move)) {
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) {
+          float x[NV], t = -INFINITY;
+#pragma unroll
+          for (int j = 0; j < NV; ++j) {
+            const int pg = j >> 2, i = j & 3;
+            const int pos = (a + pg) * kPage + 4 * c + i;
+            const float v = sp[pg][rb][i] * f16x2_half(kwp[pg][i >> 1], i & 1);
+            x[j] = (!EDGE || (a + pg < npages && this->visible(pos, rb))) ? v : -INFINITY;
+            t = fmaxf(t, x[j]);
+          }
+          const float xm = xrow32_max(xrow16_max(t));
+          const float mn = (xm > m[rb] + kLazy) ? xm : m[rb];
+          const float alpha = __builtin_amdgcn_exp2f(m[rb] - mn);
+          m[rb] = mn;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            sacc[rb][i] *= alpha;
+            lsum[rb][i] *= alpha;
+          }
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[rb][db][i] *= alpha;
+          }
+#pragma unroll
+          for (int j = 0; j < NV; ++j) y[rb][j] = x[j] - mn;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < NU; ++u) {
+        // V scales of the lane's tokens as fp16 pairs, in k-slot order
+        uint32_t vs[4] = {vwp[2 * u][0], vwp[2 * u][1], vwp[2 * u + 1][0], vwp[2 * u + 1][1]};
+        if constexpr (EDGE) {
+#pragma unroll
+          for (int h = 0; h < 4; ++h) {    // garbage rows (scale may be NaN) weigh zero
+            const int p0 = (a + 2 * u + (h >> 1)) * kPage + 4 * c + 2 * (h & 1);
+            vs[h] &= (p0 < valid_end ? 0x0000ffffu : 0u) | (p0 + 1 < valid_end ? 0xffff0000u : 0u);
+          }
+        }
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) {
+#pragma unroll
+          for (int h = 0; h < 4; ++h) {
+            pe[u][rb][h] = pack_f16x2(__builtin_amdgcn_exp2f(y[rb][8 * u + 2 * h]),
+                                      __builtin_amdgcn_exp2f(y[rb][8 * u + 2 * h + 1]));
+            pw[u][rb][h] = mul_f16x2(pe[u][rb][h], vs[h]);
+          }
+        }
+      }
+    } else {
+      // masked unscaled scores, maxima scaled once per row, one fma per weight
+      float x[NRB][NV], mx[NRB];
+      bool move = false;
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb) {
+        float t = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+          const int pg = j >> 2, i = j & 3;
+          const int pos = (a + pg) * kPage + 4 * c + i;
+          x[rb][j] = (!EDGE || (a + pg < npages && this->visible(pos, rb))) ? sp[pg][rb][i]
+                                                                               : -INFINITY;
+          t = fmaxf(t, x[rb][j]);
+        }
+        mx[rb] = xrow32_max(xrow16_max(t)) * scale_log2;
+        move |= mx[rb] > m[rb] + kLazy;
+      }
+      if (__ballot(move)) {
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) {
+          const float mn = (mx[rb] > m[rb] + kLazy) ? mx[rb] : m[rb];
+          const float alpha = __builtin_amdgcn_exp2f(m[rb] - mn);
+          m[rb] = mn;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sacc[rb][i] *= alpha;
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[rb][db][i] *= alpha;
+          }
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < NU; ++u) {
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) {
+#pragma unroll
+          for (int h = 0; h < 4; ++h)
+            pw[u][rb][h] = pack_bf16x2(
+                __builtin_amdgcn_exp2f(fmaf(x[rb][8 * u + 2 * h], scale_log2, -m[rb])),
+                __builtin_amdgcn_exp2f(fmaf(x[rb][8 * u + 2 * h + 1], scale_log2, -m[rb])));
+        }
+      }
+    }
+  }
+};
 
 // ============================================================================
 // cross-workgroup merge of a pair split over several workgroups
@@ -2278,23 +2337,27 @@ __global__ __launch_bounds__((AttnLds<KV, D, MF>::NT), 1) void verify_attn_kerne
 // above 32, splitting the keys over waves (the kernel above) would re-stream
 // the pages once per 32 rows.  Here a workgroup owns a block of 256 query rows
 // of one pair, each of its 8 waves 32 of them, and all eight share every
-// page.  A unit is two pages; units stream through a workgroup ring of up to 8
-// slots, copied by waves 0 and 1 (one page each) several units ahead.  A wave
-// never merges with another, and nothing is split over workgroups, so no
-// workspace is used.  Keys are streamed up to the block's last row's
+// page.  A group is NU units of two pages (bf16: 2, INT8: 1, whose operands
+// take more registers); groups stream through a workgroup ring of 4 to 8
+// slots, copied by 2 NU waves of the second half (one page each, at the start
+// of their softmax phase, the phase with time to spare) several groups ahead.
+// A wave never merges with another, and nothing is split over workgroups, so
+// no workspace is used.  Keys are streamed up to the block's last row's
 // position; the causal (or tree) mask applies on the pages holding drafts.
 //
 // Each SIMD holds one wave of each half of the workgroup (waves w and w + 4).
-// Per unit a wave runs a product phase (P.V of the previous unit, S^T of this
-// one: matrix cores and LDS reads) and a softmax phase (vector ALU only).  The
-// two halves run them half a unit apart, separated by workgroup barriers:
+// Per group a wave runs a product phase (P.V of the previous group, S^T of
+// this one: matrix cores and LDS reads) and a softmax phase (vector ALU only).
+// The two halves run them half a group apart, separated by workgroup barriers:
 //
-//   phase 2w     first half: products of unit w      second half: softmax of unit w-1
-//   phase 2w+1   first half: softmax of unit w       second half: products of unit w
+//   phase 2w     first half: products of group w     second half: softmax of group w-1
+//   phase 2w+1   first half: softmax of group w      second half: products of group w
 //
 // so on every SIMD one wave's matrix products run beside the other wave's
-// softmax, and the product phases run at raised wave priority.  Slot of unit
-// u: read in phases 2u .. 2u+3, refilled (unit u + NS) from phase 2u+4 on.
+// softmax, and the product phases run at raised wave priority (without it:
+// 5 % slower).  Two units per group halve the barriers per page against one
+// (7B reward-model shape: 144 us against 155).  Slot of group u: read in
+// phases 2u .. 2u+3, refilled (group u + NS) from phase 2u+4 on.
 // Iterations whose units need no mask run in a loop of their own: with both
 // kinds in one loop body the compiler keeps two copies of the accumulators at
 // the join and spills the query operands.
@@ -2306,9 +2369,11 @@ constexpr int kRowBlock = kRowWaves * kMfmaRows;   // 256 query rows per workgro
 template <typename KV, int D>
 struct RowsLds {
   using Gm = Geo<KV, D, kWavesValu>;
-  static constexpr int UNIT = 2 * Gm::SLOT;          // K, V (and scales) of two pages
+  static constexpr int NU = sizeof(KV) == 1 ? 1 : 2;  // units per group
+  static constexpr int NP = 2 * NU;                   // pages per group
+  static constexpr int UNIT = NP * Gm::SLOT;          // K, V (and scales) of a group
   static constexpr int NS_RAW = (128 * 1024) / UNIT;
-  static constexpr int NS = NS_RAW > 8 ? 8 : NS_RAW;  // units held in the ring
+  static constexpr int NS = NS_RAW > 8 ? 8 : NS_RAW;  // groups held in the ring
   static constexpr int RING = NS * UNIT;
   static_assert(NS >= 4, "ring too small");
   static_assert((NS - 3) * Gm::P <= 63, "vmcnt range");
@@ -2424,27 +2489,30 @@ void verify_attn_rows_kernel(AttnParams p) {
   sg.slot = 0;
   const int r0 = (s_info[2] % nblk) * kRowBlock;
   const int last_row = min(sg.R, r0 + kRowBlock) - 1;
-  // keys up to the last row's position: pages 0 .. npages-1, in units of two
+  // keys up to the last row's position: pages 0 .. npages-1, in groups of NP
+  constexpr int NP = L::NP;
   const int npages = min(si.np, (si.S + last_row / p.G) / kPage + 1);
   sg.pe = npages;
-  const int nunits = (npages + 1) / 2;
-  // units below u_plain hold committed context only: no masks
-  const int u_plain = min(nunits, si.S / (2 * kPage));
+  const int nunits = (npages + NP - 1) / NP;
+  // groups below u_plain hold committed context only: no masks
+  const int u_plain = min(nunits, si.S / (NP * kPage));
   const int wave = wave_id();
   const int half = wave / kRowHalf;
   const int rw = r0 + kMfmaRows * wave;            // this wave's first row
   const bool active = rw < sg.R;                    // wave-uniform
-  MfmaStep<KV, D, 2, !kTree> st(p, sg, rw);
-  const bool copier = wave < 2;
-  auto slot = [&](int u) -> const char* { return s_ring + (u % NS) * L::UNIT; };
-  auto issue = [&](int u) {                         // wave 0: page 2u, wave 1: page 2u+1
+  PhaseStep<KV, D, L::NU, !kTree> st(p, sg, rw);
+  // the copies come from the second half, at the start of its softmax phase
+  const int cw = wave - kRowHalf;
+  const bool copier = cw >= 0 && cw < NP;
+  auto slot = [&](int u) __attribute__((always_inline)) -> const char* { return s_ring + (u % NS) * L::UNIT; };
+  auto issue = [&](int u) __attribute__((always_inline)) {                         // wave j: page NP u + j
     if (u >= nunits) return;
-    const int pg = min(2 * u + wave, npages - 1);   // past the end: the last page, unused
+    const int pg = min(NP * u + cw, npages - 1);    // past the end: the last page, unused
     dma_page<KV, D, false>(p, page_id(p, b, pg), sg.g,
-                           s_ring + (u % NS) * L::UNIT + wave * Gm::SLOT);
+                           s_ring + (u % NS) * L::UNIT + cw * Gm::SLOT);
   };
-  // copies of unit u landed (this wave's), later units may still fly
-  auto wait_unit = [&](int u) {
+  // copies of group u landed (this wave's), later groups may still fly
+  auto wait_unit = [&](int u) __attribute__((always_inline)) {
     if (copier && u < nunits) wait_units<Gm::P, NS - 3>(min(NS - 3, nunits - 1 - u));
   };
   if (copier) {
@@ -2454,41 +2522,39 @@ void verify_attn_rows_kernel(AttnParams p) {
   wait_unit(0);
   block_barrier();
 
-  auto products = [&](int u, auto edge) {           // P.V of unit u-1, S^T of unit u
+  auto products = [&](int u, auto edge) __attribute__((always_inline)) {           // P.V of group u-1, S^T of group u
     constexpr bool EDGE = decltype(edge)::value;
     __builtin_amdgcn_s_setprio(1);
-    const char* cu = slot(u);
-    const char* pu = slot(u + NS - 1);              // unit u-1
-    st.template mma_phase<EDGE>(pu, pu + Gm::SLOT, 2 * (u - 1), u > 0, cu, cu + Gm::SLOT,
-                                u < nunits);
+    st.template mma_phase<EDGE>(slot(u + NS - 1), NP * (u - 1), u > 0, slot(u), u < nunits);
     __builtin_amdgcn_s_setprio(0);
   };
-  auto softmax = [&](int u, auto edge) {
+  auto softmax = [&](int u, auto edge) __attribute__((always_inline)) {
     constexpr bool EDGE = decltype(edge)::value;
-    st.template softmax_phase<EDGE>(2 * u, 2 * u + 1 < npages);
+    st.template softmax_phase<EDGE>(NP * u, npages);
   };
-  // iteration w: phases 2w and 2w+1 (the copies of unit w + NS - 2 go into
-  // the slot that unit w - 2 left in phase 2w - 1).  Each half runs a loop of
-  // its own, so each loop body is straight-line code; both halves pass the
+  // iteration w: phases 2w and 2w+1.  The copies of group w + NS - 2 go into
+  // the slot that group w - 2 left in phase 2w - 1, and group w + 1 has
+  // landed before the barrier that ends phase 2w + 1.  Each half runs a loop
+  // of its own, so each loop body is straight-line code; both halves pass the
   // same number of barriers.  A wave without rows only keeps the barriers
   // (and its copies).
   if (half == 0) {
-    auto iteration = [&](int w, auto edge) {
-      if (copier) issue(w + NS - 2);
+    auto iteration = [&](int w, auto edge) __attribute__((always_inline)) {
       if (active) products(w, edge);
       block_barrier();
       if (active && w < nunits) softmax(w, edge);
-      wait_unit(w + 1);
       block_barrier();
     };
     int it = 0;
     for (; it < u_plain; ++it) iteration(it, std::false_type{});
     for (; it <= nunits; ++it) iteration(it, std::true_type{});
   } else {
-    auto iteration = [&](int w, auto edge) {
+    auto iteration = [&](int w, auto edge) __attribute__((always_inline)) {
+      if (copier) issue(w + NS - 2);
       if (active && w > 0) softmax(w - 1, edge);
       block_barrier();
       if (active) products(w, edge);
+      wait_unit(w + 1);
       block_barrier();
     };
     int it = 0;
