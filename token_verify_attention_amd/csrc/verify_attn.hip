@@ -2487,8 +2487,14 @@ void verify_attn_rows_kernel(AttnParams p) {
   sg.pa = 0;
   sg.full = true;
   sg.slot = 0;
-  const int r0 = (s_info[2] % nblk) * kRowBlock;
-  const int last_row = min(sg.R, r0 + kRowBlock) - 1;
+  // The pair's rows are spread evenly over its blocks (whole waves of 32):
+  // blocks that stream at one pace keep each page in L2 for the others (a
+  // half-empty last block ran ahead of its pair and the rest fetched its
+  // pages again: 1.8x the pages' bytes from memory).
+  const int rpb = ((sg.R + nblk - 1) / nblk + kMfmaRows - 1) / kMfmaRows * kMfmaRows;
+  const int r0 = (s_info[2] % nblk) * rpb;
+  const int r_end = min(sg.R, r0 + rpb);
+  const int last_row = r_end - 1;
   // keys up to the last row's position: pages 0 .. npages-1, in groups of NP
   constexpr int NP = L::NP;
   const int npages = min(si.np, (si.S + last_row / p.G) / kPage + 1);
@@ -2499,7 +2505,7 @@ void verify_attn_rows_kernel(AttnParams p) {
   const int wave = wave_id();
   const int half = wave / kRowHalf;
   const int rw = r0 + kMfmaRows * wave;            // this wave's first row
-  const bool active = rw < sg.R;                    // wave-uniform
+  const bool active = rw < r_end;                   // wave-uniform
   PhaseStep<KV, D, L::NU, !kTree> st(p, sg, rw);
   // the copies come from the second half, at the start of its softmax phase
   const int cw = wave - kRowHalf;
