@@ -479,7 +479,7 @@ __device__ __forceinline__ void unit_steps(const AttnParams& p, const Seg& sg, c
 // pair of consecutive pages (a = pa + 2u, u = wave, wave + NW, ...).
 template <typename KV, int D, int NW, class Step>
 __device__ __forceinline__ void run_pages(const AttnParams& p, const Seg& sg, char* ring,
-                                          Step& st) {
+                                          Step& st, bool issued = false) {
   using Gm = Geo<KV, D, NW>;
   constexpr int S = Gm::S, P2 = 2 * Gm::P;
   const int wave = wave_id();
@@ -488,7 +488,7 @@ __device__ __forceinline__ void run_pages(const AttnParams& p, const Seg& sg, ch
     int q[S];
 #pragma unroll
     for (int i = 0; i < S; ++i) q[i] = wave + NW * i < npair ? wave + NW * i : -1;
-    issue_first_steps<KV, D, NW>(p, sg, ring, wave, q);
+    if (!issued) issue_first_steps<KV, D, NW>(p, sg, ring, wave, q);
     st.ready();
     // units whose two pages lie inside the committed context (and inside the
     // segment) need no masks
@@ -1728,16 +1728,23 @@ struct PhaseStep : MfmaStep<KV, D, 2, kIdx> {
 // cross-workgroup merge of a pair split over several workgroups
 // ============================================================================
 
+// Floor quotients through one double division each (a 64-bit integer
+// division is a long dependent sequence, on the path to the first page copy):
+// with N < 2^31 and W <= 4096 the numerators stay below 2^43, exact in a
+// double, and a quotient that is not an integer lies at least 1/W (resp.
+// 1/N) from one while the rounding error stays below 2^-22, so truncating
+// the correctly rounded quotient gives the exact floor.
 __device__ __forceinline__ int64_t range_start(int w, int64_t N, int W) {
-  return int64_t(w) * N / W;
+  return int64_t(double(int64_t(w) * N) / double(W));
 }
 // the workgroup (logical index) whose range holds global page x
 __device__ __forceinline__ int wg_of(int64_t x, int64_t N, int W) {
-  return int(((x + 1) * W - 1) / N);
+  return int(double((x + 1) * W - 1) / double(N));
 }
-__device__ __forceinline__ int slot_of(int w, int64_t pair_begin, int64_t N, int W) {
-  const int64_t s = range_start(w, N, W);
-  return (max(s, pair_begin) == s) ? 2 * w : 2 * w + 1;
+// Partial slot of workgroup w (range start g0) in the pair starting at
+// pair_begin: its first slot when the pair starts inside its range.
+__device__ __forceinline__ int slot_of(int w, int64_t g0, int64_t pair_begin) {
+  return (max(g0, pair_begin) == g0) ? 2 * w : 2 * w + 1;
 }
 
 // Folds one partial state (m, l, o) into a running one (M, L, O).  Every merge
@@ -1794,7 +1801,8 @@ __device__ __forceinline__ void merge_pair(const AttnParams& p, const Seg& sg, i
       for (int h = 0; h < 2; ++h) {
         const int w = w0 + h;
         use[h] = w <= wl && range_start(w + 1, N, p.W) > range_start(w, N, p.W);   // non-empty
-        float* sb = slot_base<D>(p, slot_of(use[h] ? w : w0, pb, N, p.W));
+        const int wu = use[h] ? w : w0;
+        float* sb = slot_base<D>(p, slot_of(wu, range_start(wu, N, p.W), pb));
         const auto rs = slot_rsrc(sb, p.slot_rows * (D + 2) * 4);
 #pragma unroll
         for (int u = 0; u < kItems; ++u) {
@@ -1935,7 +1943,7 @@ __device__ __forceinline__ void merge_fused(const AttnParams& p, const Seg& sg, 
   // issued before its partials are folded in, so a batch costs one latency
   constexpr int kBatch = 3;
   const int self = logical_wg(p.W);
-  const int first_slot = slot_of(wf, pb, N, p.W);
+  const int first_slot = slot_of(wf, range_start(wf, N, p.W), pb);
   int w = ok ? wf : wl + 1;            // after a give-up nothing is read
   while (w <= wl) {
     int ws[kBatch];
@@ -1992,16 +2000,25 @@ __device__ __forceinline__ void merge_fused(const AttnParams& p, const Seg& sg, 
 // own pages are done, and one round spread over all threads merges them;
 // VALU steps merge pairwise through the idle ring and wave 0 writes the output
 // rows or the partial slot.
+// Bytes of a wave's LDS region in the split-step pass: its ring, then (the
+// same bytes) its final state.
+template <typename KV, int D, int NW, class St>
+__device__ __forceinline__ constexpr int wave_region() {
+  constexpr int GR = Geo<KV, D, NW>::RING;
+  constexpr int SB = St::SLOT_F * 4;
+  return GR > SB ? GR : SB;
+}
+
+// issued: the first steps' page copies of this pass are already in flight.
 template <typename KV, int D, int NW, class St>
 __device__ __forceinline__ void pass(const AttnParams& p, const Seg& sg, int r0, St& st,
-                                     char* ring_all) {
+                                     char* ring_all, bool issued = false) {
   const int wave = wave_id();
   constexpr int GR = Geo<KV, D, NW>::RING;
   if constexpr (St::kSplit) {
-    constexpr int SB = St::SLOT_F * 4;
-    constexpr int WR = GR > SB ? GR : SB;             // this wave's ring, then its state
+    constexpr int WR = wave_region<KV, D, NW, St>();  // this wave's ring, then its state
     char* mine = ring_all + wave * WR;
-    run_pages<KV, D, NW>(p, sg, mine, st);
+    run_pages<KV, D, NW>(p, sg, mine, st, issued);
     // a split pair's arrival is counted as soon as wave 0's pages are done, so
     // the counter's round trip overlaps the other waves' last pages
     int old = 0;
@@ -2059,13 +2076,29 @@ template <typename KV, int D, bool MF>
 __device__ __forceinline__ void process_segment(const AttnParams& p, const Seg& sg, char* ring,
                                                 uint32_t* qs, char* ps_all) {
   if constexpr (MF) {
+    // The first pass's first page copies go out before its step is set up
+    // (query loads, row masks): that set-up is on the path to the first data,
+    // and the prologue as a whole is on the kernel's (a 2 us wait at entry
+    // lengthened the 7B MHA kernel by 1.2-1.7 us).
+    constexpr int NW = AttnLds<KV, D, MF>::NW;
+    {
+      constexpr int S = Geo<KV, D, NW>::S;
+      const int wave = wave_id();
+      const int npair = (sg.pe - sg.pa + 1) >> 1;
+      int q[S];
+#pragma unroll
+      for (int i = 0; i < S; ++i) q[i] = wave + NW * i < npair ? wave + NW * i : -1;
+      char* mine = ring + wave * (sg.R > 16 ? wave_region<KV, D, NW, MfmaStep<KV, D, 2>>()
+                                            : wave_region<KV, D, NW, MfmaStep<KV, D, 1>>());
+      issue_first_steps<KV, D, NW>(p, sg, mine, wave, q);
+    }
     for (int r0 = 0; r0 < sg.R; r0 += kMfmaRows) {
       if (sg.R - r0 > 16) {
         MfmaStep<KV, D, 2> st(p, sg, r0);
-        pass<KV, D, AttnLds<KV, D, MF>::NW>(p, sg, r0, st, ring);
+        pass<KV, D, NW>(p, sg, r0, st, ring, r0 == 0);
       } else {
         MfmaStep<KV, D, 1> st(p, sg, r0);
-        pass<KV, D, AttnLds<KV, D, MF>::NW>(p, sg, r0, st, ring);
+        pass<KV, D, NW>(p, sg, r0, st, ring, r0 == 0);
       }
     }
     return;
@@ -2290,7 +2323,7 @@ __global__ __launch_bounds__((AttnLds<KV, D, MF>::NT), 1) void verify_attn_kerne
     sg.np = si.np;
     sg.R = si.k * p.G;
     sg.full = pp.pa == 0 && pp.pe == si.np;
-    sg.slot = slot_of(w, pb, N, p.W);
+    sg.slot = slot_of(w, g0, pb);
     sg.fuse = MF && !sg.full && sg.R <= kMfmaRows;
     if (sg.fuse && tid == 0) {          // read after the barriers of the pass
       pair_info()[0] = pb;
