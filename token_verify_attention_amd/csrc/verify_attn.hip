@@ -2368,8 +2368,9 @@ __global__ __launch_bounds__((AttnLds<KV, D, MF>::NT), 1) void verify_attn_kerne
 // of drafts -- in one pass ("HeteroReason": the PRM verifies a complete step
 // in a single parallel pass).  With k*G query rows per (sequence, kv head) far
 // above 32, splitting the keys over waves (the kernel above) would re-stream
-// the pages once per 32 rows.  Here a workgroup owns a block of 256 query rows
-// of one pair, each of its 8 waves 32 of them, and all eight share every
+// the pages once per 32 rows.  Here a workgroup owns a block of up to 256
+// query rows of one pair (a pair's rows spread evenly over its blocks, in
+// whole waves), each of its 8 waves 32 of them, and all eight share every
 // page.  A group is NU units of two pages (bf16: 2, INT8: 1, whose operands
 // take more registers); groups stream through a workgroup ring of 4 to 8
 // slots, copied by 2 NU waves of the second half (one page each, at the start
