@@ -3,9 +3,9 @@ the C ABI): tens to hundreds of drafts per sequence, as when a process reward
 model scores a whole reasoning step in one pass ("HeteroReason").  These
 shapes run on the row-block kernel (256 query rows per workgroup, pages shared
 by its eight waves).  Small cases cover k from 17 to 300, GQA groups 1 to 7,
-bf16 and INT8 caches, d = 64 / 128, S = 0 and ragged mixes; a tree mask with
-more than 128 rows per pair takes the same kernel; the full prm7b_step
-workload is checked on sampled pairs.
+bf16 and INT8 caches, d = 64 / 128, S = 0 and ragged mixes; tree masks with
+more than 128 rows per pair take the same kernel (every cache type and d);
+the full prm7b_step workload is checked on sampled pairs.
 """
 import math
 
@@ -80,6 +80,50 @@ def test_tree_mask_on_row_block_kernel():
                                   np_(case["block_table"]), np_(case["ctx_lens"]),
                                   np_(case["cu_q"]), 1.0 / math.sqrt(w.d), draft_mask=om)
     assert_close(out, ref, "bf16")
+
+
+# The row-block kernel's remaining instantiations (cache type x d x mask form)
+# beyond the cases above: INT8 at d = 64 (causal), and tree masks on INT8 and
+# d = 64 caches (16 nodes x G = 16: 256 rows per pair).
+ROW_VARIANTS = [
+    (_wk("rows-int8-d64", 16, 4, 64, "int8", "bf16", 0.5, ident=119), [300, 5], [40, 70], False),
+    (_wk("rows-int8-tree", 64, 4, 128, "int8", "bf16", 0.5, ident=120), [70, 0, 300], [16, 9, 16],
+     True),
+    (_wk("rows-d64-tree", 64, 4, 64, "bf16", "bf16", ident=121), [70, 3, 300], [16, 12, 16], True),
+    (_wk("rows-int8-d64-tree", 64, 4, 64, "int8", "bf16", 0.5, ident=122), [33, 0, 200],
+     [16, 16, 5], True),
+]
+
+
+@pytest.mark.parametrize("spec", ROW_VARIANTS, ids=[s[0].name for s in ROW_VARIANTS])
+def test_row_block_kernel_variants(spec):
+    w, ctx, ks, tree = spec
+    say(f"row-block variant {w.name}")
+    case = wl.make_case(w, device=DEV, ctx=ctx, k=ks, with_logits=False)
+    batch = batch_of(case)
+    kv = paged_kv(case)
+    assert tva.verify_workspace_bytes(batch, kv, w.Hq) == tva.STATUS_OFFSET + 256   # row blocks
+    om = None
+    if tree:
+        parents = wl.make_tree(ks, device=DEV, seed=w.ident)
+        out = tva.spec_verify_attn(batch, case["q"], kv, draft_mask=tva.tree_masks(batch, parents))
+        om = oracle.ancestor_masks(np_(parents), np_(case["cu_q"]))
+    else:
+        out = tva.spec_verify_attn(batch, case["q"], kv)
+    torch.cuda.synchronize()
+    qn, kp, vp = np_(case["q"]), np_(case["k_pool"]), np_(case["v_pool"])
+    args = (np_(case["block_table"]), np_(case["ctx_lens"]), np_(case["cu_q"]), 1.0 / math.sqrt(w.d))
+    if w.kv_dtype == "int8":
+        P, H = kp.shape[:2]
+        kc, ksc = oracle.kv_quant_int8(kp.reshape(-1, w.d))
+        vc, vsc = oracle.kv_quant_int8(vp.reshape(-1, w.d))
+        ref_q = oracle.spec_verify_attn(qn, kc.reshape(kp.shape), vc.reshape(vp.shape), *args,
+                                        k_scale=ksc.reshape(P, H, 16), v_scale=vsc.reshape(P, H, 16),
+                                        draft_mask=om)
+        assert_close(out, ref_q, "int8_deq")
+        assert_close(out, oracle.spec_verify_attn(qn, kp, vp, *args, draft_mask=om), "int8")
+    else:
+        assert_close(out, oracle.spec_verify_attn(qn, kp, vp, *args, draft_mask=om), "bf16")
 
 
 def test_row_block_kernel_equals_split_kernel_on_short_steps():
