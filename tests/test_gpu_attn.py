@@ -37,6 +37,7 @@ SMALL = [
     (_wk("gqa2-bf16-d64", 8, 4, 64, "bf16", "bf16", ident=55), [70, 1, 31], [7, 8, 2]),
     (_wk("gqa4-int8-d64", 16, 4, 64, "int8", "f32", 0.5, ident=56), [90, 16, 47], [5, 4, 8]),
     (_wk("rows128-bf16", 16, 2, 128, "bf16", "bf16", ident=57), [50, 3], [16, 16]),
+    (_wk("gqa2-f32-d128", 8, 4, 128, "f32", "bf16", ident=65), [0, 300, 17, 64], [3, 4, 8, 1]),
 ]
 
 
@@ -57,7 +58,10 @@ def _check(case, out, kind_dtype=None):
         assert_close(out, ref_q, "int8_deq")
         return assert_close(out, ref_u, "int8")
     ref = oracle_attn(case)
-    return assert_close(out, ref, "f32" if kind == "f32" else "bf16")
+    # the fp32 bound needs an fp32 cache and an fp32 output: a bf16 output
+    # rounds each value to 8 significant bits whatever the cache holds
+    tight = kind == "f32" and out.dtype == torch.float32
+    return assert_close(out, ref, "f32" if tight else "bf16")
 
 
 @pytest.mark.parametrize("path", [0, 1, 2], ids=["auto", "valu", "mfma"])
@@ -87,6 +91,20 @@ def test_fp32_output_from_bf16_cache():
     w = _wk("f32out", 16, 4, 128, "bf16", "bf16", ident=59)
     case = _case(w, [300, 45], [4, 6])
     out = tva.spec_verify_attn(batch_of(case), case["q"], paged_kv(case), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert out.dtype == torch.float32
+    _check(case, out)
+
+
+@pytest.mark.parametrize("path", [0, 1], ids=["auto", "valu"])
+def test_fp32_cache_d128_fp32_output(path):
+    """An fp32 cache at d = 128 read with bf16 queries, written as fp32: held
+    to the fp32 bound, on pairs that span several pages and a ragged tail."""
+    w = _wk("f32out-d128", 8, 4, 128, "f32", "bf16", ident=66)
+    case = _case(w, [0, 300, 17, 64, 511], [3, 4, 8, 1, 6])
+    say(f"attn f32 cache d128 f32 out path={path}")
+    out = tva.spec_verify_attn(batch_of(case), case["q"], paged_kv(case),
+                               out_dtype=torch.float32, path=path)
     torch.cuda.synchronize()
     assert out.dtype == torch.float32
     _check(case, out)
