@@ -83,8 +83,11 @@ def test_tree_mask_on_row_block_kernel():
 
 
 # The row-block kernel's remaining instantiations (cache type x d x mask form)
-# beyond the cases above: INT8 at d = 64 (causal), and tree masks on INT8 and
-# d = 64 caches (16 nodes x G = 16: 256 rows per pair).
+# beyond the cases above: INT8 at d = 64 (causal), tree masks on INT8 and
+# d = 64 caches (16 nodes x G = 16: 256 rows per pair), and both ways a block
+# copies its pages: 256-row blocks (every wave holds rows: one page per
+# second-half wave) and 224-row blocks (the last wave holds none and copies
+# every page), on bf16 and INT8 caches with many committed groups.
 ROW_VARIANTS = [
     (_wk("rows-int8-d64", 16, 4, 64, "int8", "bf16", 0.5, ident=119), [300, 5], [40, 70], False),
     (_wk("rows-int8-tree", 64, 4, 128, "int8", "bf16", 0.5, ident=120), [70, 0, 300], [16, 9, 16],
@@ -92,6 +95,12 @@ ROW_VARIANTS = [
     (_wk("rows-d64-tree", 64, 4, 64, "bf16", "bf16", ident=121), [70, 3, 300], [16, 12, 16], True),
     (_wk("rows-int8-d64-tree", 64, 4, 64, "int8", "bf16", 0.5, ident=122), [33, 0, 200],
      [16, 16, 5], True),
+    (_wk("copy-bf16-256rows", 16, 4, 128, "bf16", "bf16", ident=123), [300, 170], [64, 64], False),
+    (_wk("copy-bf16-224rows", 16, 4, 128, "bf16", "bf16", ident=124), [300, 170], [56, 56], False),
+    (_wk("copy-int8-256rows", 16, 4, 128, "int8", "bf16", 0.5, ident=125), [300, 170], [64, 64],
+     False),
+    (_wk("copy-int8-224rows", 16, 4, 128, "int8", "bf16", 0.5, ident=126), [300, 170], [56, 56],
+     False),
 ]
 
 
