@@ -439,9 +439,13 @@ sva_status sva_kv_alloc_pages(const sva_batch *batch, int32_t *block_table,
  *                   read once with non-temporal 16-byte loads
  *   mode            0: into registers (8 loads in flight per thread);
  *                   1: through global -> LDS copies, the verification kernel's
- *                   path (up to 32 KB in flight per wave)
+ *                   path (up to 32 KB in flight per wave);
+ *                   2: as 1 over 4 KB pages in a scattered order, the access
+ *                   pattern of a paged cache (`bytes` must be 4096 times a
+ *                   power of two; position j reads page j * c mod n for a
+ *                   fixed odd c)
  *   num_workgroups  1 .. 65536 workgroups of 256 threads, each reading one
- *                   contiguous range
+ *                   contiguous range (mode 2: of the page order)
  *   sink            device [num_workgroups * 4] uint32 (written: one word per
  *                   wave, so no load is dead) */
 sva_status sva_stream_read_probe(const void *buf, size_t bytes, int32_t mode,

@@ -78,6 +78,17 @@ def test_host_checked_errors_need_no_gpu():
     assert lib.sva_kvmu_apply(0, None, 1, None, None, None, None) == 0
 
 
+def test_stream_read_probe_argument_checks():
+    tva, lib = _lib()
+    vp = ctypes.c_void_p
+    assert lib.sva_stream_read_probe(vp(1024), 4096, 3, 256, vp(16), None) == 1      # mode
+    assert lib.sva_stream_read_probe(vp(1024), 3 * 4096, 2, 256, vp(16), None) == 1  # 3 pages
+    assert b"power of two" in lib.sva_last_error()
+    assert lib.sva_stream_read_probe(vp(1024), 1000, 1, 256, vp(16), None) == 1      # not 1 KB
+    assert lib.sva_stream_read_probe(vp(1024), 4096, 0, 0, vp(16), None) == 1        # grid
+    assert lib.sva_stream_read_probe(None, 0, 2, 256, None, None) == 0               # no bytes
+
+
 def test_batch_and_cache_shape_checks():
     tva, lib = _lib()
     b = tva._Batch(2, 16, 32, 8, 4, 100)

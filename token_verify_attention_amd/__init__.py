@@ -792,7 +792,8 @@ def kv_alloc_pages(batch, block_table, free_list, free_count, stream=None):
 def stream_read_probe(buf, mode=0, num_workgroups=2048, sink=None, stream=None):
     """Read the device buffer `buf` once (its byte size a multiple of 1024)
     with the library's streaming-read probe kernel (mode 0: into registers,
-    1: through global -> LDS copies).  Returns the sink words."""
+    1: through global -> LDS copies, 2: as 1 over 4 KB pages in a scattered
+    order, the byte size 4096 times a power of two).  Returns the sink words."""
     lib = load()
     _need(buf, "buf")
     nbytes = buf.numel() * buf.element_size()

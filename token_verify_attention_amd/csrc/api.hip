@@ -530,7 +530,10 @@ sva_status sva_kv_alloc_pages(const sva_batch* batch, int32_t* block_table,
 sva_status sva_stream_read_probe(const void* buf, size_t bytes, int32_t mode,
                                  int32_t num_workgroups, uint32_t* sink, void* stream) {
   g_last_error.clear();
-  if (mode != 0 && mode != 1) return fail(SVA_ERR_INVALID_ARG, "mode = %d (0 or 1)", mode);
+  if (mode < 0 || mode > 2) return fail(SVA_ERR_INVALID_ARG, "mode = %d (0, 1 or 2)", mode);
+  if (mode == 2 && (bytes % 4096 != 0 || ((bytes / 4096) & (bytes / 4096 - 1)) != 0))
+    return fail(SVA_ERR_INVALID_ARG, "mode 2: bytes = %zu is not 4096 times a power of two",
+                bytes);
   if (num_workgroups < 1 || num_workgroups > 65536)
     return fail(SVA_ERR_INVALID_ARG, "num_workgroups = %d (1 .. 65536)", num_workgroups);
   if (bytes % 1024 != 0) return fail(SVA_ERR_INVALID_ARG, "bytes = %zu is not a multiple of 1024", bytes);
