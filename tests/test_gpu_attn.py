@@ -2,8 +2,9 @@
 
 Small cases span several pages, ragged tails (S = 0, 1, 15, 16, 17, ...), k = 1..16,
 GQA groups 1..8, d = 64 / 128, fp32 / bf16 / INT8 caches and both inner paths,
-and grid sizes that force pairs to be split over workgroups (the cross-workgroup
-merge).  Full-size workloads are checked on every (sequence, kv-head) pair, through
+grid sizes that force pairs to be split over workgroups (the cross-workgroup
+merge), and batches with few enough (sequence, kv head) pairs that each kv
+head's query heads are split over two workgroups as well as batches with more.  Full-size workloads are checked on every (sequence, kv-head) pair, through
 the call and launch configuration the benchmark times.
 """
 import math
@@ -38,6 +39,12 @@ SMALL = [
     (_wk("gqa4-int8-d64", 16, 4, 64, "int8", "f32", 0.5, ident=56), [90, 16, 47], [5, 4, 8]),
     (_wk("rows128-bf16", 16, 2, 128, "bf16", "bf16", ident=57), [50, 3], [16, 16]),
     (_wk("gqa2-f32-d128", 8, 4, 128, "f32", "bf16", ident=65), [0, 300, 17, 64], [3, 4, 8, 1]),
+    # 36 (sequence, kv head) pairs, above the 32 whose query heads the planner
+    # splits in two on a 256-CU part: the unsplit pairs at small sizes
+    (_wk("gqa4-36pairs-bf16", 16, 4, 128, "bf16", "bf16", ident=88),
+     [0, 1, 15, 16, 17, 100, 300, 64, 31], [4, 1, 3, 4, 2, 8, 4, 5, 1]),
+    (_wk("gqa4-36pairs-int8", 16, 4, 128, "int8", "bf16", 0.5, ident=89),
+     [5, 40, 200, 17, 0, 96, 33, 300, 63], [2, 4, 1, 8, 3, 4, 6, 2, 4]),
 ]
 
 
@@ -307,14 +314,24 @@ def test_long_context_few_pairs_many_segments(kvd, nwg):
     _check(case, outs[0])
 
 
-def test_wait_that_gives_up_writes_nan_and_leaves_the_workspace_reusable():
+# G = 4 with 16 (sequence, kv head) pairs: few enough pairs that each kv
+# head's query heads are split into two halves streamed (and merged) apart,
+# so the unit that gives up is half a pair.  G = 3 cannot be halved: the unit
+# is the whole pair.
+GIVE_UP = [(_wk("giveup", 16, 4, 128, "bf16", "bf16", ident=71), 2),
+           (_wk("giveup-g3", 12, 4, 128, "bf16", "bf16", ident=87), 1)]
+
+
+@pytest.mark.parametrize("spec", GIVE_UP, ids=[s[0].name for s in GIVE_UP])
+def test_wait_that_gives_up_writes_nan_and_leaves_the_workspace_reusable(spec):
     """Forced from the host: with no poll allowed, the workgroup that finishes
     each split pair gives up at once instead of waiting for the others'
-    partials.  Its pair's rows must come out NaN (never a fold of partials
-    that may be missing), the status word must say so, and once every
-    workgroup is done the counters must be back at zero, so the same
-    workspace then serves an ordinary call.  Every kernel exits normally."""
-    w = _wk("giveup", 16, 4, 128, "bf16", "bf16", ident=71)
+    partials.  Its rows must come out NaN (never a fold of partials that may
+    be missing) for every query head of the unit that gave up, the status
+    word must say so, and once every workgroup is done the counters must be
+    back at zero, so the same workspace then serves an ordinary call.  Every
+    kernel exits normally."""
+    w, parts = spec
     case = _case(w, [3000, 40, 1200, 700], [4, 2, 3, 4])
     batch = batch_of(case)
     kv = paged_kv(case)
@@ -329,18 +346,18 @@ def test_wait_that_gives_up_writes_nan_and_leaves_the_workspace_reusable():
     assert tva.verify_status(ws) == 0
     ref = oracle_attn(case)
     got = np_(bad).astype(np.float64)
-    G = w.Hq // w.Hkv
+    U = w.Hq // w.Hkv // parts                     # query heads per unit
     cu = np_(case["cu_q"])
-    nan_pairs = 0
+    nan_units = 0
     for b in range(case["B"]):
-        for g in range(w.Hkv):
-            blk = got[cu[b]:cu[b + 1], g * G:(g + 1) * G]
+        for u in range(w.Hkv * parts):
+            blk = got[cu[b]:cu[b + 1], u * U:(u + 1) * U]
             if np.isnan(blk).any():
-                assert np.isnan(blk).all(), (b, g)              # the whole pair, never a part
-                nan_pairs += 1
+                assert np.isnan(blk).all(), (b, u)              # the whole unit, never a part
+                nan_units += 1
             else:
-                assert_close(blk, ref[cu[b]:cu[b + 1], g * G:(g + 1) * G], "bf16")
-    assert nan_pairs > 0
+                assert_close(blk, ref[cu[b]:cu[b + 1], u * U:(u + 1) * U], "bf16")
+    assert nan_units > 0
     good = tva.spec_verify_attn(batch, case["q"], kv, workspace=ws, num_workgroups=24)
     torch.cuda.synchronize()
     assert tva.verify_status(ws) == 0

@@ -99,6 +99,10 @@ struct AttnParams {
   int slot_rows;        // rows per partial slot (max_q * G)
   int W;                // grid size
   int seg_cost;         // fixed cost of a segment, in pages (work split)
+  // Pairs are (sequence, g) with kv head g >> kv_shift: with kv_shift = 1 the
+  // G query heads of a kv head form two pairs of G/2 (Hkv and G above count
+  // those pairs), streamed by different workgroups.
+  int kv_shift;
 };
 
 struct SeqInfo {
@@ -359,7 +363,7 @@ template <typename KV, int D, bool kNT = true>
 __device__ __forceinline__ void dma_page(const AttnParams& p, int pid, int g, char* slot) {
   using Gm = Geo<KV, D, kWavesValu>;      // page geometry only
   const int lane = lane_id();
-  const int64_t off = (int64_t(pid) * p.Hkv + g) * Gm::PAGE;
+  const int64_t off = (int64_t(pid) * (p.Hkv >> p.kv_shift) + (g >> p.kv_shift)) * Gm::PAGE;
   const char* kb = static_cast<const char*>(p.k) + off;
   const char* vb = static_cast<const char*>(p.v) + off;
 #pragma unroll
@@ -373,7 +377,7 @@ __device__ __forceinline__ void dma_page(const AttnParams& p, int pid, int g, ch
   if constexpr (Gm::ES == 1) {
     // one copy for both scale rows: lanes 0-7 the 16 K scales, lanes 8-15
     // the 16 V scales, landing side by side
-    const int64_t so = (int64_t(pid) * p.Hkv + g) * kPage;
+    const int64_t so = (int64_t(pid) * (p.Hkv >> p.kv_shift) + (g >> p.kv_shift)) * kPage;
     if (lane < 16)
       dma4<kNT>((lane < 8 ? p.k_scale : p.v_scale) + so + 2 * (lane & 7), slot + 2 * Gm::PAGE);
   }
@@ -2197,6 +2201,8 @@ __device__ __forceinline__ bool append_wave_rows(const AttnParams& p, int64_t g0
       const int page = p.block_table[int64_t(b) * p.max_pages + lp];
       if (page < 0 || page >= p.num_pages) continue;
       if (first && u / NW < S_RING) early = true;
+      // (kv_shift is 0 here: a call whose pairs split the query heads appends
+      // in a launch of its own, so that no row is written by two workgroups)
       const int64_t src_row = int64_t(si.q0 + (pos - si.S)) * p.Hkv + g;
       const int64_t dst_row = (int64_t(page) * p.Hkv + g) * kPage + (pos % kPage);
 #pragma unroll
@@ -2695,9 +2701,22 @@ AttnPlan plan_verify_attn(const sva_batch* batch, const sva_paged_kv* kv, int Hq
                                (rows > kMfmaRows && blocks_ub >= num_cus));
   // a multiple of 8 (the kernel spreads its blocks evenly over the 8 XCDs)
   pl.rows_grid = int(std::min<int64_t>((blocks_ub + 7) / 8 * 8, 0x7ffffff8));
+  // Few pairs (at most one per 8 CUs): each pair's G query heads are split
+  // into two pairs of G/2, streamed by different workgroups of one XCD that
+  // read the same pages at about the same time (the second read mostly hits
+  // L2).  Every pair is then cut into half as many segments for the same
+  // grid, and each merge folds partials of half as many rows.  One GPU's
+  // TP-8 share of the 70B INT8 shape (16 pairs): 27.1 -> 21.0 us, HBM traffic
+  // 1.12x the KV bytes.  With one pair per 2 CUs (the whole 70B INT8 shape)
+  // the second reads missed L2 (1.36x the KV bytes) and the call was slower.
+  pl.kv_split = !pl.rows_kernel && mfma_ok && G % 2 == 0 &&
+                        int64_t(batch->B) * kv->Hkv * 8 <= num_cus
+                    ? 2
+                    : 1;
+  const int64_t npairs = int64_t(batch->B) * kv->Hkv * pl.kv_split;
   const int64_t pages_per_seq =
       std::min<int64_t>(kv->max_pages_per_seq, (int64_t(batch->max_len) + kPage - 1) / kPage);
-  const int64_t pages_ub = int64_t(batch->B) * kv->Hkv * std::max<int64_t>(pages_per_seq, 1);
+  const int64_t pages_ub = npairs * std::max<int64_t>(pages_per_seq, 1);
   int W = 0;
   if (opts && opts->num_workgroups > 0) {
     W = std::min(opts->num_workgroups, kMaxWorkgroups);
@@ -2707,12 +2726,11 @@ AttnPlan plan_verify_attn(const sva_batch* batch, const sva_paged_kv* kv, int Hq
     // of its pages but adds a partial to its merge, which one workgroup reads
     // after the others finish; a partial costs about as much as streaming 8
     // pages, so the time is lowest near sqrt(pages per pair / 8) segments.
-    const int64_t pairs = int64_t(batch->B) * kv->Hkv;
     const int64_t seg_cap =
         std::max<int64_t>(2, int64_t(std::sqrt(double(std::max<int64_t>(pages_per_seq, 1)) / 8.0) + 0.5));
     W = int(std::min<int64_t>(std::min<int64_t>(std::min(std::max(num_cus, 1), kMaxWorkgroups),
                                                 std::max<int64_t>(want, 1)),
-                              pairs * seg_cap));
+                              npairs * seg_cap));
   }
   pl.num_wg = W;
   // fixed cost of a segment in pages: about kSegCostBytes of streaming
@@ -2720,7 +2738,7 @@ AttnPlan plan_verify_attn(const sva_batch* batch, const sva_paged_kv* kv, int Hq
                          (kv->kv_dtype == SVA_INT8 ? 4 * kPage : 0);
   pl.seg_cost = int((kSegCostBytes + page_bytes / 2) / page_bytes);
   pl.wait_polls = !opts || opts->wait_polls == 0 ? kSpinLimit : std::max(opts->wait_polls, 0);
-  pl.slot_rows = std::max(batch->max_q, 1) * G;
+  pl.slot_rows = std::max(batch->max_q, 1) * (G / pl.kv_split);
   // arrival and publication counters, then the status word (256 bytes keep
   // the partial slots aligned)
   pl.counter_bytes = size_t(2 * kMaxWorkgroups) * 4 + 256;
@@ -2789,8 +2807,9 @@ hipError_t launch_verify_attn(const sva_batch* batch, const void* q, int q_dtype
   p.B = batch->B;
   p.T = batch->total_q;
   p.Hq = Hq;
-  p.Hkv = kv->Hkv;
-  p.G = Hq / kv->Hkv;
+  p.Hkv = kv->Hkv * plan.kv_split;
+  p.G = Hq / kv->Hkv / plan.kv_split;
+  p.kv_shift = plan.kv_split == 2 ? 1 : 0;
   p.num_pages = kv->num_pages;
   p.max_pages = kv->max_pages_per_seq;
   p.max_q = batch->max_q;
@@ -2811,6 +2830,11 @@ hipError_t launch_verify_attn(const sva_batch* batch, const void* q, int q_dtype
                          : attn_rows_launch<uint16_t, 128>(p, plan.rows_grid, st);
     return kv->d == 64 ? attn_rows_launch<int8_t, 64>(p, plan.rows_grid, st)
                        : attn_rows_launch<int8_t, 128>(p, plan.rows_grid, st);
+  }
+  if (k_new && plan.kv_split > 1) {     // both halves of a pair read its new rows
+    const hipError_t e = launch_kv_append(batch, k_new, v_new, src_dtype, kv, st);
+    if (e != hipSuccess) return e;
+    p.k_new = p.v_new = nullptr;
   }
   if (kv->kv_dtype == SVA_F32)
     return kv->d == 64 ? attn_launch<float, 64>(p, false, st) : attn_launch<float, 128>(p, false, st);
