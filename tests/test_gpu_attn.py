@@ -3,8 +3,8 @@
 Small cases span several pages, ragged tails (S = 0, 1, 15, 16, 17, ...), k = 1..16,
 GQA groups 1..8, d = 64 / 128, fp32 / bf16 / INT8 caches and both inner paths,
 grid sizes that force pairs to be split over workgroups (the cross-workgroup
-merge), and batches with few enough (sequence, kv head) pairs that each kv
-head's query heads are split over two workgroups as well as batches with more.  Full-size workloads are checked on every (sequence, kv-head) pair, through
+merge), and pairs whose kv head's query heads are split over workgroups (to
+fit one 32-row pass, or because the pairs are few) as well as unsplit ones.  Full-size workloads are checked on every (sequence, kv-head) pair, through
 the call and launch configuration the benchmark times.
 """
 import math
@@ -39,12 +39,15 @@ SMALL = [
     (_wk("gqa4-int8-d64", 16, 4, 64, "int8", "f32", 0.5, ident=56), [90, 16, 47], [5, 4, 8]),
     (_wk("rows128-bf16", 16, 2, 128, "bf16", "bf16", ident=57), [50, 3], [16, 16]),
     (_wk("gqa2-f32-d128", 8, 4, 128, "f32", "bf16", ident=65), [0, 300, 17, 64], [3, 4, 8, 1]),
-    # 36 (sequence, kv head) pairs, above the 32 whose query heads the planner
-    # splits in two on a 256-CU part: the unsplit pairs at small sizes
+    # 36 (sequence, kv head) pairs of 32 query rows, more pairs than the
+    # planner splits into query-head halves on a 256-CU part: unsplit pairs
+    # at small sizes; and 36 pairs of 64 rows, split in two to fit one pass
     (_wk("gqa4-36pairs-bf16", 16, 4, 128, "bf16", "bf16", ident=88),
      [0, 1, 15, 16, 17, 100, 300, 64, 31], [4, 1, 3, 4, 2, 8, 4, 5, 1]),
     (_wk("gqa4-36pairs-int8", 16, 4, 128, "int8", "bf16", 0.5, ident=89),
      [5, 40, 200, 17, 0, 96, 33, 300, 63], [2, 4, 1, 8, 3, 4, 6, 2, 4]),
+    (_wk("gqa8-36pairs-64rows", 32, 4, 128, "bf16", "bf16", ident=85),
+     [9, 70, 0, 33, 130, 16, 250, 47, 5], [8, 3, 5, 8, 1, 6, 8, 2, 7]),
 ]
 
 
@@ -314,11 +317,11 @@ def test_long_context_few_pairs_many_segments(kvd, nwg):
     _check(case, outs[0])
 
 
-# G = 4 with 16 (sequence, kv head) pairs: few enough pairs that each kv
-# head's query heads are split into two halves streamed (and merged) apart,
-# so the unit that gives up is half a pair.  G = 3 cannot be halved: the unit
-# is the whole pair.
-GIVE_UP = [(_wk("giveup", 16, 4, 128, "bf16", "bf16", ident=71), 2),
+# G = 8, up to 4 drafts (32 query rows per pair) and 16 (sequence, kv head)
+# pairs: few enough pairs that each kv head's query heads are split into two
+# halves streamed (and merged) apart, so the unit that gives up is half a
+# pair.  G = 3 cannot be halved: the unit is the whole pair.
+GIVE_UP = [(_wk("giveup", 32, 4, 128, "bf16", "bf16", ident=71), 2),
            (_wk("giveup-g3", 12, 4, 128, "bf16", "bf16", ident=87), 1)]
 
 

@@ -26,7 +26,7 @@ struct AttnPlan {
   int wait_polls;       // bound on a split pair's wait for the others' partials
   int seg_cost;         // fixed cost of a segment, in pages, for the work split
   int slot_rows;
-  int kv_split;         // 2: each kv head's query heads form two pairs (few pairs)
+  int kv_split;         // pairs per kv head (its query heads split over workgroups)
   size_t counter_bytes;
   size_t slot_bytes;
   size_t total_bytes;

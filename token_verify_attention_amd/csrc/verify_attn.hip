@@ -99,9 +99,9 @@ struct AttnParams {
   int slot_rows;        // rows per partial slot (max_q * G)
   int W;                // grid size
   int seg_cost;         // fixed cost of a segment, in pages (work split)
-  // Pairs are (sequence, g) with kv head g >> kv_shift: with kv_shift = 1 the
-  // G query heads of a kv head form two pairs of G/2 (Hkv and G above count
-  // those pairs), streamed by different workgroups.
+  // Pairs are (sequence, g) with kv head g >> kv_shift: the G query heads of
+  // a kv head form 2^kv_shift pairs (Hkv and G above count those pairs),
+  // streamed by different workgroups.
   int kv_shift;
 };
 
@@ -2701,18 +2701,28 @@ AttnPlan plan_verify_attn(const sva_batch* batch, const sva_paged_kv* kv, int Hq
                                (rows > kMfmaRows && blocks_ub >= num_cus));
   // a multiple of 8 (the kernel spreads its blocks evenly over the 8 XCDs)
   pl.rows_grid = int(std::min<int64_t>((blocks_ub + 7) / 8 * 8, 0x7ffffff8));
-  // Few pairs (at most one per 8 CUs): each pair's G query heads are split
-  // into two pairs of G/2, streamed by different workgroups of one XCD that
-  // read the same pages at about the same time (the second read mostly hits
-  // L2).  Every pair is then cut into half as many segments for the same
-  // grid, and each merge folds partials of half as many rows.  One GPU's
-  // TP-8 share of the 70B INT8 shape (16 pairs): 27.1 -> 21.0 us, HBM traffic
-  // 1.12x the KV bytes.  With one pair per 2 CUs (the whole 70B INT8 shape)
-  // the second reads missed L2 (1.36x the KV bytes) and the call was slower.
-  pl.kv_split = !pl.rows_kernel && mfma_ok && G % 2 == 0 &&
-                        int64_t(batch->B) * kv->Hkv * 8 <= num_cus
-                    ? 2
-                    : 1;
+  // Query heads split over workgroups: a kv head's G query heads form
+  // kv_split pairs of G / kv_split, streamed by neighbouring workgroups of
+  // one XCD that read the same pages at about the same time (the later read
+  // mostly hits L2).  First until a pair's rows fit one 32-row pass: a pair
+  // with more rows is otherwise streamed once per pass (8B-shaped GQA, G = 8,
+  // k = 8, 64 pairs: 63.5 -> 40.3 us; 128 pairs: 100.6 -> 61.8 us; k = 16,
+  // G = 8, 16 pairs: 134.6 -> 81.2 us).  Then once more for few pairs (at
+  // most one per 8 CUs) of 32 rows: every pair is cut into half as many
+  // segments for the same grid and each merge folds half as many rows (one
+  // GPU's TP-8 share of the 70B INT8 shape: 27.1 -> 21.0 us; 4 sequences of
+  // 8192 tokens, G = 8, k = 4: bf16 39.4 -> 36.0 us, INT8 30.0 -> 25.8 us).
+  // Not for pairs of 16 rows or fewer (half an MFMA block per part: 4 x 8192
+  // tokens, G = 4, k = 4 took 32.7 -> 35 us), nor for many pairs of 32 rows
+  // (the whole 70B INT8 shape: the later reads missed L2, 1.36x the KV bytes,
+  // and the call was slower).
+  pl.kv_split = 1;
+  if (!pl.rows_kernel && mfma_ok) {
+    while (rows / pl.kv_split > kMfmaRows && G % (2 * pl.kv_split) == 0) pl.kv_split *= 2;
+    if (rows / pl.kv_split >= kMfmaRows && G % (2 * pl.kv_split) == 0 &&
+        int64_t(batch->B) * kv->Hkv * pl.kv_split * 8 <= num_cus)
+      pl.kv_split *= 2;
+  }
   const int64_t npairs = int64_t(batch->B) * kv->Hkv * pl.kv_split;
   const int64_t pages_per_seq =
       std::min<int64_t>(kv->max_pages_per_seq, (int64_t(batch->max_len) + kPage - 1) / kPage);
@@ -2809,7 +2819,7 @@ hipError_t launch_verify_attn(const sva_batch* batch, const void* q, int q_dtype
   p.Hq = Hq;
   p.Hkv = kv->Hkv * plan.kv_split;
   p.G = Hq / kv->Hkv / plan.kv_split;
-  p.kv_shift = plan.kv_split == 2 ? 1 : 0;
+  p.kv_shift = __builtin_ctz(unsigned(plan.kv_split));
   p.num_pages = kv->num_pages;
   p.max_pages = kv->max_pages_per_seq;
   p.max_q = batch->max_q;
@@ -2831,7 +2841,7 @@ hipError_t launch_verify_attn(const sva_batch* batch, const void* q, int q_dtype
     return kv->d == 64 ? attn_rows_launch<int8_t, 64>(p, plan.rows_grid, st)
                        : attn_rows_launch<int8_t, 128>(p, plan.rows_grid, st);
   }
-  if (k_new && plan.kv_split > 1) {     // both halves of a pair read its new rows
+  if (k_new && plan.kv_split > 1) {     // every part of a kv head reads its new rows
     const hipError_t e = launch_kv_append(batch, k_new, v_new, src_dtype, kv, st);
     if (e != hipSuccess) return e;
     p.k_new = p.v_new = nullptr;
