@@ -109,7 +109,11 @@ typedef struct {
  *                   such wait gives up (a way to exercise the failure path).
  *                   A wait that gives up writes NaN to the rows of that pair and
  *                   sets bit 0 of the workspace status word (see
- *                   sva_spec_verify_attn); the workspace stays reusable. */
+ *                   sva_spec_verify_attn); the workspace stays reusable.  Where
+ *                   the planner splits a kv head's G query heads over 2 or 4
+ *                   workgroups (pairs of more than 32 query rows, or few
+ *                   pairs), a pair is that share of the heads, and so are its
+ *                   NaN rows. */
 typedef struct {
   int32_t path;
   int32_t num_workgroups;
@@ -248,7 +252,8 @@ sva_status sva_spec_verify_attn_tree(const sva_batch *batch, const void *q, int3
  *     loaded on that device, held until the process ends).  A shape whose
  *     workspace (sva_verify_workspace_bytes) exceeds it returns
  *     SVA_ERR_UNSUPPORTED before anything is enqueued; at d = 128 and 256
- *     workgroups that is above 62 query rows (k_b * G) per pair.
+ *     workgroups that is above 62 query rows per pair (k_b * G, or the share
+ *     of it a pair keeps where the query heads are split over workgroups).
  *   - The first call on a device takes the array's address and enqueues one
  *     small kernel on `stream` that zeroes its counters; no call allocates
  *     memory.
@@ -270,7 +275,9 @@ sva_status sva_spec_verify_attn_noalloc(const sva_batch *batch, const void *q, i
  * enter the cache and are verified in the same pass).  On the split-KV
  * kernels the appended rows are written by the workgroup that streams their
  * page, before it starts streaming, so the step needs one launch fewer; for
- * long speculated steps (the row-block kernel) the append is its own launch.
+ * long speculated steps (the row-block kernel), and where a kv head's query
+ * heads are split over workgroups (each of them reads the new rows), the
+ * append is its own launch.
  *   k_new, v_new  device [T, Hkv, d] of src_dtype (SVA_F32 or SVA_BF16), as for
  *                 sva_kv_append
  * Every other argument, and every limit, is as for sva_spec_verify_attn (or
