@@ -2707,7 +2707,7 @@ AttnPlan plan_verify_attn(const sva_batch* batch, const sva_paged_kv* kv, int Hq
   // mostly hits L2).  First until a pair's rows fit one 32-row pass: a pair
   // with more rows is otherwise streamed once per pass (8B-shaped GQA, G = 8,
   // k = 8, 64 pairs: 63.5 -> 40.3 us; 128 pairs: 100.6 -> 61.8 us; k = 16,
-  // G = 8, 16 pairs: 134.6 -> 81.2 us).  Then once more for few pairs (at
+  // G = 8, 16 pairs, in four: 134.6 -> 56.1 us).  Then once more for few pairs (at
   // most one per 8 CUs) of 32 rows: every pair is cut into half as many
   // segments for the same grid and each merge folds half as many rows (one
   // GPU's TP-8 share of the 70B INT8 shape: 27.1 -> 21.0 us; 4 sequences of
@@ -2715,15 +2715,20 @@ AttnPlan plan_verify_attn(const sva_batch* batch, const sva_paged_kv* kv, int Hq
   // Not for pairs of 16 rows or fewer (half an MFMA block per part: 4 x 8192
   // tokens, G = 4, k = 4 took 32.7 -> 35 us), nor for many pairs of 32 rows
   // (the whole 70B INT8 shape: the later reads missed L2, 1.36x the KV bytes,
-  // and the call was slower).
+  // and the call was slower), nor beyond one pair per CU: the parts of a kv
+  // head must stream at the same time, on different workgroups, for L2 to
+  // serve the later reads.
   pl.kv_split = 1;
+  const int64_t kv_pairs = int64_t(batch->B) * kv->Hkv;
   if (!pl.rows_kernel && mfma_ok) {
-    while (rows / pl.kv_split > kMfmaRows && G % (2 * pl.kv_split) == 0) pl.kv_split *= 2;
+    while (rows / pl.kv_split > kMfmaRows && G % (2 * pl.kv_split) == 0 &&
+           kv_pairs * 2 * pl.kv_split <= num_cus)
+      pl.kv_split *= 2;
     if (rows / pl.kv_split >= kMfmaRows && G % (2 * pl.kv_split) == 0 &&
-        int64_t(batch->B) * kv->Hkv * pl.kv_split * 8 <= num_cus)
+        kv_pairs * pl.kv_split * 8 <= num_cus)
       pl.kv_split *= 2;
   }
-  const int64_t npairs = int64_t(batch->B) * kv->Hkv * pl.kv_split;
+  const int64_t npairs = kv_pairs * pl.kv_split;
   const int64_t pages_per_seq =
       std::min<int64_t>(kv->max_pages_per_seq, (int64_t(batch->max_len) + kPage - 1) / kPage);
   const int64_t pages_ub = npairs * std::max<int64_t>(pages_per_seq, 1);
