@@ -123,7 +123,9 @@ def test_fused_against_the_oracle():
     assert_close(out, ref, "bf16")
 
 
-@pytest.mark.parametrize("name", ["gqa8b", "gqa70b_int8"])
+# gqa70b_int8_tp8 (16 pairs of 32 query rows) splits each kv head's query
+# heads over two workgroups, so its fused call appends in a launch of its own
+@pytest.mark.parametrize("name", ["gqa8b", "gqa70b_int8", "gqa70b_int8_tp8"])
 def test_fused_full_size(name):
     w = wl.WORKLOADS[name]
     say(f"fused append full size {name}")
