@@ -12,7 +12,8 @@ One step = one pass of the whole hot path over one synthetic batch:
   --workload prm7b_step verifies long speculated steps (128 drafts per
   sequence, the attention shape of a 7B process reward model): kv_append ->
   verification attention, whose roofline is MFMA throughput (the reward
-  model's threshold is not part of this path).
+  model's threshold is not part of this path); --workload prm7b_step_b1 is the
+  same for one sequence (the latency of scoring one step).
 
 Default workload: the ragged serving batch -- B=64, S_b ~ U[256, 16384],
 k_b ~ U{1..8}, Hq=32, Hkv=8, d=128, bf16 paged KV (16-token pages, random page
@@ -178,6 +179,7 @@ class CpuBaseline:
         tree = w.name in wl.TREE_WORKLOADS
         long = w.name in wl.LONG_WORKLOADS
         sampled = w.name in wl.SAMPLED_WORKLOADS
+        self.long = long
         t0 = time.perf_counter()
         case = wl.make_case(w, device="cpu", seed_offset=0, with_logits=not (tree or long))
         np_ = lambda t: (t.float() if t.dtype == torch.bfloat16 else t).numpy()
@@ -268,7 +270,7 @@ class CpuBaseline:
                        f"processes (each repeating its share of the batch's {len(self.pairs)} "
                        f"pairs for {budget_s:.0f} s; a pass takes {t_attn * 1e3:.1f} ms, the slowest "
                        f"share), the whole append once ({self.t_append * 1e3:.1f} ms, one core)"
-                       + ("" if w.name == "prm7b_step" else
+                       + ("" if self.long else
                           f", acceptance of all {self.B} sequences x {self.accept_reps} "
                           f"({self.t_accept * 1e3:.2f} ms each, one core)")
                        + f"; inputs drawn on the host with the workload's recipe and seeds; "

@@ -87,7 +87,11 @@ def test_tree_mask_on_row_block_kernel():
 # d = 64 caches (16 nodes x G = 16: 256 rows per pair), and both ways a block
 # copies its pages: 256-row blocks (every wave holds rows: one page per
 # second-half wave) and 224-row blocks (the last wave holds none and copies
-# every page), on bf16 and INT8 caches with many committed groups.
+# every page), on bf16 and INT8 caches with many committed groups.  These
+# shapes take the row-block kernel by rule (more than 16 drafts or 128 rows
+# per pair); on a 256-CU part rows-int8-d64 and rows-int8-tree cut their
+# blocks into 2 key slices and the INT8 copy cases into 3, the others (fewer
+# page groups per block) keep one.
 ROW_VARIANTS = [
     (_wk("rows-int8-d64", 16, 4, 64, "int8", "bf16", 0.5, ident=119), [300, 5], [40, 70], False),
     (_wk("rows-int8-tree", 64, 4, 128, "int8", "bf16", 0.5, ident=120), [70, 0, 300], [16, 9, 16],
@@ -111,7 +115,6 @@ def test_row_block_kernel_variants(spec):
     case = wl.make_case(w, device=DEV, ctx=ctx, k=ks, with_logits=False)
     batch = batch_of(case)
     kv = paged_kv(case)
-    assert tva.verify_workspace_bytes(batch, kv, w.Hq) == tva.STATUS_OFFSET + 256   # row blocks
     om = None
     if tree:
         parents = wl.make_tree(ks, device=DEV, seed=w.ident)
@@ -172,3 +175,79 @@ def test_prm7b_step_full_size_sampled():
     pairs = [(0, 0), (5, 3), (11, 1), (15, 2)]
     ref = oracle_attn(case, select=pairs)
     assert_close(out, ref, "bf16", rows=rows_of_pairs(case, pairs))
+
+
+# One sequence of the 7B PRM shape: its 4 pairs of 896 query rows make 16 row
+# blocks, far fewer than the CUs, so each block's keys are cut into slices
+# streamed by separate workgroups whose partial states a second launch folds
+# (the workspace then holds those states).  Checked on every query row.
+KEY_SLICES = [
+    (_wk("slices-bf16", 28, 4, 128, "bf16", "bf16", ident=127), [3000], [128], False),
+    (_wk("slices-int8", 28, 4, 128, "int8", "bf16", 0.5, ident=128), [2100], [128], False),
+    (_wk("slices-d64-two", 16, 4, 64, "bf16", "bf16", ident=129), [1500, 40], [96, 200], False),
+    (_wk("slices-tree", 64, 4, 128, "bf16", "bf16", ident=130), [2000], [16], True),
+]
+
+
+@pytest.mark.parametrize("spec", KEY_SLICES, ids=[s[0].name for s in KEY_SLICES])
+def test_row_blocks_cut_into_key_slices(spec):
+    w, ctx, ks, tree = spec
+    say(f"row-block key slices {w.name}")
+    case = wl.make_case(w, device=DEV, ctx=ctx, k=ks, with_logits=False)
+    batch = batch_of(case)
+    kv = paged_kv(case)
+    assert tva.verify_workspace_bytes(batch, kv, w.Hq) > tva.STATUS_OFFSET + 256   # sliced
+    masks = om = None
+    if tree:
+        parents = wl.make_tree(ks, device=DEV, seed=w.ident)
+        masks = tva.tree_masks(batch, parents)
+        om = oracle.ancestor_masks(np_(parents), np_(case["cu_q"]))
+    out = tva.spec_verify_attn(batch, case["q"], kv, draft_mask=masks)
+    again = tva.spec_verify_attn(batch, case["q"], kv, draft_mask=masks)
+    torch.cuda.synchronize()
+    assert torch.equal(out, again)                     # the slices fold in a fixed order
+    qn, kp, vp = np_(case["q"]), np_(case["k_pool"]), np_(case["v_pool"])
+    args = (np_(case["block_table"]), np_(case["ctx_lens"]), np_(case["cu_q"]), 1.0 / math.sqrt(w.d))
+    if w.kv_dtype == "int8":
+        P, H = kp.shape[:2]
+        kc, ksc = oracle.kv_quant_int8(kp.reshape(-1, w.d))
+        vc, vsc = oracle.kv_quant_int8(vp.reshape(-1, w.d))
+        ref_q = oracle.spec_verify_attn(qn, kc.reshape(kp.shape), vc.reshape(vp.shape), *args,
+                                        k_scale=ksc.reshape(P, H, 16), v_scale=vsc.reshape(P, H, 16))
+        assert_close(out, ref_q, "int8_deq")
+        assert_close(out, oracle.spec_verify_attn(qn, kp, vp, *args), "int8")
+    else:
+        assert_close(out, oracle.spec_verify_attn(qn, kp, vp, *args, draft_mask=om), "bf16")
+
+
+def test_key_slices_without_allocation():
+    """The allocation-free entry point limits the slices' partial states to its
+    static scratch (fewer slices) and gives the same rows within the bar."""
+    w = KEY_SLICES[0][0]
+    case = wl.make_case(w, device=DEV, ctx=[3000], k=[128], with_logits=False)
+    batch = batch_of(case)
+    kv = paged_kv(case)
+    out = tva.spec_verify_attn_noalloc(batch, case["q"], kv)
+    torch.cuda.synchronize()
+    ref = oracle.spec_verify_attn(np_(case["q"]), np_(case["k_pool"]), np_(case["v_pool"]),
+                                  np_(case["block_table"]), np_(case["ctx_lens"]),
+                                  np_(case["cu_q"]), 1.0 / math.sqrt(w.d))
+    assert_close(out, ref, "bf16")
+
+
+def test_prm7b_step_b1_full_size_every_pair():
+    """One sequence of the 7B PRM shape (its row blocks cut into key slices),
+    through the fused append call the benchmark times, on every pair."""
+    w = wl.WORKLOADS["prm7b_step_b1"]
+    say("prm7b_step_b1 full size")
+    case = wl.make_case(w, device=DEV, with_logits=False)
+    batch = batch_of(case)
+    kv = paged_kv(case)
+    kp, vp = np_(case["k_pool"]), np_(case["v_pool"])          # before the GPU append
+    out = tva.spec_verify_attn_append(batch, case["q"], kv, case["k_new"], case["v_new"])
+    torch.cuda.synchronize()
+    bt, ctx, cu = np_(case["block_table"]), np_(case["ctx_lens"]), np_(case["cu_q"])
+    kp, vp, _, _ = oracle.kv_append(np_(case["k_new"]), np_(case["v_new"]), kp, vp, bt, ctx, cu,
+                                    "bf16")
+    ref = oracle.spec_verify_attn(np_(case["q"]), kp, vp, bt, ctx, cu, 1.0 / math.sqrt(w.d))
+    assert_close(out, ref, "bf16")

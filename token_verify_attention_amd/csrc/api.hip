@@ -254,7 +254,8 @@ static sva_status verify_attn(const sva_batch* batch, const void* q, int32_t q_d
                               const sva_verify_opts* opts, void* workspace,
                               size_t workspace_bytes, void* stream,
                               const void* k_new = nullptr, const void* v_new = nullptr,
-                              int32_t src_dtype = SVA_BF16) {
+                              int32_t src_dtype = SVA_BF16,
+                              size_t max_bytes = size_t(1) << 30) {
   if (sva_status s = check_attn_shape(batch, kv, Hq, opts, draft_mask != nullptr)) return s;
   if (q_dtype != SVA_F32 && q_dtype != SVA_BF16)
     return fail(SVA_ERR_UNSUPPORTED, "q_dtype = %d", q_dtype);
@@ -274,7 +275,7 @@ static sva_status verify_attn(const sva_batch* batch, const void* q, int32_t q_d
     return fail(SVA_ERR_INVALID_ARG, "INT8 scales must be 16-byte aligned");
   const DeviceInfo* dev;
   if (sva_status s = current_device(&dev)) return s;
-  const sva::AttnPlan plan = sva::plan_verify_attn(batch, kv, Hq, dev->num_cus, opts);
+  const sva::AttnPlan plan = sva::plan_verify_attn(batch, kv, Hq, dev->num_cus, opts, max_bytes);
   if (!workspace || workspace_bytes < plan.total_bytes)
     return fail(SVA_ERR_INVALID_ARG, "workspace of %zu bytes < %zu needed", workspace_bytes,
                 plan.total_bytes);
@@ -302,7 +303,10 @@ sva_status sva_spec_verify_attn_noalloc(const sva_batch* batch, const void* q, i
   if (sva_status s = check_attn_shape(batch, kv, Hq, opts, false)) return s;
   const DeviceInfo* dev;
   if (sva_status s = current_device(&dev)) return s;
-  const size_t need = sva::plan_verify_attn(batch, kv, Hq, dev->num_cus, opts).total_bytes;
+  // the row-block kernel's key slices are limited to the scratch; the split
+  // kernel's partials are not (a shape that needs more is refused)
+  const size_t need =
+      sva::plan_verify_attn(batch, kv, Hq, dev->num_cus, opts, kScratchBytes).total_bytes;
   if (need > kScratchBytes)
     return fail(SVA_ERR_UNSUPPORTED,
                 "this call needs %zu bytes of workspace; the static scratch holds %zu "
@@ -311,7 +315,7 @@ sva_status sva_spec_verify_attn_noalloc(const sva_batch* batch, const void* q, i
   void* ws = nullptr;
   if (sva_status s = scratch_for_current_device(&ws, as_stream(stream))) return s;
   return verify_attn(batch, q, q_dtype, Hq, kv, nullptr, softmax_scale, out, out_dtype, opts, ws,
-                     kScratchBytes, stream);
+                     kScratchBytes, stream, nullptr, nullptr, SVA_BF16, kScratchBytes);
 }
 
 sva_status sva_spec_verify_attn_append(const sva_batch* batch, const void* q, int32_t q_dtype,

@@ -21,7 +21,9 @@ hipError_t launch_kv_append(const sva_batch* batch, const void* k_new, const voi
 // slots.
 struct AttnPlan {
   bool rows_kernel;     // row-block kernel (many query rows per pair); no workspace
-  int rows_grid;        // its grid (an upper bound on the row blocks)
+  int rows_grid;        // its grid (an upper bound on the row blocks times rows_nseg)
+  int rows_nseg;        // key slices per row block (> 1: a merge launch follows)
+  int rows_merge_grid;  // the merge's grid (an upper bound on the row blocks)
   int num_wg;
   int wait_polls;       // bound on a split pair's wait for the others' partials
   int seg_cost;         // fixed cost of a segment, in pages, for the work split
@@ -31,8 +33,10 @@ struct AttnPlan {
   size_t slot_bytes;
   size_t total_bytes;
 };
+// max_bytes: the workspace the plan may need at most (the row-block kernel's
+// key slices are limited to it).
 AttnPlan plan_verify_attn(const sva_batch* batch, const sva_paged_kv* kv, int Hq, int num_cus,
-                          const sva_verify_opts* opts);
+                          const sva_verify_opts* opts, size_t max_bytes = size_t(1) << 30);
 // draft_mask: [T] tree attention masks (bit j: draft j of the sequence is
 // visible), or NULL for causal drafts.
 // k_new / v_new (may be NULL): [T, Hkv, d] rows of src_dtype appended to the

@@ -103,6 +103,10 @@ struct AttnParams {
   // a kv head form 2^kv_shift pairs (Hkv and G above count those pairs),
   // streamed by different workgroups.
   int kv_shift;
+  // Row-block kernel: key slices per row block (1: each block streams all of
+  // its pair's pages and writes its rows; more: each slice writes partial
+  // states that a second launch merges).
+  int rows_nseg;
 };
 
 struct SeqInfo {
@@ -1392,6 +1396,23 @@ struct MfmaStep {
     }
   }
 
+  // This wave's partial state -- unnormalised O, running maxima, weight sums
+  // -- of rows rr0 .. rr0 + 16 NRB - 1 of a slot of slot_rows rows laid out
+  // as O [slot_rows][D], m [slot_rows], l [slot_rows] (row-block key slices).
+  __device__ __forceinline__ void write_partial(float* slot, int rr0, int slot_rows) const {
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+      const int rr = rr0 + 16 * rb + l16;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+        *reinterpret_cast<f32x4*>(slot + rr * D + 16 * db + 4 * c) = acc[rb][db];
+      if (c == 0) {
+        slot[slot_rows * D + rr] = m[rb];
+        slot[slot_rows * (D + 1) + rr] = l[rb];
+      }
+    }
+  }
+
   // One (row, 4-column) item of the merge of the nw waves' states stored at
   // mrg + w * stride (store() layout), combined in wave order: the running
   // maximum M, the denominator L and the unnormalised output columns O.
@@ -2430,6 +2451,13 @@ __global__ __launch_bounds__((AttnLds<KV, D, MF>::NT), 1) void verify_attn_kerne
 constexpr int kRowWaves = 8;                       // two waves per SIMD
 constexpr int kRowHalf = kRowWaves / 2;
 constexpr int kRowBlock = kRowWaves * kMfmaRows;   // 256 query rows per workgroup
+constexpr int kRowMergeThreads = 256;
+constexpr int kMinSliceGroups = 4;                  // groups of pages per key slice, at least
+constexpr size_t kCounterBytes = size_t(2 * kMaxWorkgroups) * 4 + 256;
+// A key slice's partial state of one row block: unnormalised O [256][D], then
+// the running maxima [256] and the weight sums [256] (fp32).
+template <int D>
+constexpr int kRowSlotFloats = kRowBlock * (D + 2);
 
 template <typename KV, int D>
 struct RowsLds {
@@ -2444,9 +2472,70 @@ struct RowsLds {
   static_assert((NS - 3) * Gm::P <= 63, "vmcnt range");
 };
 
-// Row blocks of sequence b: Hkv * ceil(k_b * G / 256).
-__device__ __forceinline__ int row_blocks(const AttnParams& p, const SeqInfo& si) {
-  return si.k > 0 ? p.Hkv * ((si.k * p.G + kRowBlock - 1) / kRowBlock) : 0;
+// Row blocks of sequence b: Hkv * ceil(k_b * G / 256), times nseg key slices.
+__device__ __forceinline__ int row_blocks(const AttnParams& p, const SeqInfo& si, int nseg) {
+  return si.k > 0 ? p.Hkv * ((si.k * p.G + kRowBlock - 1) / kRowBlock) * nseg : 0;
+}
+
+// The blocks of the batch lie sequence after sequence.  rows_scan: NT threads
+// each count the blocks of a contiguous chunk of sequences (returned) and
+// their exclusive prefix sums go to s_scan; the total to s_info[0].
+template <int NT>
+__device__ __forceinline__ int rows_scan(const AttnParams& p, int nseg, int32_t* s_scan,
+                                         int32_t* s_info) {
+  const int tid = threadIdx.x;
+  const int per = (p.B + NT - 1) / NT;
+  int tot = 0;
+  for (int e = 0; e < per; ++e) {
+    const int b = tid * per + e;
+    if (b < p.B) tot += row_blocks(p, seq_info(p, b), nseg);
+  }
+  s_scan[tid] = tot;
+  __syncthreads();
+  if (tid < kWave) {
+    constexpr int PER_LANE = NT / kWave;
+    int run = 0;
+    for (int i = 0; i < PER_LANE; ++i) {
+      const int v = s_scan[tid * PER_LANE + i];
+      s_scan[tid * PER_LANE + i] = run;
+      run += v;
+    }
+    int incl = run;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int u = __shfl_up(incl, o, kWave);
+      if (tid >= o) incl += u;
+    }
+    const int excl = incl - run;
+    for (int i = 0; i < PER_LANE; ++i) s_scan[tid * PER_LANE + i] += excl;
+    if (tid == kWave - 1) s_info[0] = incl;
+  }
+  __syncthreads();
+  return tot;
+}
+// rows_find: block w (< the total) lies in sequence s_info[1], which starts at
+// block s_info[3]; s_info[2] = w - s_info[3].  Ends with a barrier.
+template <int NT>
+__device__ __forceinline__ void rows_find(const AttnParams& p, int nseg, int w, int tot,
+                                          const int32_t* s_scan, int32_t* s_info) {
+  const int tid = threadIdx.x;
+  const int per = (p.B + NT - 1) / NT;
+  const int base = s_scan[tid];
+  if (tot > 0 && base <= w && w < base + tot) {
+    int run = base;
+    for (int e = 0; e < per; ++e) {
+      const int b = tid * per + e;
+      const int n = row_blocks(p, seq_info(p, b), nseg);
+      if (w < run + n) {
+        s_info[1] = b;
+        s_info[2] = w - run;
+        s_info[3] = run;
+        break;
+      }
+      run += n;
+    }
+  }
+  __syncthreads();
 }
 
 // Wait until at most n (<= MAXN) later units of P copies each are in flight.
@@ -2479,37 +2568,10 @@ void verify_attn_rows_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(1024))) char s_ring[L::RING];
   __shared__ int32_t s_scan[NT];
   __shared__ int32_t s_info[4];
-  const int tid = threadIdx.x;
-  const int B = p.B;
+  const int nseg = p.rows_nseg;
 
   // ---- this workgroup's block: exclusive scan of the per-sequence counts
-  const int per = (B + NT - 1) / NT;
-  int tot = 0;
-  for (int e = 0; e < per; ++e) {
-    const int b = tid * per + e;
-    if (b < B) tot += row_blocks(p, seq_info(p, b));
-  }
-  s_scan[tid] = tot;
-  __syncthreads();
-  if (tid < kWave) {
-    constexpr int PER_LANE = NT / kWave;
-    int run = 0;
-    for (int i = 0; i < PER_LANE; ++i) {
-      const int v = s_scan[tid * PER_LANE + i];
-      s_scan[tid * PER_LANE + i] = run;
-      run += v;
-    }
-    int incl = run;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-      const int u = __shfl_up(incl, o, kWave);
-      if (tid >= o) incl += u;
-    }
-    const int excl = incl - run;
-    for (int i = 0; i < PER_LANE; ++i) s_scan[tid * PER_LANE + i] += excl;
-    if (tid == kWave - 1) s_info[0] = incl;
-  }
-  __syncthreads();
+  const int tot = rows_scan<NT>(p, nseg, s_scan, s_info);
   const int total = s_info[0];
   // Workgroups are dispatched to the 8 XCDs in turn (blockIdx.x % 8), one per
   // CU here (the ring takes most of the LDS): XCD x takes blocks
@@ -2521,29 +2583,17 @@ void verify_attn_rows_kernel(AttnParams p) {
   const int j = hw / 8;
   const int w = (hw % 8) * per_xcd + j;
   if (j >= per_xcd || w >= total) return;
-  {
-    const int base = s_scan[tid];
-    if (tot > 0 && base <= w && w < base + tot) {
-      int run = base;
-      for (int e = 0; e < per; ++e) {
-        const int b = tid * per + e;
-        const int n = row_blocks(p, seq_info(p, b));
-        if (w < run + n) {
-          s_info[1] = b;
-          s_info[2] = w - run;
-          break;
-        }
-        run += n;
-      }
-    }
-  }
-  __syncthreads();
+  rows_find<NT>(p, nseg, w, tot, s_scan, s_info);
   const int b = s_info[1];
   const SeqInfo si = seq_info(p, b);
   const int nblk = (si.k * p.G + kRowBlock - 1) / kRowBlock;
+  // within the sequence: kv head, then key slice, then row block, so that the
+  // row blocks of one slice (which read the same pages) are neighbours
+  const int x = s_info[2];
+  const int seg = (x / nblk) % nseg, rbk = x % nblk;
   Seg sg;
   sg.b = b;
-  sg.g = s_info[2] / nblk;
+  sg.g = x / (nblk * nseg);
   sg.S = si.S;
   sg.k = si.k;
   sg.q0 = si.q0;
@@ -2557,16 +2607,22 @@ void verify_attn_rows_kernel(AttnParams p) {
   // half-empty last block ran ahead of its pair and the rest fetched its
   // pages again: 1.8x the pages' bytes from memory).
   const int rpb = ((sg.R + nblk - 1) / nblk + kMfmaRows - 1) / kMfmaRows * kMfmaRows;
-  const int r0 = (s_info[2] % nblk) * rpb;
+  const int r0 = rbk * rpb;
   const int r_end = min(sg.R, r0 + rpb);
   const int last_row = r_end - 1;
   // keys up to the last row's position: pages 0 .. npages-1, in groups of NP
   constexpr int NP = L::NP;
   const int npages = min(si.np, (si.S + last_row / p.G) / kPage + 1);
   sg.pe = npages;
-  const int nunits = (npages + NP - 1) / NP;
+  // Key slice seg: groups [ua, ua + nunits) of the pair's groups cut into
+  // nseg equal ranges (the same cut for every row block of the pair), up to
+  // this block's last group; loop indices below count from ua.
+  const int npages_pair = min(si.np, (si.S + (sg.R - 1) / p.G) / kPage + 1);
+  const int nunits_pair = (npages_pair + NP - 1) / NP;
+  const int ua = seg * nunits_pair / nseg;
+  const int nunits = max(0, min((seg + 1) * nunits_pair / nseg, (npages + NP - 1) / NP) - ua);
   // groups below u_plain hold committed context only: no masks
-  const int u_plain = min(nunits, si.S / (NP * kPage));
+  const int u_plain = max(0, min(nunits, si.S / (NP * kPage) - ua));
   const int wave = wave_id();
   const int half = wave / kRowHalf;
   const int rw = r0 + kMfmaRows * wave;            // this wave's first row
@@ -2589,13 +2645,13 @@ void verify_attn_rows_kernel(AttnParams p) {
     if (idle_copier) {
       int ids[NP];
 #pragma unroll
-      for (int j = 0; j < NP; ++j) ids[j] = page_id(p, b, min(NP * u + j, npages - 1));
+      for (int j = 0; j < NP; ++j) ids[j] = page_id(p, b, min(NP * (ua + u) + j, npages - 1));
 #pragma unroll
       for (int j = 0; j < NP; ++j)
         dma_page<KV, D, false>(p, ids[j], sg.g, s_ring + (u % NS) * L::UNIT + j * Gm::SLOT);
       return;
     }
-    const int pg = min(NP * u + cw, npages - 1);
+    const int pg = min(NP * (ua + u) + cw, npages - 1);
     dma_page<KV, D, false>(p, page_id(p, b, pg), sg.g,
                            s_ring + (u % NS) * L::UNIT + cw * Gm::SLOT);
   };
@@ -2620,18 +2676,18 @@ void verify_attn_rows_kernel(AttnParams p) {
   auto products = [&](int u, auto edge) __attribute__((always_inline)) {           // P.V of group u-1, S^T of group u
     constexpr bool EDGE = decltype(edge)::value;
     __builtin_amdgcn_s_setprio(1);
-    st.template mma_phase<EDGE>(slot(u + NS - 1), NP * (u - 1), u > 0, slot(u), u < nunits);
+    st.template mma_phase<EDGE>(slot(u + NS - 1), NP * (ua + u - 1), u > 0, slot(u), u < nunits);
     __builtin_amdgcn_s_setprio(0);
   };
   // groups 1 .. u_plain - 1: both groups of the phase exist and need no masks
   auto products_steady = [&](int u) __attribute__((always_inline)) {
     __builtin_amdgcn_s_setprio(1);
-    st.template mma_phase<false, true>(slot(u + NS - 1), NP * (u - 1), true, slot(u), true);
+    st.template mma_phase<false, true>(slot(u + NS - 1), NP * (ua + u - 1), true, slot(u), true);
     __builtin_amdgcn_s_setprio(0);
   };
   auto softmax = [&](int u, auto edge) __attribute__((always_inline)) {
     constexpr bool EDGE = decltype(edge)::value;
-    st.template softmax_phase<EDGE>(NP * u, npages);
+    st.template softmax_phase<EDGE>(NP * (ua + u), npages);
   };
   // iteration w: phases 2w and 2w+1.  The copies of group w + NS - 2 go into
   // the slot that group w - 2 left in phase 2w - 1, and group w + 1 has
@@ -2678,8 +2734,69 @@ void verify_attn_rows_kernel(AttnParams p) {
   }
   if (active) {
     st.finish();
-    st.write_rows(p, sg, rw);
+    if (nseg == 1) {
+      st.write_rows(p, sg, rw);
+    } else {                                     // this slice's partial state
+      const int slot = ((s_info[3] / nseg) + sg.g * nblk + rbk) * nseg + seg;
+      st.write_partial(p.partials + int64_t(slot) * kRowSlotFloats<D>, rw - r0, kRowBlock);
+    }
   }
+}
+
+// Key slices of the row blocks: workgroup w folds the nseg partial states of
+// rows kMergeRows (w % kMergeParts) .. + kMergeRows of row block
+// w / kMergeParts, slice by slice in key order (the same operations whatever
+// the grid), and writes them normalised.  One (row, 4-column) item per
+// thread; the states of 8 slices are loaded together before they are folded,
+// so an item costs a memory round trip per 8 slices.
+template <int D>
+__global__ __launch_bounds__(kRowMergeThreads) void verify_rows_merge_kernel(AttnParams p) {
+  constexpr int NT = kRowMergeThreads;
+  constexpr int kMergeRows = NT / (D / 4);
+  constexpr int kMergeParts = kRowBlock / kMergeRows;
+  constexpr int kBatch = 8;
+  __shared__ int32_t s_scan[NT];
+  __shared__ int32_t s_info[4];
+  const int nseg = p.rows_nseg;
+  const int tot = rows_scan<NT>(p, 1, s_scan, s_info);
+  const int w = blockIdx.x / kMergeParts;
+  if (w >= s_info[0]) return;
+  rows_find<NT>(p, 1, w, tot, s_scan, s_info);
+  const int b = s_info[1];
+  const SeqInfo si = seq_info(p, b);
+  const int nblk = (si.k * p.G + kRowBlock - 1) / kRowBlock;
+  Seg sg;
+  sg.b = b;
+  sg.g = s_info[2] / nblk;
+  sg.q0 = si.q0;
+  sg.R = si.k * p.G;
+  const int rpb = ((sg.R + nblk - 1) / nblk + kMfmaRows - 1) / kMfmaRows * kMfmaRows;
+  const int r0 = (s_info[2] % nblk) * rpb;
+  const int rows = min(sg.R, r0 + rpb) - r0;
+  const int r = (blockIdx.x % kMergeParts) * kMergeRows + int(threadIdx.x) / (D / 4);
+  const int d4 = int(threadIdx.x) % (D / 4);
+  if (r >= rows) return;
+  const float* base = p.partials + int64_t(w) * nseg * kRowSlotFloats<D>;
+  float M = kNegBig, L = 0.f;
+  f32x4 O{0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < nseg; s0 += kBatch) {
+    float ms[kBatch], ls[kBatch];
+    f32x4 os[kBatch];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const float* sl = base + int64_t(min(s0 + i, nseg - 1)) * kRowSlotFloats<D>;
+      ms[i] = sl[kRowBlock * D + r];
+      ls[i] = sl[kRowBlock * (D + 1) + r];
+      os[i] = *reinterpret_cast<const f32x4*>(sl + r * D + 4 * d4);
+    }
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i)
+      if (s0 + i < nseg) combine_partial(M, L, O, ms[i], ls[i], os[i]);
+  }
+  const float inv = 1.f / L;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) O[i] *= inv;
+  store_out4(p, out_row(p, sg, r0 + r) * D + 4 * d4, O);
 }
 
 // ============================================================================
@@ -2687,7 +2804,7 @@ void verify_attn_rows_kernel(AttnParams p) {
 // ============================================================================
 
 AttnPlan plan_verify_attn(const sva_batch* batch, const sva_paged_kv* kv, int Hq, int num_cus,
-                          const sva_verify_opts* opts) {
+                          const sva_verify_opts* opts, size_t max_bytes) {
   AttnPlan pl;
   const int G = Hq / kv->Hkv;
   // Row-block kernel: when a pair has more query rows than the split kernel
@@ -2699,8 +2816,27 @@ AttnPlan plan_verify_attn(const sva_batch* batch, const sva_paged_kv* kv, int Hq
       int64_t(kv->Hkv) * ((int64_t(batch->total_q) * G + kRowBlock - 1) / kRowBlock + batch->B);
   pl.rows_kernel = mfma_ok && (batch->max_q > kMaxDraftsSplit || rows > kMaxRowsSplit ||
                                (rows > kMfmaRows && blocks_ub >= num_cus));
+  const int64_t pages_per_seq =
+      std::min<int64_t>(kv->max_pages_per_seq, (int64_t(batch->max_len) + kPage - 1) / kPage);
+  // Key slices for the row-block kernel when its blocks leave CUs idle (a few
+  // long steps): about one block per CU, each slice at least kMinSliceGroups
+  // groups of pages, and the partial states within max_bytes.
+  pl.rows_nseg = 1;
+  const size_t row_slot_bytes = size_t(kRowBlock) * (kv->d + 2) * sizeof(float);
+  if (pl.rows_kernel) {
+    const int group_pages = kv->kv_dtype == SVA_INT8 ? 2 : 4;
+    const int64_t groups = (std::max<int64_t>(pages_per_seq, 1) + group_pages - 1) / group_pages;
+    int64_t ns = std::min<int64_t>(num_cus / std::max<int64_t>(blocks_ub, 1),
+                                   groups / kMinSliceGroups);
+    const size_t avail = max_bytes > kCounterBytes ? max_bytes - kCounterBytes : 0;
+    ns = std::min<int64_t>(ns, int64_t(avail / (row_slot_bytes * size_t(std::max<int64_t>(blocks_ub, 1)))));
+    if (ns > 1) pl.rows_nseg = int(std::min<int64_t>(ns, 64));
+  }
   // a multiple of 8 (the kernel spreads its blocks evenly over the 8 XCDs)
-  pl.rows_grid = int(std::min<int64_t>((blocks_ub + 7) / 8 * 8, 0x7ffffff8));
+  pl.rows_grid = int(std::min<int64_t>((blocks_ub * pl.rows_nseg + 7) / 8 * 8, 0x7ffffff8));
+  // merge: kRowBlock / (kRowMergeThreads / (d / 4)) workgroups per row block
+  pl.rows_merge_grid = int(std::min<int64_t>(
+      blocks_ub * (kRowBlock / (kRowMergeThreads / (kv->d / 4))), 0x7fffffff));
   // Query heads split over workgroups: a kv head's G query heads form
   // kv_split pairs of G / kv_split, streamed by neighbouring workgroups of
   // one XCD that read the same pages at about the same time (the later read
@@ -2729,8 +2865,6 @@ AttnPlan plan_verify_attn(const sva_batch* batch, const sva_paged_kv* kv, int Hq
       pl.kv_split *= 2;
   }
   const int64_t npairs = kv_pairs * pl.kv_split;
-  const int64_t pages_per_seq =
-      std::min<int64_t>(kv->max_pages_per_seq, (int64_t(batch->max_len) + kPage - 1) / kPage);
   const int64_t pages_ub = npairs * std::max<int64_t>(pages_per_seq, 1);
   int W = 0;
   if (opts && opts->num_workgroups > 0) {
@@ -2756,25 +2890,31 @@ AttnPlan plan_verify_attn(const sva_batch* batch, const sva_paged_kv* kv, int Hq
   pl.slot_rows = std::max(batch->max_q, 1) * (G / pl.kv_split);
   // arrival and publication counters, then the status word (256 bytes keep
   // the partial slots aligned)
-  pl.counter_bytes = size_t(2 * kMaxWorkgroups) * 4 + 256;
+  pl.counter_bytes = kCounterBytes;
   pl.slot_bytes = size_t(2) * W * pl.slot_rows * (kv->d + 2) * sizeof(float);
   pl.total_bytes = pl.counter_bytes + pl.slot_bytes;
-  if (pl.rows_kernel) {                 // no workspace needed
+  if (pl.rows_kernel) {                 // the key slices' partial states, if any
     pl.num_wg = 0;
-    pl.slot_bytes = 0;
-    pl.total_bytes = pl.counter_bytes;
+    pl.slot_bytes = pl.rows_nseg > 1 ? row_slot_bytes * size_t(blocks_ub) * pl.rows_nseg : 0;
+    pl.total_bytes = pl.counter_bytes + pl.slot_bytes;
   }
   return pl;
 }
 
 template <typename KV, int D>
-static hipError_t attn_rows_launch(const AttnParams& p, int grid, hipStream_t st) {
+static hipError_t attn_rows_launch(const AttnParams& p, int grid, int merge_grid, hipStream_t st) {
   if (p.draft_mask)
     hipLaunchKernelGGL((verify_attn_rows_kernel<KV, D, true>), dim3(grid), dim3(kRowWaves * kWave),
                        0, st, p);
   else
     hipLaunchKernelGGL((verify_attn_rows_kernel<KV, D, false>), dim3(grid), dim3(kRowWaves * kWave),
                        0, st, p);
+  if (p.rows_nseg > 1) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((verify_rows_merge_kernel<D>), dim3(merge_grid), dim3(kRowMergeThreads), 0,
+                       st, p);
+  }
   return hipGetLastError();
 }
 
@@ -2825,6 +2965,7 @@ hipError_t launch_verify_attn(const sva_batch* batch, const void* q, int q_dtype
   p.Hkv = kv->Hkv * plan.kv_split;
   p.G = Hq / kv->Hkv / plan.kv_split;
   p.kv_shift = __builtin_ctz(unsigned(plan.kv_split));
+  p.rows_nseg = plan.rows_nseg;
   p.num_pages = kv->num_pages;
   p.max_pages = kv->max_pages_per_seq;
   p.max_q = batch->max_q;
@@ -2840,11 +2981,12 @@ hipError_t launch_verify_attn(const sva_batch* batch, const void* q, int q_dtype
       if (e != hipSuccess) return e;
     }
     if (plan.rows_grid <= 0) return hipSuccess;
+    const int mg = plan.rows_merge_grid;
     if (kv->kv_dtype == SVA_BF16)
-      return kv->d == 64 ? attn_rows_launch<uint16_t, 64>(p, plan.rows_grid, st)
-                         : attn_rows_launch<uint16_t, 128>(p, plan.rows_grid, st);
-    return kv->d == 64 ? attn_rows_launch<int8_t, 64>(p, plan.rows_grid, st)
-                       : attn_rows_launch<int8_t, 128>(p, plan.rows_grid, st);
+      return kv->d == 64 ? attn_rows_launch<uint16_t, 64>(p, plan.rows_grid, mg, st)
+                         : attn_rows_launch<uint16_t, 128>(p, plan.rows_grid, mg, st);
+    return kv->d == 64 ? attn_rows_launch<int8_t, 64>(p, plan.rows_grid, mg, st)
+                       : attn_rows_launch<int8_t, 128>(p, plan.rows_grid, mg, st);
   }
   if (k_new && plan.kv_split > 1) {     // every part of a kv head reads its new rows
     const hipError_t e = launch_kv_append(batch, k_new, v_new, src_dtype, kv, st);

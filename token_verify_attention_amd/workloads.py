@@ -36,6 +36,9 @@ for are not available, and none of their items are reproduced):
                   attention shape of a 7B process reward model (Qwen2.5-Math-
                   7B: Hq=28, Hkv=4, d=128) scoring a 128-token step per
                   sequence, B=16, S=4096, bf16 ~ N(0,1).
+* ``prm7b_step_b1`` the same for one sequence (B=1): the latency of scoring
+                  a single reasoning step, where the row blocks alone would
+                  occupy 16 CUs.
 * ``ragged_sampled`` the ragged serving batch with stochastic acceptance:
                   drafter logits [T, 128256] = the target row's logits plus
                   N(0, 0.5^2) noise, temperature 1, uniforms u_accept [T] and
@@ -100,10 +103,12 @@ WORKLOADS = {
                                "bf16", 1.0, 128256, 0.8, ident=7),
     "prm7b_step": Workload("prm7b_step", 16, 28, 4, 128, 4096, 128, "bf16", "bf16", append=True,
                            ident=8),
+    "prm7b_step_b1": Workload("prm7b_step_b1", 1, 28, 4, 128, 4096, 128, "bf16", "bf16",
+                              append=True, ident=10),
 }
 
 SAMPLED_WORKLOADS = ("ragged_sampled",)
-LONG_WORKLOADS = ("prm7b_step",)
+LONG_WORKLOADS = ("prm7b_step", "prm7b_step_b1")
 
 TREE_WORKLOADS = ("tree8b",)
 
