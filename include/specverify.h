@@ -177,7 +177,11 @@ size_t sva_verify_workspace_bytes(const sva_batch *batch, const sva_paged_kv *kv
  * reasoning step in one parallel pass).  Pairs with many query rows (k_b * G
  * above 32, when their 256-row blocks fill the device, and always above 16
  * drafts or 128 rows) run on a row-block kernel that reads each page once per
- * block of 256 rows and needs no more workspace than the counters.  SVA_F32
+ * block of 256 rows.  When those blocks are fewer than the CUs (a few long
+ * steps), each block's keys are cut into slices streamed by separate
+ * workgroups, whose partial states (256 * (d + 2) fp32 per block and slice)
+ * the workspace holds and a second launch folds in key order; otherwise the
+ * row-block kernel needs no more workspace than the counters.  SVA_F32
  * caches always take the VALU path (query rows past 16 are handled in further
  * passes over the pages). */
 sva_status sva_spec_verify_attn(const sva_batch *batch, const void *q, int32_t q_dtype,
