@@ -258,6 +258,9 @@ sva_status sva_spec_verify_attn_tree(const sva_batch *batch, const void *q, int3
  *     SVA_ERR_UNSUPPORTED before anything is enqueued; at d = 128 and 256
  *     workgroups that is above 62 query rows per pair (k_b * G, or the share
  *     of it a pair keeps where the query heads are split over workgroups).
+ *     Long speculated steps whose row blocks are cut into key slices take
+ *     as many slices as the array holds (fewer than sva_spec_verify_attn may
+ *     take), so they are never refused for it.
  *   - The first call on a device takes the array's address and enqueues one
  *     small kernel on `stream` that zeroes its counters; no call allocates
  *     memory.
