@@ -251,3 +251,21 @@ def test_prm7b_step_b1_full_size_every_pair():
                                     "bf16")
     ref = oracle.spec_verify_attn(np_(case["q"]), kp, vp, bt, ctx, cu, 1.0 / math.sqrt(w.d))
     assert_close(out, ref, "bf16")
+
+
+# bf16 pairs of 33-128 query rows whose query heads cannot be split into one
+# 32-row pass (odd G) take the row-block kernel, cut into key slices here.
+MULTI_PASS = [
+    (_wk("g7-56rows", 28, 4, 128, "bf16", "bf16", ident=131), [300, 1000, 40, 0], [8, 5, 8, 3]),
+    (_wk("g3-48rows", 24, 8, 128, "bf16", "bf16", ident=132), [500, 77], [16, 9]),
+]
+
+
+@pytest.mark.parametrize("spec", MULTI_PASS, ids=[s[0].name for s in MULTI_PASS])
+def test_multi_pass_pairs_on_row_blocks(spec):
+    w, ctx, ks = spec
+    say(f"multi-pass pairs {w.name}")
+    case = wl.make_case(w, device=DEV, ctx=ctx, k=ks, with_logits=False)
+    out = tva.spec_verify_attn(batch_of(case), case["q"], paged_kv(case))
+    torch.cuda.synchronize()
+    assert_close(out, oracle_attn(case), "bf16")

@@ -2808,14 +2808,27 @@ AttnPlan plan_verify_attn(const sva_batch* batch, const sva_paged_kv* kv, int Hq
   AttnPlan pl;
   const int G = Hq / kv->Hkv;
   // Row-block kernel: when a pair has more query rows than the split kernel
-  // handles in one pass and the blocks alone fill the device (or the split
-  // kernel cannot take the shape at all).  MFMA path only.
+  // handles in one pass and the blocks alone fill the device, or (bf16
+  // caches) the query-head split below cannot bring a pair to one pass, or
+  // the split kernel cannot take the shape at all.  MFMA path only.  For
+  // bf16, pairs of 33-128 rows that the split kernel streams once per pass
+  // run faster as row blocks, cut into key slices where they are few (G = 7,
+  // k = 8, 64 pairs: 62.3 -> 42.9 us; G = 7, k = 16, 16 pairs: 71.2 ->
+  // 25.3 us; G = 8, k = 8, 192 pairs: 145.5 -> 85.8 us); the INT8 row-block
+  // kernel is slower there (G = 7, k = 8, 64 pairs: 45.0 -> 53.9 us).
   const bool mfma_ok = kv->kv_dtype != SVA_F32 && !(opts && opts->path == 1);
   const int64_t rows = int64_t(std::max(batch->max_q, 1)) * G;
   const int64_t blocks_ub =
       int64_t(kv->Hkv) * ((int64_t(batch->total_q) * G + kRowBlock - 1) / kRowBlock + batch->B);
+  const int64_t kv_pairs = int64_t(batch->B) * kv->Hkv;
+  int one_pass_split = 1;             // the query-head split that fits one pass
+  while (rows / one_pass_split > kMfmaRows && G % (2 * one_pass_split) == 0 &&
+         kv_pairs * 2 * one_pass_split <= num_cus)
+    one_pass_split *= 2;
+  const bool split_passes = rows / one_pass_split > kMfmaRows;
   pl.rows_kernel = mfma_ok && (batch->max_q > kMaxDraftsSplit || rows > kMaxRowsSplit ||
-                               (rows > kMfmaRows && blocks_ub >= num_cus));
+                               (rows > kMfmaRows && blocks_ub >= num_cus) ||
+                               (split_passes && kv->kv_dtype == SVA_BF16));
   const int64_t pages_per_seq =
       std::min<int64_t>(kv->max_pages_per_seq, (int64_t(batch->max_len) + kPage - 1) / kPage);
   // Key slices for the row-block kernel when its blocks leave CUs idle (a few
@@ -2855,11 +2868,8 @@ AttnPlan plan_verify_attn(const sva_batch* batch, const sva_paged_kv* kv, int Hq
   // head must stream at the same time, on different workgroups, for L2 to
   // serve the later reads.
   pl.kv_split = 1;
-  const int64_t kv_pairs = int64_t(batch->B) * kv->Hkv;
   if (!pl.rows_kernel && mfma_ok) {
-    while (rows / pl.kv_split > kMfmaRows && G % (2 * pl.kv_split) == 0 &&
-           kv_pairs * 2 * pl.kv_split <= num_cus)
-      pl.kv_split *= 2;
+    pl.kv_split = one_pass_split;
     if (rows / pl.kv_split >= kMfmaRows && G % (2 * pl.kv_split) == 0 &&
         kv_pairs * pl.kv_split * 8 <= num_cus)
       pl.kv_split *= 2;
