@@ -54,7 +54,8 @@ HBM_PEAK_GBPS = 8000.0
 MALL_BYTES = 256 << 20
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 MAX_CPU_WORKERS = 16
-EXTRA_CONFIGS = ("tiny", "mha7b", "gqa8b", "gqa70b_int8")
+EXTRA_CONFIGS = ("tiny", "mha7b", "gqa8b", "gqa70b_int8", "prm7b_step", "prm7b_step_b1")
+CONFIG_MIN_STEPS = 50
 
 
 def log(*a):
@@ -551,7 +552,8 @@ def main():
         for name in EXTRA_CONFIGS:
             log(f"config {name}")
             wc = step_workload(wl, name)
-            r = measure(tva, wl, wc, dev, args.steps, args.warmup)
+            # at least 50 steps: the configs' launches are short and 20 of them vary
+            r = measure(tva, wl, wc, dev, max(args.steps, CONFIG_MIN_STEPS), max(args.warmup, 5))
             configs[name] = {
                 "workload": describe(wc, wl),
                 "attn_us": r["attn_ms"] * 1e3, "kv_bytes_per_launch": r["kv_bytes"],
@@ -568,6 +570,11 @@ def main():
             if name == "tiny":
                 configs[name]["note"] = ("0.56 MB working set: launch-bound, far below the time "
                                          "70 % of 8 TB/s would take (0.1 us)")
+            if name in wl.LONG_WORKLOADS:       # MFMA-bound; no acceptance in the step
+                configs[name].update({
+                    "attn_flops_per_launch": r["flops"], "attn_tflops": r["tflops"],
+                    "mfma_frac_of_peak": r["tflops"] / MFMA_BF16_PEAK_TFLOPS,
+                    "goodput_accepted_tokens_per_s": None, "emitted_tokens_per_step": None})
 
     achieved = m["kv_gbps"]
     result = {
