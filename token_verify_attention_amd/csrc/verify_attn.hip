@@ -2427,9 +2427,12 @@ __global__ __launch_bounds__((AttnLds<KV, D, MF>::NT), 1) void verify_attn_kerne
 // slots, copied several groups ahead by 2 NU waves of the second half (one
 // page each, at the start of their softmax phase, the phase with time to
 // spare), or by the last wave alone when it holds no rows.
-// A wave never merges with another, and nothing is split over workgroups, so
-// no workspace is used.  Keys are streamed up to the block's last row's
-// position; the causal (or tree) mask applies on the pages holding drafts.
+// A wave never merges with another.  While the blocks fill the device,
+// nothing is split over workgroups and no workspace is used; fewer blocks (a
+// few long steps) are cut into key slices, each writing its rows' partial
+// state to the workspace, and a second launch (verify_rows_merge_kernel)
+// folds them.  Keys are streamed up to the block's last row's position; the
+// causal (or tree) mask applies on the pages holding drafts.
 //
 // Each SIMD holds one wave of each half of the workgroup (waves w and w + 4).
 // Per group a wave runs a product phase (P.V of the previous group, S^T of
@@ -2640,7 +2643,7 @@ void verify_attn_rows_kernel(AttnParams p) {
   const bool copier = idle_copier ? wave == kRowWaves - 1 : (cw >= 0 && cw < NP);
   auto slot = [&](int u) __attribute__((always_inline)) -> const char* { return s_ring + (u % NS) * L::UNIT; };
   // pages past the end copy the last page (unused)
-  auto issue = [&](int u) __attribute__((always_inline)) {                         // wave j: page NP u + j
+  auto issue = [&](int u) __attribute__((always_inline)) {          // wave j: page NP (ua + u) + j
     if (u >= nunits) return;
     if (idle_copier) {
       int ids[NP];
